@@ -1,0 +1,300 @@
+// QK-norm + RoPE + paged KV write, and attention over the paged KV pool.
+//
+// Pool layout per layer: [num_blocks][kv_heads][block_size = 16][head_dim], so one (block, kv head)
+// tile is contiguous (4 KiB at head_dim 128 in 16-bit types) and is read with 16-byte loads.
+// A row with slot -1 (padding) writes its K and V to the scratch block num_blocks - 1, which no
+// block table holds ("Removing overhead: fusion, graphs and async scheduling", section "CUDA
+// graphs for a changing batch"). A row with seq_len 0 gets a zero attention output.
+#pragma once
+#include "common.h"
+
+namespace gr {
+
+constexpr int kBlk = 16;  // tokens per KV block
+
+// One wave per (row, head). Heads [0, nq) are query heads: RMSNorm over head_dim (qk_norm), then
+// rotate-half RoPE at the row's position, stored fp32 to q_out. Heads [nq, nq + nkv) are KV heads:
+// k gets the same treatment with its own gain, v is copied; both go to the pool slot.
+template <class T>
+__global__ __launch_bounds__(64) void k_qkv_post(int nq, int nkv, int d, const float* __restrict__ qkv,
+                                                 int n_parts, size_t part_stride, const int* __restrict__ pos,
+                                                 const int* __restrict__ slot, const float* __restrict__ rope_cos,
+                                                 const float* __restrict__ rope_sin, const void* __restrict__ q_norm,
+                                                 const void* __restrict__ k_norm, float eps, float* __restrict__ q_out,
+                                                 void* __restrict__ k_pool, void* __restrict__ v_pool, int num_blocks) {
+  using S = typename T::S;
+  const int row = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int half = d / 2;
+  const int ld = (nq + 2 * nkv) * d;
+  const bool is_q = h < nq;
+  const int g = h - nq;
+  const int col = is_q ? h * d : (nq + g) * d;
+  const bool act = lane < half;
+  auto fetch = [&](int c) -> float {
+    float s = 0.f;
+    for (int p = 0; p < n_parts; ++p) s += qkv[p * part_stride + static_cast<size_t>(row) * ld + c];
+    return s;
+  };
+  float x0 = act ? fetch(col + lane) : 0.f;
+  float x1 = act ? fetch(col + lane + half) : 0.f;
+  const void* gain = is_q ? q_norm : k_norm;
+  if (gain) {
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+    const S* gw = static_cast<const S*>(gain);
+    if (act) {
+      x0 = x0 * inv * T::to_f(gw[lane]);
+      x1 = x1 * inv * T::to_f(gw[lane + half]);
+    }
+  }
+  const int p = pos[row];
+  const float c = act ? rope_cos[static_cast<size_t>(p) * half + lane] : 0.f;
+  const float s = act ? rope_sin[static_cast<size_t>(p) * half + lane] : 0.f;
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x1 * c + x0 * s;
+  if (is_q) {
+    if (act) {
+      float* q = q_out + (static_cast<size_t>(row) * nq + h) * d;
+      q[lane] = y0;
+      q[lane + half] = y1;
+    }
+    return;
+  }
+  const int sl = slot[row];
+  const int blk = sl >= 0 ? sl / kBlk : num_blocks - 1;
+  const int off = sl >= 0 ? sl % kBlk : 0;
+  const size_t base = ((static_cast<size_t>(blk) * nkv + g) * kBlk + off) * d;
+  if (act) {
+    S* kp = static_cast<S*>(k_pool) + base;
+    S* vp = static_cast<S*>(v_pool) + base;
+    kp[lane] = T::from_f(y0);
+    kp[lane + half] = T::from_f(y1);
+    const int vcol = (nq + nkv + g) * d;
+    vp[lane] = T::from_f(fetch(vcol + lane));
+    vp[lane + half] = T::from_f(fetch(vcol + lane + half));
+  }
+}
+
+struct AttnRowsArgs {
+  int nq, nkv;
+  const float* q;            // [rows][nq][D] fp32
+  const void* k_pool;
+  const void* v_pool;
+  const int* block_table;    // [reqs][bt_stride]
+  int bt_stride;
+  const int* row_req;        // row -> block-table row (nullptr: identity)
+  const int* seq_lens;       // [rows] keys visible to the row, its own token included
+  int split_tokens;          // P: keys per split (multiple of 64)
+  int max_splits;            // gridDim.z
+  int num_blocks;            // pool blocks; a negative table entry reads the scratch block
+  void* out;                 // [rows][nq * D] in the model dtype
+  float* partials;           // [rows][nq][max_splits][D + 2]
+  unsigned* counters;        // [rows][nkv], zero between launches
+  float scale;
+};
+
+// Decode attention with one query row per request ("One forward per step", section "What
+// changed"), split over the key range so that short batches still fill the GPU (the same page,
+// section "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers
+// keys [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends
+// on the bucket only and replays as captured. The splits of a (row, kv head) each write
+// (max, sum, unnormalised output) and the last to finish combines them in split order.
+// Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv query
+// heads sharing the KV head are processed together.
+template <class T, int D, int G>
+__global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
+  using S = typename T::S;
+  constexpr int KL = D / 8;          // dims per lane in the score phase (8 lanes per key)
+  constexpr int VG = 64 / (D / 8);   // key groups in the value phase (lane owns 8 dims)
+  __shared__ float p_s[4][G][kBlk];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wo[4][G][D];
+  __shared__ int last_flag;
+  const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int L = a.seq_lens[row];
+  const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
+  S* out = static_cast<S*>(a.out) + static_cast<size_t>(row) * a.nq * D;
+  if (L <= 0) {
+    if (sp == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x) out[(g * G) * D + i] = T::from_f(0.f);
+    }
+    return;
+  }
+  if (sp >= nsplit) return;
+  const int t0 = sp * a.split_tokens, t1 = min(L, t0 + a.split_tokens);
+  const int req = a.row_req ? a.row_req[row] : row;
+  const int* bt = a.block_table + static_cast<size_t>(req) * a.bt_stride;
+
+  // query heads g*G .. g*G+G-1, score-phase slice of this lane: dims (lane % 8) * KL .. + KL
+  float q[G][KL];
+  const int sub = lane & 7, kt = lane >> 3;
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < KL; ++e) q[j][e] = a.q[(static_cast<size_t>(row) * a.nq + g * G + j) * D + sub * KL + e] * a.scale;
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  }
+  const int vd = (lane % (D / 8)) * 8;  // value-phase dims of this lane
+  const int vg = lane / (D / 8);        // value-phase key group
+
+  const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+  for (int bi = wid; bi < nblk; bi += 4) {
+    const int tb = t0 + bi * kBlk;                          // first key of the block
+    const int pb0 = (tb / kBlk < a.bt_stride) ? bt[tb / kBlk] : -1;
+    const int pb = pb0 >= 0 ? pb0 : a.num_blocks - 1;
+    const size_t tile = (static_cast<size_t>(pb) * a.nkv + g) * kBlk * D;
+    const S* kt_ptr = static_cast<const S*>(a.k_pool) + tile;
+    const S* vt_ptr = static_cast<const S*>(a.v_pool) + tile;
+    // issue all loads of the block up front
+    constexpr int KV16 = KL * sizeof(S) / 16;               // 16-byte vectors per lane per key pass
+    uint4 kr[2][KV16 > 0 ? KV16 : 1];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int v = 0; v < KV16; ++v)
+        kr[ps][v] = *reinterpret_cast<const uint4*>(kt_ptr + (ps * 8 + kt) * D + sub * KL + v * (16 / sizeof(S)));
+    constexpr int VV = 8 * sizeof(S) / 16;                  // 16-byte vectors per 8 dims
+    uint4 vr[kBlk / VG][VV];
+#pragma unroll
+    for (int i = 0; i < kBlk / VG; ++i)
+#pragma unroll
+      for (int v = 0; v < VV; ++v)
+        vr[i][v] = *reinterpret_cast<const uint4*>(vt_ptr + (vg + i * VG) * D + vd + v * (16 / sizeof(S)));
+
+    // scores: 8 lanes per key, two passes of 8 keys
+    float sc[2][G];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      float kf[KL];
+#pragma unroll
+      for (int v = 0; v < KV16; ++v) cvt_vec<T>(kr[ps][v], kf + v * T::kEPV);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < KL; ++e) acc = fmaf(q[j][e], kf[e], acc);
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 4, 64);
+        const int t = tb + ps * 8 + kt;
+        sc[ps][j] = (t < t1) ? acc : -INFINITY;
+      }
+    }
+    // block max per head over the 16 keys, new running max, probabilities
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float bm = fmaxf(sc[0][j], sc[1][j]);
+      bm = fmaxf(bm, __shfl_xor(bm, 8, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(m[j], bm);
+      const float corr = __expf(m[j] - mn);
+      const float p0 = __expf(sc[0][j] - mn), p1 = __expf(sc[1][j] - mn);
+      if (sub == 0) {
+        p_s[wid][j][kt] = p0;
+        p_s[wid][j][8 + kt] = p1;
+      }
+      float ps = p0 + p1;
+      ps += __shfl_xor(ps, 8, 64);
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l[j] = l[j] * corr + ps;
+      m[j] = mn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] *= corr;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // values: lane owns dims vd .. vd+7 for keys vg, vg + VG, ...
+#pragma unroll
+    for (int i = 0; i < kBlk / VG; ++i) {
+      float vf[8];
+#pragma unroll
+      for (int v = 0; v < VV; ++v) cvt_vec<T>(vr[i][v], vf + v * (16 / sizeof(S)));
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float p = p_s[wid][j][vg + i * VG];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = fmaf(p, vf[e], o[j][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // reduce the value accumulators over the key groups of the wave
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      for (int off = D / 8; off < 64; off <<= 1) o[j][e] += __shfl_xor(o[j][e], off, 64);
+  if (lane < D / 8) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wo[wid][j][vd + e] = o[j][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) { wm[wid][j] = m[j]; wl[wid][j] = l[j]; }
+  }
+  __syncthreads();
+  // combine the four waves (fixed order); thread t handles (head, dim) pairs
+  float* part = a.partials + (static_cast<size_t>(row) * a.nq + g * G) * a.max_splits * (D + 2);
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int j = i / D, dd = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][j]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (wm[w][j] == -INFINITY) ? 0.f : __expf(wm[w][j] - M);
+      Ls += wl[w][j] * f;
+      O += wo[w][j][dd] * f;
+    }
+    if (nsplit == 1) {
+      out[(g * G + j) * D + dd] = T::from_f(O / Ls);
+    } else {
+      float* pp = part + (static_cast<size_t>(j) * a.max_splits + sp) * (D + 2);
+      pp[2 + dd] = O;
+      if (dd == 0) { pp[0] = M; pp[1] = Ls; }
+    }
+  }
+  if (nsplit == 1) return;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* c = a.counters + static_cast<size_t>(row) * a.nkv + g;
+    const unsigned prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (prev == static_cast<unsigned>(nsplit - 1));
+    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = last;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int j = i / D, dd = i % D;
+    const float* pj = part + static_cast<size_t>(j) * a.max_splits * (D + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pj[s * (D + 2)]);
+    float Ls = 0.f, O = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float* ps = pj + s * (D + 2);
+      const float f = __expf(ps[0] - M);
+      Ls += ps[1] * f;
+      O += ps[2 + dd] * f;
+    }
+    out[(g * G + j) * D + dd] = T::from_f(O / Ls);
+  }
+}
+
+}  // namespace gr

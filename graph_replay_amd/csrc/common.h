@@ -1,0 +1,84 @@
+// Device helpers shared by the kernels: storage types, 16-byte vector loads, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gr {
+
+// Storage types. Arithmetic is fp32 everywhere; bf16/fp16 are storage and MFMA operand formats.
+struct F32 {
+  using S = float;
+  static constexpr int kEPV = 4;  // elements per 16-byte vector
+  __device__ static inline float to_f(S x) { return x; }
+  __device__ static inline S from_f(float f) { return f; }
+};
+struct BF16 {
+  using S = uint16_t;
+  static constexpr int kEPV = 8;
+  __device__ static inline float to_f(S x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+  __device__ static inline S from_f(float f) {  // round to nearest even, NaN kept quiet
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<S>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<S>(u >> 16);
+  }
+};
+struct F16 {
+  using S = _Float16;
+  static constexpr int kEPV = 8;
+  __device__ static inline float to_f(S x) { return static_cast<float>(x); }
+  __device__ static inline S from_f(float f) { return static_cast<_Float16>(f); }
+};
+
+// 16-byte load/store of kEPV elements converted to/from fp32.
+template <class T>
+__device__ inline void load_vec(const typename T::S* p, float* out) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  if constexpr (T::kEPV == 4) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  } else {
+    const typename T::S* e = reinterpret_cast<const typename T::S*>(&v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = T::to_f(e[i]);
+  }
+}
+template <class T>
+__device__ inline void cvt_vec(const uint4& v, float* out) {
+  if constexpr (T::kEPV == 4) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  } else {
+    const typename T::S* e = reinterpret_cast<const typename T::S*>(&v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = T::to_f(e[i]);
+  }
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a block of blockDim.x threads (multiple of 64); every thread gets the result.
+// `red` must hold blockDim.x / 64 floats of shared memory.
+__device__ inline float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+__device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace gr

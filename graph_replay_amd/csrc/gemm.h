@@ -1,0 +1,515 @@
+// Projections y = x W^T for the fused QKV, O, fused gate|up, down and LM-head matrices.
+//
+// The stacked matrices follow "Removing overhead: fusion, graphs and async scheduling", section
+// "Fewer, larger matmuls": one matmul over [W_Q | W_K | W_V] and one over [W_gate | W_up]. Three
+// kernels cover the row counts of a step:
+//   k_gemv       VALU, <= 8 token rows: every weight element is read once with 16-byte loads and
+//                used for all rows; optional prologue computing x = RMSNorm(r + sum of deltas) * g
+//                (the fused residual-add + RMSNorm), optional SiLU(gate) * up epilogue.
+//   k_gemv_mfma  16 or 32 token rows (bf16/fp16): v_mfma_f32_16x16x32 with both operands loaded
+//                straight from memory in the MFMA lane layout; the four waves split K.
+//   k_gemm       >= 33 token rows (bf16/fp16): LDS-tiled MFMA GEMM, optional split-K into fp32
+//                partial outputs that the consumer sums in fixed order.
+#pragma once
+#include "common.h"
+
+namespace gr {
+
+enum { EPI_F32 = 0, EPI_SILU = 1, EPI_STORE_T = 2 };
+
+struct GemmArgs {
+  int M, N, K;           // x [M][K]; W [N][K] (EPI_SILU: W [2N][K], rows N.. are `up`)
+  const void* W;
+  const void* bias;      // [N] in the weight dtype, or nullptr
+  const void* x;         // [M][K] in the weight dtype (norm == 0)
+  // norm == 1 prologue: v = r_in[m] + sum_s delta[s][m] (or embed[tok[m]] when embed != nullptr),
+  // x = v / sqrt(mean(v^2) + eps) * gain, rounded to the weight dtype; block 0 stores v to r_out.
+  int norm;
+  const float* r_in;
+  const float* delta;
+  int n_delta;           // number of [M][K] partial deltas to add
+  size_t delta_stride;   // floats between partials
+  const void* embed;
+  const int* tok;
+  float* r_out;
+  const void* gain;
+  float eps;
+  void* out;             // EPI_F32: float [ksplit][M][ldo]; EPI_SILU / EPI_STORE_T: dtype [M][ldo]
+  int ldo;
+  int ksplit;            // k_gemm / k_gemv_mfma: number of K ranges (gridDim.z / y)
+  size_t out_split_stride;
+};
+
+// ------------------------------------------------------------------------------------------
+// Residual-add + RMSNorm as a kernel of its own (used when the row count is too large to redo the
+// norm in every projection block). One block per row.
+template <class T>
+__global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const float* __restrict__ r_in,
+                                                     const float* __restrict__ delta, int n_delta,
+                                                     size_t delta_stride, const void* __restrict__ embed,
+                                                     const int* __restrict__ tok, const int* __restrict__ row_map,
+                                                     float* __restrict__ r_out, const void* __restrict__ gain,
+                                                     void* __restrict__ h_out, float eps) {
+  using S = typename T::S;
+  extern __shared__ float sm_norm[];
+  float* v = sm_norm;          // [H]
+  float* red = sm_norm + H;    // [8]
+  const int m = blockIdx.x;
+  const int src = row_map ? row_map[m] : m;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) {
+    float x;
+    if (embed) {
+      x = T::to_f(static_cast<const S*>(embed)[static_cast<size_t>(tok[src]) * H + k]);
+    } else {
+      x = r_in[static_cast<size_t>(src) * H + k];
+      for (int s = 0; s < n_delta; ++s) x += delta[s * delta_stride + static_cast<size_t>(src) * H + k];
+    }
+    v[k] = x;
+    ss += x * x;
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
+  const S* g = static_cast<const S*>(gain);
+  S* h = static_cast<S*>(h_out) + static_cast<size_t>(m) * H;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) {
+    if (r_out) r_out[static_cast<size_t>(m) * H + k] = v[k];
+    h[k] = T::from_f(v[k] * inv * T::to_f(g[k]));
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// VALU GEMV. Block = 4 waves; wave w owns ROWS weight rows (EPI_SILU: ROWS/2 gate rows and the
+// matching up rows). Lanes stride over K in 16-byte vectors. The block's MT token rows of x are
+// staged in LDS (as the weight dtype) in chunks of KC elements.
+template <class T, int MT, int ROWS>
+__global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
+  using S = typename T::S;
+  constexpr int EPV = T::kEPV;
+  constexpr int U = 2;                                   // vectors per lane per row in flight
+  constexpr int KC = (32768 / (MT * static_cast<int>(sizeof(S)))) / (64 * EPV) * (64 * EPV);
+  __shared__ __align__(16) S xs[MT * KC];
+  __shared__ float red[8];
+  __shared__ float inv_rms[MT];
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * MT;
+  const int mrows = min(MT, a.M - m0);
+  const int K = a.K;
+  const S* W = static_cast<const S*>(a.W);
+
+  // weight rows of this wave
+  int rows[ROWS];
+  if (epi == EPI_SILU) {
+    const int j0 = (blockIdx.x * 4 + wid) * (ROWS / 2);
+#pragma unroll
+    for (int r = 0; r < ROWS / 2; ++r) { rows[r] = j0 + r; rows[ROWS / 2 + r] = a.N + j0 + r; }
+  } else {
+    const int n0 = (blockIdx.x * 4 + wid) * ROWS;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) rows[r] = n0 + r;
+  }
+  const int nrows_total = (epi == EPI_SILU) ? 2 * a.N : a.N;
+
+  // prologue: RMSNorm statistics of the block's token rows
+  if (a.norm) {
+    for (int mm = 0; mm < mrows; ++mm) {
+      const int m = m0 + mm;
+      float ss = 0.f;
+      for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        float v;
+        if (a.embed) {
+          v = T::to_f(static_cast<const S*>(a.embed)[static_cast<size_t>(a.tok[m]) * K + k]);
+        } else {
+          v = a.r_in[static_cast<size_t>(m) * K + k];
+          for (int s = 0; s < a.n_delta; ++s) v += a.delta[s * a.delta_stride + static_cast<size_t>(m) * K + k];
+        }
+        if (blockIdx.x == 0 && a.r_out) a.r_out[static_cast<size_t>(m) * K + k] = v;
+        ss += v * v;
+      }
+      ss = block_sum(ss, red);
+      if (threadIdx.x == 0) inv_rms[mm] = 1.0f / sqrtf(ss / static_cast<float>(K) + a.eps);
+    }
+    __syncthreads();
+  }
+
+  float acc[ROWS][MT];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.f;
+
+  for (int kc0 = 0; kc0 < K; kc0 += KC) {
+    const int kc = min(KC, K - kc0);
+    __syncthreads();
+    // stage x[m0 .. m0+mrows)[kc0 .. kc0+kc) into LDS
+    for (int i = threadIdx.x; i < MT * (kc / EPV); i += blockDim.x) {
+      const int mm = i / (kc / EPV), vv = i % (kc / EPV);
+      S* dst = xs + mm * KC + vv * EPV;
+      if (mm >= mrows) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+        continue;
+      }
+      const int m = m0 + mm, k = kc0 + vv * EPV;
+      if (!a.norm) {
+        *reinterpret_cast<uint4*>(dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) + static_cast<size_t>(m) * K + k);
+      } else {
+        const S* g = static_cast<const S*>(a.gain);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          float v;
+          if (a.embed) {
+            v = T::to_f(static_cast<const S*>(a.embed)[static_cast<size_t>(a.tok[m]) * K + k + e]);
+          } else {
+            v = a.r_in[static_cast<size_t>(m) * K + k + e];
+            for (int s = 0; s < a.n_delta; ++s) v += a.delta[s * a.delta_stride + static_cast<size_t>(m) * K + k + e];
+          }
+          dst[e] = T::from_f(v * inv_rms[mm] * T::to_f(g[k + e]));
+        }
+      }
+    }
+    __syncthreads();
+    const int nv = kc / EPV;  // vectors in this chunk
+    for (int v0 = 0; v0 < nv; v0 += 64 * U) {
+      uint4 wv[ROWS][U];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int vv = v0 + lane + 64 * u;
+          if (vv < nv && rows[r] < nrows_total)
+            wv[r][u] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(rows[r]) * K + kc0 + vv * EPV);
+          else
+            wv[r][u] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int vv = v0 + lane + 64 * u;
+        if (vv >= nv) continue;
+        float xf[MT][EPV];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) load_vec<T>(xs + mm * KC + vv * EPV, xf[mm]);
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          float wf[EPV];
+          cvt_vec<T>(wv[r][u], wf);
+#pragma unroll
+          for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[r][mm] = fmaf(wf[e], xf[mm][e], acc[r][mm]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) acc[r][mm] = wave_sum(acc[r][mm]);
+
+  if (lane == 0) {
+    if (epi == EPI_SILU) {
+      S* out = static_cast<S*>(a.out);
+#pragma unroll
+      for (int r = 0; r < ROWS / 2; ++r) {
+        if (rows[r] >= a.N) continue;
+        for (int mm = 0; mm < mrows; ++mm)
+          out[static_cast<size_t>(m0 + mm) * a.ldo + rows[r]] = T::from_f(silu(acc[r][mm]) * acc[ROWS / 2 + r][mm]);
+      }
+    } else {
+      float* out = static_cast<float*>(a.out);
+      const S* b = static_cast<const S*>(a.bias);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        if (rows[r] >= a.N) continue;
+        const float bb = b ? T::to_f(b[rows[r]]) : 0.f;
+        for (int mm = 0; mm < mrows; ++mm) out[static_cast<size_t>(m0 + mm) * a.ldo + rows[r]] = acc[r][mm] + bb;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// MFMA fragment types (gfx950 v_mfma_f32_16x16x32_{bf16,f16}). Lane l of a 16x32 A fragment holds
+// row l % 16, k = 8 * (l / 16) .. + 8; the B fragment holds column l % 16 with the same k slots;
+// the 16x16 fp32 result holds rows 4 * (l / 16) + i (i = 0..3) of column l % 16.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  if constexpr (sizeof(typename T::S) == 2 && T::kEPV == 8 && __is_same(T, BF16)) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// Skinny MFMA GEMV: block = 4 waves, 16 weight rows (EPI_SILU: 8 gate + the 8 matching up rows),
+// MB 16-token tiles; wave w accumulates k-steps w, w+4, ... and the partial tiles are summed in
+// wave order through LDS. gridDim.y splits K into a.ksplit ranges (EPI_F32 only) whose fp32
+// partials go to out + split * out_split_stride.
+template <class T, int MB>
+__global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
+  using S = typename T::S;
+  __shared__ f32x4_t part[4][MB][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int K = a.K;
+  const S* W = static_cast<const S*>(a.W);
+  const S* X = static_cast<const S*>(a.x);
+  int wrow;
+  if (epi == EPI_SILU) {
+    const int j = blockIdx.x * 8 + (lane & 7);
+    wrow = ((lane & 15) < 8) ? j : a.N + j;
+  } else {
+    wrow = blockIdx.x * 16 + (lane & 15);
+  }
+  const int nrows_total = (epi == EPI_SILU) ? 2 * a.N : a.N;
+  const bool wrow_ok = wrow < nrows_total;
+  const int ksteps = K / 32;
+  const int per = (ksteps + a.ksplit - 1) / a.ksplit;
+  const int ks0 = blockIdx.y * per, ks1 = min(ksteps, ks0 + per);
+  const int koff = 8 * (lane >> 4);
+
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const S* wp = W + static_cast<size_t>(wrow_ok ? wrow : 0) * K + koff;
+  const S* xp[MB];
+  bool xok[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) {
+    const int m = t * 16 + (lane & 15);
+    xok[t] = m < a.M;
+    xp[t] = X + static_cast<size_t>(xok[t] ? m : 0) * K + koff;
+  }
+  constexpr int UN = 4;
+  int ks = ks0 + wid;
+  for (; ks + 4 * (UN - 1) < ks1; ks += 4 * UN) {
+    uint4 av[UN], bv[UN][MB];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int k = (ks + 4 * u) * 32;
+      av[u] = wrow_ok ? *reinterpret_cast<const uint4*>(wp + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) bv[u][t] = xok[t] ? *reinterpret_cast<const uint4*>(xp[t] + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u)
+#pragma unroll
+      for (int t = 0; t < MB; ++t) acc[t] = mfma16x16x32<T>(av[u], bv[u][t], acc[t]);
+  }
+  for (; ks < ks1; ks += 4) {
+    const int k = ks * 32;
+    uint4 av = wrow_ok ? *reinterpret_cast<const uint4*>(wp + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      uint4 bv = xok[t] ? *reinterpret_cast<const uint4*>(xp[t] + k) : make_uint4(0, 0, 0, 0);
+      acc[t] = mfma16x16x32<T>(av, bv, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MB; ++t) part[wid][t][lane] = acc[t];
+  __syncthreads();
+  if (wid != 0) return;
+#pragma unroll
+  for (int t = 0; t < MB; ++t) {
+    f32x4_t s = part[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s += part[w][t][lane];
+    acc[t] = s;
+  }
+  const int col = lane & 15;          // token within the tile
+  const int rbase = 4 * (lane >> 4);  // first of the 4 weight rows this lane holds
+  if (epi == EPI_SILU) {
+    // lanes 0..31 hold gate rows 0..7, lanes 32..63 the matching up rows 8..15
+    S* out = static_cast<S*>(a.out);
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      f32x4_t up;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up[i] = __shfl(acc[t][i], lane + 32, 64);
+      const int m = t * 16 + col;
+      if (lane < 32 && m < a.M) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = blockIdx.x * 8 + rbase + i;
+          if (j < a.N) out[static_cast<size_t>(m) * a.ldo + j] = T::from_f(silu(acc[t][i]) * up[i]);
+        }
+      }
+    }
+  } else {
+    float* out = static_cast<float*>(a.out) + blockIdx.y * a.out_split_stride;
+    const S* b = (blockIdx.y == 0) ? static_cast<const S*>(a.bias) : nullptr;
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      const int m = t * 16 + col;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = blockIdx.x * 16 + rbase + i;
+        if (n < a.N) out[static_cast<size_t>(m) * a.ldo + n] = acc[t][i] + (b ? T::to_f(b[n]) : 0.f);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// LDS-tiled MFMA GEMM for many token rows. Tile BN weight rows x BM tokens, BK = 32, 4 waves as
+// 2 (weight rows) x 2 (tokens). EPI_SILU maps the first BN/2 tile rows to gate rows and the last
+// BN/2 to the matching up rows. Block index: x = weight-row tile, y = token tile, z = K split.
+template <class T, int BN, int BM>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int epi) {
+  using S = typename T::S;
+  constexpr int BK = 32, LDK = BK + 8;            // padded LDS rows (elements)
+  constexpr int WN = BN / 2, WM = BM / 2;         // wave tile
+  constexpr int TN = WN / 16, TM = WM / 16;       // MFMA tiles per wave
+  constexpr size_t kTileBytes = 2 * (BN + BM) * LDK * sizeof(S);
+  constexpr size_t kExBytes = sizeof(float) * WN * BM;
+  __shared__ __align__(16) unsigned char smem[kTileBytes > kExBytes ? kTileBytes : kExBytes];
+  S (*ws)[BN * LDK] = reinterpret_cast<S (*)[BN * LDK]>(smem);
+  S (*xs_)[BM * LDK] = reinterpret_cast<S (*)[BM * LDK]>(smem + 2 * BN * LDK * sizeof(S));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid & 1, wm = wid >> 1;
+  const int K = a.K;
+  const S* W = static_cast<const S*>(a.W);
+  const S* X = static_cast<const S*>(a.x);
+  const int nrows_total = (epi == EPI_SILU) ? 2 * a.N : a.N;
+  const int m0 = blockIdx.y * BM;
+
+  auto wrow_of = [&](int r) -> int {  // tile row -> weight row
+    if (epi == EPI_SILU) {
+      const int half = BN / 2;
+      const int j = blockIdx.x * half + (r % half);
+      return (r < half) ? j : a.N + j;
+    }
+    return blockIdx.x * BN + r;
+  };
+  const int ksteps = K / BK;
+  const int per = (ksteps + a.ksplit - 1) / a.ksplit;
+  const int ks0 = blockIdx.z * per, ks1 = min(ksteps, ks0 + per);
+
+  // global -> register staging: each thread moves (BN + BM) * BK / 8 / 256 vectors per k-step
+  constexpr int WV = BN * BK / 8 / 256, XV = BM * BK / 8 / 256;
+  static_assert(WV >= 1 && XV >= 1, "tile too small for 256 threads");
+  uint4 wreg[WV], xreg[XV];
+  auto load_tiles = [&](int ks) {
+    const int k0 = ks * BK;
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 2, c = (idx & 3) * 8;
+      const int wr = wrow_of(r);
+      wreg[i] = (wr < nrows_total) ? *reinterpret_cast<const uint4*>(W + static_cast<size_t>(wr) * K + k0 + c)
+                                   : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 2, c = (idx & 3) * 8;
+      const int m = m0 + r;
+      xreg[i] = (m < a.M) ? *reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0 + c)
+                          : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tiles = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 2, c = (idx & 3) * 8;
+      *reinterpret_cast<uint4*>(&ws[buf][r * LDK + c]) = wreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 2, c = (idx & 3) * 8;
+      *reinterpret_cast<uint4*>(&xs_[buf][r * LDK + c]) = xreg[i];
+    }
+  };
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (ks0 < ks1) {
+    load_tiles(ks0);
+    store_tiles(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const bool more = ks + 1 < ks1;
+    if (more) load_tiles(ks + 1);
+    uint4 af[TN], bfr[TM];
+    const int koff = 8 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      af[i] = *reinterpret_cast<const uint4*>(&ws[buf][(wn * WN + i * 16 + (lane & 15)) * LDK + koff]);
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+      bfr[j] = *reinterpret_cast<const uint4*>(&xs_[buf][(wm * WM + j * 16 + (lane & 15)) * LDK + koff]);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bfr[j], acc[i][j]);
+    if (more) {
+      store_tiles(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  const int col = lane & 15, rbase = 4 * (lane >> 4);
+  if (epi == EPI_SILU) {
+    // wave wn = 1 holds the up rows matching wave wn = 0's gate rows: exchange through LDS
+    __syncthreads();
+    float* ex = reinterpret_cast<float*>(smem);   // WN * BM floats
+    if (wn == 1) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ex[(i * 16 + rbase + e) * BM + wm * WM + j * 16 + col] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (wn == 0) {
+      S* out = static_cast<S*>(a.out);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int m = m0 + wm * WM + j * 16 + col;
+          if (m >= a.M) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = blockIdx.x * (BN / 2) + i * 16 + rbase + e;
+            const float up = ex[(i * 16 + rbase + e) * BM + wm * WM + j * 16 + col];
+            if (jj < a.N) out[static_cast<size_t>(m) * a.ldo + jj] = T::from_f(silu(acc[i][j][e]) * up);
+          }
+        }
+    }
+  } else {
+    float* outf = static_cast<float*>(a.out) + blockIdx.z * a.out_split_stride;
+    S* outt = static_cast<S*>(a.out);
+    const S* b = (blockIdx.z == 0) ? static_cast<const S*>(a.bias) : nullptr;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = m0 + wm * WM + j * 16 + col;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = blockIdx.x * BN + wn * WN + i * 16 + rbase + e;
+          if (n >= a.N) continue;
+          const float v = acc[i][j][e] + (b ? T::to_f(b[n]) : 0.f);
+          if (epi == EPI_STORE_T) outt[static_cast<size_t>(m) * a.ldo + n] = T::from_f(v);
+          else outf[static_cast<size_t>(m) * a.ldo + n] = v;
+        }
+      }
+  }
+}
+
+}  // namespace gr

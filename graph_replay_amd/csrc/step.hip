@@ -1,0 +1,974 @@
+// libstep: the C ABI declared in include/step.h.
+//
+// Host side of the decode / mixed step: validation, the workspace layout, the launch sequence of a
+// step, one hipGraph per decode bucket ("Removing overhead: fusion, graphs and async scheduling",
+// section "CUDA graphs for a changing batch": static buffers sized for the largest bucket, copy-in
+// and padding before each replay, capture largest bucket first after two warm-ups, eager launch of
+// the same kernels when no graph exists), and the eager packed mixed step ("One forward per step",
+// section "What changed").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "attention.h"
+#include "common.h"
+#include "gemm.h"
+#include "sample.h"
+#include "../../include/step.h"
+
+using namespace gr;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {  // byte offsets into the workspace
+  size_t dmeta, dmeta_bytes;          // decode static inputs: rng[2] | ids | pos | slot | len | temp | bt
+  size_t mmeta, mmeta_bytes;          // mixed step inputs
+  size_t rope_cos, rope_sin;
+  size_t resid[2], h, qkv, q, attn_o, d_o, d_d, act;
+  size_t attn_part, attn_cnt, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
+  size_t total;
+  int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
+  int max_splits_alloc;               // splits per row the partial buffer holds (at 64 keys/split)
+  int ksplit_max;                     // partial copies of split-K outputs
+};
+
+struct Launch;  // forward
+
+}  // namespace
+
+struct step_ctx {
+  step_config cfg{};
+  step_weights w{};
+  std::vector<const void*> in_norm, qkv_w, qkv_b, q_norm, k_norm, o_w, post_norm, gate_up_w, down_w;
+  std::vector<void*> k_pool, v_pool;
+  float* logits = nullptr;
+  int* tokens = nullptr;
+  int* history = nullptr;
+  char* ws = nullptr;
+  Layout lay{};
+  hipStream_t stream = nullptr;
+  hipStream_t cap_stream = nullptr;
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> execs;
+  std::vector<int> kernels_per_bucket;
+  int last_bucket = 0;
+  int launches = 0;                   // kernels enqueued by the current plan run
+  uint64_t step_count = 0;            // Philox step counter the next host-fed step starts from
+  bool have_batch = false;
+  // pinned staging (two slots each, reused after their copy has completed)
+  char* h_stage[2] = {nullptr, nullptr};
+  hipEvent_t stage_ev[2] = {nullptr, nullptr};
+  int stage_next = 0;
+  size_t stage_bytes = 0;
+  std::string err;
+  bool dead = false;
+};
+
+static const void* c_embed_of(step_ctx* ctx) { return ctx->w.d_embed; }
+static const void* c_lm_head_of(step_ctx* ctx) { return ctx->w.d_lm_head; }
+static const void* c_final_norm_of(step_ctx* ctx) { return ctx->w.d_final_norm; }
+
+namespace {
+
+int fail(step_ctx* c, int code, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return code;
+}
+
+#define HIPCHK(ctx, call)                                                                          \
+  do {                                                                                             \
+    hipError_t e_ = (call);                                                                        \
+    if (e_ != hipSuccess) return fail((ctx), STEP_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+int elem_bytes(int dtype) { return dtype == STEP_F32 ? 4 : 2; }
+
+// keys per attention split for a given row count (fixed per bucket, so the grid is too)
+int split_tokens_for(int rows) { return rows <= 8 ? 64 : (rows <= 32 ? 128 : 256); }
+
+// copies of split-K partial outputs the workspace holds
+constexpr int kMaxKsplit = 8;
+
+bool compute_layout(const step_config& c, Layout& L) {
+  const int H = c.hidden, d = c.head_dim, nq = c.q_heads, nkv = c.kv_heads, I = c.intermediate;
+  const int QKV = (nq + 2 * nkv) * d;
+  const int W = c.max_blocks_per_seq;
+  const int MB = c.max_batch;
+  L.TM = std::max(c.max_batch, c.max_tokens);
+  L.RM = std::max(c.max_batch, c.max_reqs);
+  L.LM = std::max(c.max_batch, c.max_logit_rows);
+  const int TM = L.TM, RM = L.RM, LM = L.LM;
+  const int eb = elem_bytes(c.dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.dmeta_bytes = 16 + sizeof(int) * (5 * static_cast<size_t>(MB) + static_cast<size_t>(MB) * W);
+  L.dmeta = take(L.dmeta_bytes);
+  // mixed: rng[2] | tok | pos | slot | row_req | row_len [TM] | qsl [RM+1] | req_len [RM] | bt [RM*W]
+  //        | logit_idx [LM] | temp [LM] | tile_req, tile_q0 [TM/16 + RM]
+  const size_t tiles = TM / 16 + RM + 1;
+  L.mmeta_bytes = 16 + sizeof(int) * (5 * static_cast<size_t>(TM) + (RM + 1) + RM + static_cast<size_t>(RM) * W +
+                                      2 * static_cast<size_t>(LM) + 2 * tiles);
+  L.mmeta = take(L.mmeta_bytes);
+  L.rope_cos = take(sizeof(float) * static_cast<size_t>(c.max_position) * (d / 2));
+  L.rope_sin = take(sizeof(float) * static_cast<size_t>(c.max_position) * (d / 2));
+  L.ksplit_max = kMaxKsplit;
+  L.resid[0] = take(sizeof(float) * static_cast<size_t>(TM) * H);
+  L.resid[1] = take(sizeof(float) * static_cast<size_t>(TM) * H);
+  L.h = take(static_cast<size_t>(eb) * TM * std::max(H, 1));
+  L.qkv = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * QKV);
+  L.q = take(sizeof(float) * static_cast<size_t>(TM) * nq * d);
+  L.attn_o = take(static_cast<size_t>(eb) * TM * nq * d);
+  L.d_o = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * H);
+  L.d_d = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * H);
+  L.act = take(static_cast<size_t>(eb) * TM * I);
+  // attention partials: rows * ceil(max_position / split) splits, maximised over row classes
+  size_t part_rows_splits = 0;
+  for (int rows : {8, 32, TM}) {
+    const int r = std::min(rows, TM);
+    const int s = (c.max_position + split_tokens_for(r) - 1) / split_tokens_for(r);
+    part_rows_splits = std::max(part_rows_splits, static_cast<size_t>(r) * s);
+  }
+  L.max_splits_alloc = 0;
+  L.attn_part = take(sizeof(float) * part_rows_splits * nq * (d + 2));
+  L.attn_cnt = take(sizeof(unsigned) * static_cast<size_t>(TM) * nkv);
+  const int nch_max = (c.vocab + 1023) / 1024;
+  L.samp_val = take(sizeof(float) * static_cast<size_t>(LM) * nch_max);
+  L.samp_idx = take(sizeof(int) * static_cast<size_t>(LM) * nch_max);
+  L.samp_cnt = take(sizeof(unsigned) * static_cast<size_t>(LM));
+  L.samp_done = take(sizeof(unsigned) * 4);
+  L.samp_temp = take(sizeof(float) * static_cast<size_t>(LM));
+  L.samp_rng = take(16);
+  L.total = off;
+  (void)RM;
+  return true;
+}
+
+int validate_config(step_ctx* ctx, const step_config* c) {
+  if (!c) return fail(ctx, STEP_EINVAL, "config is NULL");
+  if (c->dtype != STEP_F32 && c->dtype != STEP_BF16 && c->dtype != STEP_F16)
+    return fail(ctx, STEP_EUNSUPPORTED, "dtype %d is not one of F32/BF16/F16", c->dtype);
+  if (c->layers <= 0 || c->hidden <= 0 || c->q_heads <= 0 || c->kv_heads <= 0 || c->intermediate <= 0 || c->vocab <= 0)
+    return fail(ctx, STEP_EINVAL, "non-positive model dimension");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(ctx, STEP_EUNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", c->head_dim);
+  if (c->q_heads % c->kv_heads != 0) return fail(ctx, STEP_EINVAL, "q_heads must be a multiple of kv_heads");
+  const int G = c->q_heads / c->kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 6 && G != 8)
+    return fail(ctx, STEP_EUNSUPPORTED, "query heads per KV head = %d: kernels are built for 1, 2, 4, 6, 8", G);
+  const int epv = c->dtype == STEP_F32 ? 4 : 8;
+  if (c->hidden % (c->dtype == STEP_F32 ? 4 : 32) || c->intermediate % 32 || (c->q_heads * c->head_dim) % 32)
+    return fail(ctx, STEP_EUNSUPPORTED, "hidden, intermediate and q_heads*head_dim must be multiples of 32");
+  (void)epv;
+  if (c->block_size != 16) return fail(ctx, STEP_EUNSUPPORTED, "block_size must be 16");
+  if (c->num_blocks < 2) return fail(ctx, STEP_EINVAL, "num_blocks must be >= 2 (one is the scratch block)");
+  if (c->max_blocks_per_seq <= 0 || c->max_position <= 0) return fail(ctx, STEP_EINVAL, "bad max_blocks_per_seq / max_position");
+  if (c->max_batch <= 0 || c->max_tokens < 0 || c->max_reqs < 0 || c->max_logit_rows < 0)
+    return fail(ctx, STEP_EINVAL, "bad max_batch / max_tokens / max_reqs / max_logit_rows");
+  if (c->num_buckets < 0 || c->num_buckets > STEP_MAX_BUCKETS) return fail(ctx, STEP_EINVAL, "num_buckets out of range");
+  if (c->num_buckets == 0) return fail(ctx, STEP_EINVAL, "at least one bucket (== max_batch) is needed");
+  for (int i = 0; i < c->num_buckets; ++i) {
+    if (c->buckets[i] <= 0 || (i && c->buckets[i] <= c->buckets[i - 1]))
+      return fail(ctx, STEP_EINVAL, "buckets must be positive and ascending");
+  }
+  if (c->buckets[c->num_buckets - 1] != c->max_batch) return fail(ctx, STEP_EINVAL, "last bucket must equal max_batch");
+  if (c->max_tokens > 0 && (c->max_reqs <= 0 || c->max_logit_rows <= 0))
+    return fail(ctx, STEP_EINVAL, "mixed steps need max_reqs and max_logit_rows");
+  return STEP_OK;
+}
+
+template <class T>
+const typename T::S* tp(const void* p) { return static_cast<const typename T::S*>(p); }
+
+// ------------------------------------------------------------------------------------------------
+// linear-layer dispatch
+
+struct Lin {
+  int M, N, K;
+  const void* W;
+  const void* bias;
+  const void* x;
+  int epi;
+  void* out;
+  int ldo;
+  // fused-norm prologue (M <= 8, or fp32)
+  int norm = 0;
+  const float* r_in = nullptr;
+  const float* delta = nullptr;
+  int n_delta = 0;
+  size_t delta_stride = 0;
+  const void* embed = nullptr;
+  const int* tok = nullptr;
+  float* r_out = nullptr;
+  const void* gain = nullptr;
+  float eps = 0.f;
+  int ksplit_ok = 0;          // output may be split into fp32 partials (consumer sums them)
+  int* ksplit_used = nullptr; // out: partial count
+  size_t split_stride = 0;
+};
+
+template <class T, int MT, int ROWS>
+hipError_t launch_gemv_rows(const GemmArgs& a, int epi, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv<T, MT, ROWS>), grid, dim3(256), 0, s, a, epi);
+  return hipGetLastError();
+}
+
+template <class T, int MT>
+hipError_t launch_gemv_mt(const GemmArgs& a, int epi, int rows_pw, dim3 grid, hipStream_t s) {
+  switch (rows_pw) {
+    case 1: return launch_gemv_rows<T, MT, 1>(a, epi, grid, s);
+    case 2: return launch_gemv_rows<T, MT, 2>(a, epi, grid, s);
+    case 4: return launch_gemv_rows<T, MT, 4>(a, epi, grid, s);
+    default:
+      if constexpr (MT < 8) return launch_gemv_rows<T, MT, 8>(a, epi, grid, s);
+      else return hipErrorInvalidValue;
+  }
+}
+
+template <class T>
+int run_linear(step_ctx* ctx, const Lin& l) {
+  GemmArgs a{};
+  a.M = l.M; a.N = l.N; a.K = l.K; a.W = l.W; a.bias = l.bias; a.x = l.x;
+  a.norm = l.norm; a.r_in = l.r_in; a.delta = l.delta; a.n_delta = l.n_delta; a.delta_stride = l.delta_stride;
+  a.embed = l.embed; a.tok = l.tok; a.r_out = l.r_out; a.gain = l.gain; a.eps = l.eps;
+  a.out = l.out; a.ldo = l.ldo; a.ksplit = 1; a.out_split_stride = l.split_stride;
+  if (l.ksplit_used) *l.ksplit_used = 1;
+  hipStream_t s = ctx->stream;
+  hipError_t e;
+  const bool is_f32 = std::is_same<T, F32>::value;
+  if (l.M <= 8 || is_f32 || l.norm) {
+    const int MT = l.M <= 1 ? 1 : l.M <= 2 ? 2 : l.M <= 4 ? 4 : 8;
+    const int units = l.N;  // output columns (EPI_SILU: gate/up pairs)
+    const int ygrid = (l.M + MT - 1) / MT;
+    int rows_pw = (MT >= 8) ? 4 : 8;   // 8 x 8 accumulators would spill
+    const int min_rows = (l.epi == EPI_SILU) ? 2 : 1;
+    // largest rows-per-wave that still gives >= 512 blocks
+    while (rows_pw > min_rows) {
+      const int per_block = 4 * ((l.epi == EPI_SILU) ? rows_pw / 2 : rows_pw);
+      if (static_cast<long>((units + per_block - 1) / per_block) * ygrid >= 512) break;
+      rows_pw /= 2;
+    }
+    const int per_block = 4 * ((l.epi == EPI_SILU) ? rows_pw / 2 : rows_pw);
+    dim3 grid((units + per_block - 1) / per_block, ygrid);
+    switch (MT) {
+      case 1: e = launch_gemv_mt<T, 1>(a, l.epi, rows_pw, grid, s); break;
+      case 2: e = launch_gemv_mt<T, 2>(a, l.epi, rows_pw, grid, s); break;
+      case 4: e = launch_gemv_mt<T, 4>(a, l.epi, rows_pw, grid, s); break;
+      default: e = launch_gemv_mt<T, 8>(a, l.epi, rows_pw, grid, s); break;
+    }
+  } else if constexpr (!std::is_same<T, F32>::value) {
+    if (l.M <= 32) {
+      const int bx = (l.epi == EPI_SILU) ? (l.N + 7) / 8 : (l.N + 15) / 16;
+      int ks = 1;
+      if (l.ksplit_ok && l.epi == EPI_F32) {
+        while (ks < kMaxKsplit && bx * ks < 256 && (l.K / 32) / (ks * 2) >= 4) ks *= 2;
+      }
+      a.ksplit = ks;
+      if (l.ksplit_used) *l.ksplit_used = ks;
+      dim3 grid(bx, ks);
+      if (l.M <= 16) hipLaunchKernelGGL((k_gemv_mfma<T, 1>), grid, dim3(256), 0, s, a, l.epi);
+      else hipLaunchKernelGGL((k_gemv_mfma<T, 2>), grid, dim3(256), 0, s, a, l.epi);
+      e = hipGetLastError();
+    } else {
+      const bool big = l.M > 64;
+      const int BN = big ? 128 : 64, BM = big ? 128 : 64;
+      const int bx = (l.epi == EPI_SILU) ? (l.N + BN / 2 - 1) / (BN / 2) : (l.N + BN - 1) / BN;
+      const int by = (l.M + BM - 1) / BM;
+      int ks = 1;
+      if (l.ksplit_ok && l.epi == EPI_F32) {
+        while (ks < kMaxKsplit && bx * by * ks < 256 && (l.K / 32) / (ks * 2) >= 4) ks *= 2;
+      }
+      a.ksplit = ks;
+      if (l.ksplit_used) *l.ksplit_used = ks;
+      dim3 grid(bx, by, ks);
+      if (big) hipLaunchKernelGGL((k_gemm<T, 128, 128>), grid, dim3(256), 0, s, a, l.epi);
+      else hipLaunchKernelGGL((k_gemm<T, 64, 64>), grid, dim3(256), 0, s, a, l.epi);
+      e = hipGetLastError();
+    }
+  } else {
+    e = hipErrorInvalidValue;
+  }
+  ctx->launches++;
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "linear launch failed: %s", hipGetErrorString(e));
+  return STEP_OK;
+}
+
+template <class T>
+int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_delta, size_t dstride,
+             const void* embed, const int* tok, const int* row_map, float* r_out, const void* gain, void* h_out) {
+  const int H = ctx->cfg.hidden;
+  const size_t sm = sizeof(float) * (H + 8);
+  hipLaunchKernelGGL((k_add_rmsnorm<T>), dim3(M), dim3(256), sm, ctx->stream, H, r_in, delta, n_delta, dstride, embed,
+                     tok, row_map, r_out, gain, h_out, ctx->cfg.rms_eps);
+  ctx->launches++;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "norm launch failed: %s", hipGetErrorString(e));
+  return STEP_OK;
+}
+
+template <class T, int D>
+hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream_t s) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_attn_rows<T, D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_rows<T, D, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_rows<T, D, 4>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_attn_rows<T, D, 6>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_attn_rows<T, D, 8>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+// Row-attention over `rows` query rows; max_len bounds the keys of any row (sets the split grid).
+template <class T>
+int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, const int* bt, int bt_stride, const int* row_req,
+                  const int* seq_lens, int max_len, void* out) {
+  const step_config& c = ctx->cfg;
+  AttnRowsArgs a{};
+  a.nq = c.q_heads; a.nkv = c.kv_heads; a.q = q;
+  a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
+  a.block_table = bt; a.bt_stride = bt_stride; a.row_req = row_req; a.seq_lens = seq_lens;
+  a.split_tokens = split_tokens_for(rows);
+  a.max_splits = std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
+  a.num_blocks = c.num_blocks;
+  a.out = out;
+  a.partials = reinterpret_cast<float*>(ctx->ws + ctx->lay.attn_part);
+  a.counters = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.attn_cnt);
+  a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+  const int G = c.q_heads / c.kv_heads;
+  dim3 grid(rows, c.kv_heads, a.max_splits);
+  hipError_t e = (c.head_dim == 64) ? launch_attn_rows_d<T, 64>(a, G, grid, ctx->stream)
+                                    : launch_attn_rows_d<T, 128>(a, G, grid, ctx->stream);
+  ctx->launches++;
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return STEP_OK;
+}
+
+template <class T>
+int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_stride, const int* pos, const int* slot) {
+  const step_config& c = ctx->cfg;
+  const Layout& L = ctx->lay;
+  hipLaunchKernelGGL((k_qkv_post<T>), dim3(rows, c.q_heads + c.kv_heads), dim3(64), 0, ctx->stream, c.q_heads,
+                     c.kv_heads, c.head_dim, reinterpret_cast<const float*>(ctx->ws + L.qkv), n_parts, part_stride, pos,
+                     slot, reinterpret_cast<const float*>(ctx->ws + L.rope_cos),
+                     reinterpret_cast<const float*>(ctx->ws + L.rope_sin), c.qk_norm ? ctx->q_norm[layer] : nullptr,
+                     c.qk_norm ? ctx->k_norm[layer] : nullptr, c.rms_eps, reinterpret_cast<float*>(ctx->ws + L.q),
+                     ctx->k_pool[layer], ctx->v_pool[layer], c.num_blocks);
+  ctx->launches++;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "qkv_post launch failed: %s", hipGetErrorString(e));
+  return STEP_OK;
+}
+
+int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, const float* temp, const float* uniforms,
+               const uint64_t* rng, uint64_t seed, uint64_t stepc, int* tokens_out, int advance, int* ids, int* pos,
+               int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld) {
+  SampleArgs a{};
+  a.logits = logits; a.ld = ld; a.vocab = vocab;
+  int chunk = 1024;
+  while (chunk < 16384 && static_cast<long>(rows) * ((vocab + chunk * 2 - 1) / (chunk * 2)) >= 256) chunk *= 2;
+  a.chunk = chunk;
+  a.temperature = temp; a.uniforms = uniforms; a.rng = rng; a.seed = seed; a.step = stepc;
+  a.part_val = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_val);
+  a.part_idx = reinterpret_cast<int*>(ctx->ws + ctx->lay.samp_idx);
+  a.row_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_cnt);
+  a.done_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_done);
+  a.tokens_out = tokens_out;
+  a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
+  a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
+  const int nch = (vocab + chunk - 1) / chunk;
+  hipLaunchKernelGGL(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
+  ctx->launches++;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
+  return STEP_OK;
+}
+
+#define TRY(x)                  \
+  do {                          \
+    int rc_ = (x);              \
+    if (rc_ != STEP_OK) return rc_; \
+  } while (0)
+
+// Pointers into a metadata block laid out as rng[2] | ids | pos | slot | len | temp | bt.
+struct DecodeMeta {
+  uint64_t* rng;
+  int *ids, *pos, *slot, *len;
+  float* temp;
+  int* bt;
+};
+DecodeMeta decode_meta(char* base, int MB, int W) {
+  DecodeMeta m;
+  m.rng = reinterpret_cast<uint64_t*>(base);
+  m.ids = reinterpret_cast<int*>(base + 16);
+  m.pos = m.ids + MB;
+  m.slot = m.pos + MB;
+  m.len = m.slot + MB;
+  m.temp = reinterpret_cast<float*>(m.len + MB);
+  m.bt = reinterpret_cast<int*>(m.temp + MB);
+  (void)W;
+  return m;
+}
+
+// The transformer layers over M rows: embed -> layers -> final norm (rows of row_map) -> LM head.
+// attn(layer) enqueues the attention of one layer (rows or packed prefill + rows).
+template <class T, class AttnFn>
+int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* slot, int n_logits, const int* logit_rows,
+               AttnFn attn) {
+  const step_config& c = ctx->cfg;
+  const Layout& L = ctx->lay;
+  const int H = c.hidden, d = c.head_dim, nq = c.q_heads, nkv = c.kv_heads, I = c.intermediate;
+  const int QKV = (nq + 2 * nkv) * d;
+  float* resid[2] = {reinterpret_cast<float*>(ctx->ws + L.resid[0]), reinterpret_cast<float*>(ctx->ws + L.resid[1])};
+  void* h = ctx->ws + L.h;
+  float* qkv = reinterpret_cast<float*>(ctx->ws + L.qkv);
+  void* attn_o = ctx->ws + L.attn_o;
+  float* d_o = reinterpret_cast<float*>(ctx->ws + L.d_o);
+  float* d_d = reinterpret_cast<float*>(ctx->ws + L.d_d);
+  void* act = ctx->ws + L.act;
+  const bool fuse_norm = (M <= 8) || std::is_same<T, F32>::value;
+  const size_t res_stride = static_cast<size_t>(L.TM) * H;     // floats between split-K partials of H-wide outputs
+  const size_t qkv_stride = static_cast<size_t>(L.TM) * QKV;
+  int n_dd = 0;                                                 // partial count of the previous down output
+  for (int l = 0; l < c.layers; ++l) {
+    // ---- attention half: r1 = r0 + down(l-1); h = RMSNorm(r1) * in_norm; qkv = h Wqkv^T (+b)
+    const float* r_in = resid[0];
+    float* r_out = resid[1];
+    const bool first = (l == 0);
+    int n_qkv = 1;
+    Lin lin{};
+    lin.M = M; lin.N = QKV; lin.K = H; lin.W = ctx->qkv_w[l]; lin.bias = c.qkv_bias ? ctx->qkv_b[l] : nullptr;
+    lin.epi = EPI_F32; lin.out = qkv; lin.ldo = QKV; lin.ksplit_ok = 1; lin.ksplit_used = &n_qkv;
+    lin.split_stride = qkv_stride;
+    if (fuse_norm) {
+      lin.norm = 1; lin.r_in = r_in; lin.delta = first ? nullptr : d_d; lin.n_delta = first ? 0 : n_dd;
+      lin.delta_stride = res_stride; lin.embed = first ? c_embed_of(ctx) : nullptr; lin.tok = tok; lin.r_out = r_out;
+      lin.gain = ctx->in_norm[l]; lin.eps = c.rms_eps;
+    } else {
+      TRY(run_norm<T>(ctx, M, r_in, first ? nullptr : d_d, first ? 0 : n_dd, res_stride, first ? c_embed_of(ctx) : nullptr,
+                      tok, nullptr, r_out, ctx->in_norm[l], h));
+      lin.x = h;
+    }
+    TRY(run_linear<T>(ctx, lin));
+    TRY(run_qkv_post<T>(ctx, l, M, n_qkv, qkv_stride, pos, slot));
+    TRY(attn(l));
+    // ---- O projection
+    int n_o = 1;
+    Lin lo{};
+    lo.M = M; lo.N = H; lo.K = nq * d; lo.W = ctx->o_w[l]; lo.x = attn_o; lo.epi = EPI_F32; lo.out = d_o; lo.ldo = H;
+    lo.ksplit_ok = 1; lo.ksplit_used = &n_o; lo.split_stride = res_stride;
+    TRY(run_linear<T>(ctx, lo));
+    // ---- MLP half: r0 = r1 + o; h = RMSNorm(r0) * post_norm; a = SiLU(h Wg^T) * (h Wu^T); down
+    Lin lg{};
+    lg.M = M; lg.N = I; lg.K = H; lg.W = ctx->gate_up_w[l]; lg.epi = EPI_SILU; lg.out = act; lg.ldo = I;
+    if (fuse_norm) {
+      lg.norm = 1; lg.r_in = r_out; lg.delta = d_o; lg.n_delta = n_o; lg.delta_stride = res_stride; lg.r_out = resid[0];
+      lg.gain = ctx->post_norm[l]; lg.eps = c.rms_eps;
+    } else {
+      TRY(run_norm<T>(ctx, M, r_out, d_o, n_o, res_stride, nullptr, nullptr, nullptr, resid[0], ctx->post_norm[l], h));
+      lg.x = h;
+    }
+    TRY(run_linear<T>(ctx, lg));
+    Lin ld{};
+    ld.M = M; ld.N = H; ld.K = I; ld.W = ctx->down_w[l]; ld.x = act; ld.epi = EPI_F32; ld.out = d_d; ld.ldo = H;
+    ld.ksplit_ok = 1; ld.ksplit_used = &n_dd; ld.split_stride = res_stride;
+    TRY(run_linear<T>(ctx, ld));
+  }
+  // ---- final norm + LM head on the sampled rows
+  Lin lh{};
+  lh.N = c.vocab; lh.K = H; lh.W = c_lm_head_of(ctx); lh.epi = EPI_F32; lh.out = ctx->logits; lh.ldo = c.vocab;
+  if (logit_rows == nullptr && fuse_norm) {
+    lh.M = M; lh.norm = 1; lh.r_in = resid[0]; lh.delta = d_d; lh.n_delta = n_dd; lh.delta_stride = res_stride;
+    lh.gain = c_final_norm_of(ctx); lh.eps = c.rms_eps;
+  } else {
+    const int rows = logit_rows ? n_logits : M;
+    TRY(run_norm<T>(ctx, rows, resid[0], d_d, n_dd, res_stride, nullptr, nullptr, logit_rows, nullptr,
+                    c_final_norm_of(ctx), h));
+    lh.M = rows; lh.x = h;
+  }
+  TRY(run_linear<T>(ctx, lh));
+  return STEP_OK;
+}
+
+}  // namespace
+
+
+namespace {
+
+// Mixed-step metadata: rng[2] | tok | pos | slot | row_req | row_len [TM] | qsl [RM+1] | req_len [RM]
+// | bt [RM*W] | logit_idx [LM] | temp [LM] | tile_req [tiles] | tile_q0 [tiles]
+struct MixedMeta {
+  uint64_t* rng;
+  int *tok, *pos, *slot, *row_req, *row_len, *qsl, *req_len, *bt, *lidx;
+  float* temp;
+  int *tile_req, *tile_q0;
+};
+MixedMeta mixed_meta(char* base, const Layout& L, int W) {
+  MixedMeta m;
+  const int TM = L.TM, RM = L.RM, LM = L.LM;
+  const int tiles = TM / 16 + RM + 1;
+  m.rng = reinterpret_cast<uint64_t*>(base);
+  m.tok = reinterpret_cast<int*>(base + 16);
+  m.pos = m.tok + TM;
+  m.slot = m.pos + TM;
+  m.row_req = m.slot + TM;
+  m.row_len = m.row_req + TM;
+  m.qsl = m.row_len + TM;
+  m.req_len = m.qsl + RM + 1;
+  m.bt = m.req_len + RM;
+  m.lidx = m.bt + static_cast<size_t>(RM) * W;
+  m.temp = reinterpret_cast<float*>(m.lidx + LM);
+  m.tile_req = reinterpret_cast<int*>(m.temp + LM);
+  m.tile_q0 = m.tile_req + tiles;
+  return m;
+}
+
+template <class T>
+int run_decode(step_ctx* ctx, int B) {
+  const step_config& c = ctx->cfg;
+  const Layout& L = ctx->lay;
+  const int W = c.max_blocks_per_seq;
+  DecodeMeta m = decode_meta(ctx->ws + L.dmeta, c.max_batch, W);
+  const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
+  void* attn_o = ctx->ws + L.attn_o;
+  auto attn = [&](int l) {
+    return run_attn_rows<T>(ctx, l, B, q, m.bt, W, nullptr, m.len, c.max_position, attn_o);
+  };
+  TRY(run_layers<T>(ctx, B, m.ids, m.pos, m.slot, 0, nullptr, attn));
+  return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
+                    m.len, m.slot, m.bt, W, ctx->history, c.max_position);
+}
+
+int run_decode_any(step_ctx* ctx, int B) {
+  switch (ctx->cfg.dtype) {
+    case STEP_F32: return run_decode<F32>(ctx, B);
+    case STEP_BF16: return run_decode<BF16>(ctx, B);
+    default: return run_decode<F16>(ctx, B);
+  }
+}
+
+struct MixedPlan {
+  int T, n_pre_tok, n_pre_req, n_dec, n_logits, max_len, mode;
+};
+
+template <class T>
+int run_mixed(step_ctx* ctx, const MixedPlan& p) {
+  const step_config& c = ctx->cfg;
+  const Layout& L = ctx->lay;
+  const int W = c.max_blocks_per_seq;
+  MixedMeta m = mixed_meta(ctx->ws + L.mmeta, L, W);
+  const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
+  void* attn_o = ctx->ws + L.attn_o;
+  auto attn = [&](int l) -> int {
+    // one query row per token: prefill rows see keys [0, pos], decode rows their request's keys
+    return run_attn_rows<T>(ctx, l, p.T, q, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
+  };
+  TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, attn));
+  return run_sample(ctx, ctx->logits, p.n_logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0);
+}
+
+int run_mixed_any(step_ctx* ctx, const MixedPlan& p) {
+  switch (ctx->cfg.dtype) {
+    case STEP_F32: return run_mixed<F32>(ctx, p);
+    case STEP_BF16: return run_mixed<BF16>(ctx, p);
+    default: return run_mixed<F16>(ctx, p);
+  }
+}
+
+char* stage_slot(step_ctx* ctx, int* which) {
+  const int i = ctx->stage_next;
+  ctx->stage_next ^= 1;
+  // the previous copy out of this slot has completed
+  if (hipEventSynchronize(ctx->stage_ev[i]) != hipSuccess) return nullptr;
+  *which = i;
+  return ctx->h_stage[i];
+}
+
+// all decode rows padding: token 0, position 0, slot -1, length 0, zero table, greedy
+void fill_decode_padding(const step_config& c, char* base) {
+  DecodeMeta m = decode_meta(base, c.max_batch, c.max_blocks_per_seq);
+  m.rng[0] = 0;
+  m.rng[1] = 0;
+  for (int i = 0; i < c.max_batch; ++i) { m.ids[i] = 0; m.pos[i] = 0; m.slot[i] = -1; m.len[i] = 0; m.temp[i] = 0.f; }
+  std::memset(m.bt, 0, sizeof(int) * static_cast<size_t>(c.max_batch) * c.max_blocks_per_seq);
+}
+
+int bucket_of(const step_config& c, int r) {
+  for (int i = 0; i < c.num_buckets; ++i)
+    if (c.buckets[i] >= r) return c.buckets[i];
+  return -1;
+}
+
+int bucket_index(const step_config& c, int b) {
+  for (int i = 0; i < c.num_buckets; ++i)
+    if (c.buckets[i] == b) return i;
+  return -1;
+}
+
+}  // namespace
+
+// ================================================================================================
+// C ABI
+
+extern "C" size_t step_workspace_bytes(const step_config* cfg) {
+  if (validate_config(nullptr, cfg) != STEP_OK) return 0;
+  Layout L{};
+  compute_layout(*cfg, L);
+  return L.total;
+}
+
+extern "C" int step_init(const step_config* cfg, const step_weights* w, const step_buffers* b, void* stream,
+                         step_ctx** out) {
+  if (!out) return STEP_EINVAL;
+  *out = nullptr;
+  step_ctx* ctx = new step_ctx();
+  auto bail = [&](int rc) {
+    // keep the context so the caller can read the message; it is marked dead
+    ctx->dead = true;
+    *out = ctx;
+    return rc;
+  };
+  int rc = validate_config(ctx, cfg);
+  if (rc != STEP_OK) return bail(rc);
+  const step_config& c = *cfg;
+  ctx->cfg = c;
+  if (!w || !b) return bail(fail(ctx, STEP_EINVAL, "weights or buffers is NULL"));
+  if (!w->d_embed || !w->d_lm_head || !w->d_final_norm || !w->d_in_norm || !w->d_qkv_w || !w->d_o_w ||
+      !w->d_post_norm || !w->d_gate_up_w || !w->d_down_w)
+    return bail(fail(ctx, STEP_EINVAL, "a required weight pointer is NULL"));
+  if (c.qkv_bias && !w->d_qkv_b) return bail(fail(ctx, STEP_EINVAL, "qkv_bias set but d_qkv_b is NULL"));
+  if (c.qk_norm && (!w->d_q_norm || !w->d_k_norm)) return bail(fail(ctx, STEP_EINVAL, "qk_norm set but gains are NULL"));
+  ctx->w = *w;
+  for (int l = 0; l < c.layers; ++l) {
+    ctx->in_norm.push_back(w->d_in_norm[l]);
+    ctx->qkv_w.push_back(w->d_qkv_w[l]);
+    ctx->qkv_b.push_back(c.qkv_bias ? w->d_qkv_b[l] : nullptr);
+    ctx->q_norm.push_back(c.qk_norm ? w->d_q_norm[l] : nullptr);
+    ctx->k_norm.push_back(c.qk_norm ? w->d_k_norm[l] : nullptr);
+    ctx->o_w.push_back(w->d_o_w[l]);
+    ctx->post_norm.push_back(w->d_post_norm[l]);
+    ctx->gate_up_w.push_back(w->d_gate_up_w[l]);
+    ctx->down_w.push_back(w->d_down_w[l]);
+    if (!ctx->in_norm[l] || !ctx->qkv_w[l] || !ctx->o_w[l] || !ctx->post_norm[l] || !ctx->gate_up_w[l] ||
+        !ctx->down_w[l] || (c.qkv_bias && !ctx->qkv_b[l]) || (c.qk_norm && (!ctx->q_norm[l] || !ctx->k_norm[l])))
+      return bail(fail(ctx, STEP_EINVAL, "NULL weight pointer at layer %d", l));
+  }
+  if (!b->d_k_pool || !b->d_v_pool || !b->d_logits || !b->d_tokens || !b->d_workspace)
+    return bail(fail(ctx, STEP_EINVAL, "a required buffer pointer is NULL"));
+  for (int l = 0; l < c.layers; ++l) {
+    if (!b->d_k_pool[l] || !b->d_v_pool[l]) return bail(fail(ctx, STEP_EINVAL, "NULL KV pool at layer %d", l));
+    ctx->k_pool.push_back(b->d_k_pool[l]);
+    ctx->v_pool.push_back(b->d_v_pool[l]);
+  }
+  compute_layout(c, ctx->lay);
+  if (b->workspace_bytes < ctx->lay.total)
+    return bail(fail(ctx, STEP_EINVAL, "workspace has %zu bytes, needs %zu", b->workspace_bytes, ctx->lay.total));
+  if (reinterpret_cast<uintptr_t>(b->d_workspace) % kAlign)
+    return bail(fail(ctx, STEP_EINVAL, "workspace must be 256-byte aligned"));
+  ctx->ws = static_cast<char*>(b->d_workspace);
+  ctx->logits = b->d_logits;
+  ctx->tokens = b->d_tokens;
+  ctx->history = b->d_history;
+  ctx->stream = static_cast<hipStream_t>(stream);
+
+  auto hip_fail = [&](hipError_t e, const char* what) {
+    return bail(fail(ctx, STEP_EHIP, "%s failed: %s", what, hipGetErrorString(e)));
+  };
+  hipError_t e;
+  if ((e = hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking)) != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  ctx->stage_bytes = std::max(ctx->lay.dmeta_bytes, ctx->lay.mmeta_bytes);
+  ctx->stage_bytes = std::max(ctx->stage_bytes, sizeof(float) * static_cast<size_t>(ctx->lay.LM));
+  for (int i = 0; i < 2; ++i) {
+    if ((e = hipHostMalloc(reinterpret_cast<void**>(&ctx->h_stage[i]), ctx->stage_bytes, hipHostMallocDefault)) != hipSuccess)
+      return hip_fail(e, "hipHostMalloc");
+    if ((e = hipEventCreateWithFlags(&ctx->stage_ev[i], hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  // Everything below runs on the private stream, then the caller's stream waits for it.
+  hipStream_t s = ctx->cap_stream;
+  if ((e = hipMemsetAsync(ctx->ws, 0, ctx->lay.total, s)) != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
+  // RoPE table: angle = pos * theta^(-2i/d) in fp64, cos/sin rounded to fp32
+  {
+    const int half = c.head_dim / 2;
+    std::vector<float> cs(static_cast<size_t>(c.max_position) * half), sn(cs.size());
+    for (int p = 0; p < c.max_position; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double inv = std::pow(static_cast<double>(c.rope_theta), -2.0 * i / c.head_dim);
+        const double ang = static_cast<double>(p) * inv;
+        cs[static_cast<size_t>(p) * half + i] = static_cast<float>(std::cos(ang));
+        sn[static_cast<size_t>(p) * half + i] = static_cast<float>(std::sin(ang));
+      }
+    if ((e = hipMemcpy(ctx->ws + ctx->lay.rope_cos, cs.data(), sizeof(float) * cs.size(), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(rope)");
+    if ((e = hipMemcpy(ctx->ws + ctx->lay.rope_sin, sn.data(), sizeof(float) * sn.size(), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(rope)");
+  }
+  // zero the scratch block of every pool
+  const size_t blk_bytes = static_cast<size_t>(c.kv_heads) * 16 * c.head_dim * elem_bytes(c.dtype);
+  for (int l = 0; l < c.layers; ++l) {
+    if ((e = hipMemsetAsync(static_cast<char*>(ctx->k_pool[l]) + blk_bytes * (c.num_blocks - 1), 0, blk_bytes, s)) != hipSuccess)
+      return hip_fail(e, "hipMemsetAsync(scratch)");
+    if ((e = hipMemsetAsync(static_cast<char*>(ctx->v_pool[l]) + blk_bytes * (c.num_blocks - 1), 0, blk_bytes, s)) != hipSuccess)
+      return hip_fail(e, "hipMemsetAsync(scratch)");
+  }
+  fill_decode_padding(c, ctx->h_stage[0]);
+  if ((e = hipMemcpyAsync(ctx->ws + ctx->lay.dmeta, ctx->h_stage[0], ctx->lay.dmeta_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return hip_fail(e, "hipMemcpyAsync(meta)");
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+
+  ctx->graphs.assign(c.num_buckets, nullptr);
+  ctx->execs.assign(c.num_buckets, nullptr);
+  ctx->kernels_per_bucket.assign(c.num_buckets, 0);
+  hipStream_t user = ctx->stream;
+  ctx->stream = s;
+  for (int bi = c.num_buckets - 1; bi >= 0; --bi) {   // largest bucket first
+    const int B = c.buckets[bi];
+    // two warm-up steps over all-padding rows: only the scratch block is written
+    for (int wup = 0; wup < 2; ++wup) {
+      ctx->launches = 0;
+      rc = run_decode_any(ctx, B);
+      if (rc != STEP_OK) { ctx->stream = user; return bail(rc); }
+    }
+    ctx->kernels_per_bucket[bi] = ctx->launches;
+    if (!c.use_graphs) continue;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) { ctx->stream = user; return hip_fail(e, "hipStreamSynchronize"); }
+    if ((e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+      ctx->stream = user;
+      return bail(fail(ctx, STEP_ECAPTURE, "hipStreamBeginCapture: %s", hipGetErrorString(e)));
+    }
+    ctx->launches = 0;
+    rc = run_decode_any(ctx, B);
+    hipGraph_t g = nullptr;
+    hipError_t ee = hipStreamEndCapture(s, &g);
+    if (rc != STEP_OK || ee != hipSuccess || !g) {
+      ctx->stream = user;
+      if (g) (void)hipGraphDestroy(g);
+      return bail(rc != STEP_OK ? rc : fail(ctx, STEP_ECAPTURE, "hipStreamEndCapture: %s", hipGetErrorString(ee)));
+    }
+    hipGraphExec_t x = nullptr;
+    if ((e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0)) != hipSuccess) {
+      ctx->stream = user;
+      (void)hipGraphDestroy(g);
+      return bail(fail(ctx, STEP_ECAPTURE, "hipGraphInstantiate: %s", hipGetErrorString(e)));
+    }
+    ctx->graphs[bi] = g;
+    ctx->execs[bi] = x;
+  }
+  ctx->stream = user;
+  // warm-ups moved the Philox step counter: put the padding state back
+  fill_decode_padding(c, ctx->h_stage[0]);
+  if ((e = hipMemcpyAsync(ctx->ws + ctx->lay.dmeta, ctx->h_stage[0], ctx->lay.dmeta_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return hip_fail(e, "hipMemcpyAsync(meta)");
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  *out = ctx;
+  return STEP_OK;
+}
+
+extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  const step_config& c = ctx->cfg;
+  int B;
+  if (hb) {
+    const int r = hb->num_rows;
+    if (r < 1 || r > c.max_batch) return fail(ctx, STEP_EINVAL, "num_rows %d outside [1, %d]", r, c.max_batch);
+    if (hb->bt_width < 0 || hb->bt_width > c.max_blocks_per_seq)
+      return fail(ctx, STEP_EINVAL, "bt_width %d above max_blocks_per_seq %d", hb->bt_width, c.max_blocks_per_seq);
+    if (!hb->h_tokens || !hb->h_positions || !hb->h_seq_lens || !hb->h_slot_mapping || (hb->bt_width && !hb->h_block_table))
+      return fail(ctx, STEP_EINVAL, "NULL batch array");
+    B = bucket_of(c, r);
+    if (B < 0) return fail(ctx, STEP_EINVAL, "no bucket holds %d rows", r);
+    const int W = c.max_blocks_per_seq;
+    const int max_slot = (c.num_blocks - 1) * 16;   // slots of the scratch block are not addressable
+    for (int i = 0; i < r; ++i) {
+      const int t = hb->h_tokens[i], p = hb->h_positions[i], len = hb->h_seq_lens[i], sl = hb->h_slot_mapping[i];
+      if (t < 0 || t >= c.vocab) return fail(ctx, STEP_EINVAL, "row %d: token %d outside the vocabulary", i, t);
+      if (p < 0 || p >= c.max_position) return fail(ctx, STEP_EINVAL, "row %d: position %d outside [0, max_position)", i, p);
+      if (len < 0 || len > c.max_position || (len + 15) / 16 > hb->bt_width)
+        return fail(ctx, STEP_EINVAL, "row %d: seq_len %d needs more blocks than the table holds", i, len);
+      if (sl < -1 || sl >= max_slot) return fail(ctx, STEP_EINVAL, "row %d: slot %d outside the pool", i, sl);
+      for (int j = 0; j < hb->bt_width; ++j) {
+        const int blk = hb->h_block_table[static_cast<size_t>(i) * hb->bt_width + j];
+        if (blk < -1 || blk >= c.num_blocks - 1) return fail(ctx, STEP_EINVAL, "row %d: block id %d outside the pool", i, blk);
+        if (blk < 0 && j < (len + 15) / 16) return fail(ctx, STEP_EINVAL, "row %d: missing block %d of its keys", i, j);
+      }
+    }
+    int slot_i;
+    char* st = stage_slot(ctx, &slot_i);
+    if (!st) return fail(ctx, STEP_EHIP, "waiting for the staging buffer failed");
+    fill_decode_padding(c, st);
+    DecodeMeta m = decode_meta(st, c.max_batch, W);
+    m.rng[0] = hb->seed;
+    m.rng[1] = ctx->step_count;
+    for (int i = 0; i < r; ++i) {
+      m.ids[i] = hb->h_tokens[i];
+      m.pos[i] = hb->h_positions[i];
+      m.slot[i] = hb->h_slot_mapping[i];
+      m.len[i] = hb->h_seq_lens[i];
+      m.temp[i] = hb->h_temperature ? hb->h_temperature[i] : 0.f;
+      int* row = m.bt + static_cast<size_t>(i) * W;
+      for (int j = 0; j < W; ++j) row[j] = j < hb->bt_width ? hb->h_block_table[static_cast<size_t>(i) * hb->bt_width + j] : -1;
+    }
+    HIPCHK(ctx, hipMemcpyAsync(ctx->ws + ctx->lay.dmeta, st, ctx->lay.dmeta_bytes, hipMemcpyHostToDevice, ctx->stream));
+    HIPCHK(ctx, hipEventRecord(ctx->stage_ev[slot_i], ctx->stream));
+    ctx->last_bucket = B;
+    ctx->have_batch = true;
+  } else {
+    if (!ctx->have_batch) return fail(ctx, STEP_EINVAL, "continue step before any batch");
+    B = ctx->last_bucket;
+  }
+  const int bi = bucket_index(c, B);
+  if (ctx->execs[bi]) {
+    HIPCHK(ctx, hipGraphLaunch(ctx->execs[bi], ctx->stream));
+  } else {
+    ctx->launches = 0;
+    int rc = run_decode_any(ctx, B);
+    if (rc != STEP_OK) return rc;
+  }
+  ctx->step_count++;
+  return STEP_OK;
+}
+
+extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  const step_config& c = ctx->cfg;
+  if (!hp) return fail(ctx, STEP_EINVAL, "batch is NULL");
+  if (c.max_tokens <= 0) return fail(ctx, STEP_EINVAL, "context built without mixed-step buffers (max_tokens 0)");
+  const int T = hp->num_tokens, Rp = hp->num_prefill_reqs, Rd = hp->num_decode_reqs, R = Rp + Rd, NL = hp->num_logits;
+  const int W = c.max_blocks_per_seq;
+  if (T < 1 || T > c.max_tokens) return fail(ctx, STEP_EINVAL, "num_tokens %d outside [1, %d]", T, c.max_tokens);
+  if (Rp < 0 || Rd < 0 || R < 1 || R > c.max_reqs) return fail(ctx, STEP_EINVAL, "request count %d outside [1, %d]", R, c.max_reqs);
+  if (NL < 1 || NL > c.max_logit_rows) return fail(ctx, STEP_EINVAL, "num_logits %d outside [1, %d]", NL, c.max_logit_rows);
+  if (hp->bt_width < 1 || hp->bt_width > W) return fail(ctx, STEP_EINVAL, "bt_width %d outside [1, %d]", hp->bt_width, W);
+  if (!hp->h_query_start_loc || !hp->h_seq_lens || !hp->h_tokens || !hp->h_positions || !hp->h_slot_mapping ||
+      !hp->h_block_table || !hp->h_logits_indices)
+    return fail(ctx, STEP_EINVAL, "NULL batch array");
+  if (hp->prefill_attention != 0 && hp->prefill_attention != 1)
+    return fail(ctx, STEP_EINVAL, "prefill_attention must be 0 or 1");
+  const int* qsl = hp->h_query_start_loc;
+  if (qsl[0] != 0 || qsl[R] != T) return fail(ctx, STEP_EINVAL, "query_start_loc must run from 0 to num_tokens");
+  for (int j = 0; j < R; ++j) {
+    if (qsl[j + 1] <= qsl[j]) return fail(ctx, STEP_EINVAL, "request %d has no tokens", j);
+    if (j >= Rp && qsl[j + 1] - qsl[j] != 1) return fail(ctx, STEP_EINVAL, "decode request %d must have one token", j);
+    const int len = hp->h_seq_lens[j];
+    if (len < 1 || len > c.max_position || (len + 15) / 16 > hp->bt_width)
+      return fail(ctx, STEP_EINVAL, "request %d: seq_len %d does not fit the block table", j, len);
+    for (int b = 0; b < (len + 15) / 16; ++b) {
+      const int blk = hp->h_block_table[static_cast<size_t>(j) * hp->bt_width + b];
+      if (blk < 0 || blk >= c.num_blocks - 1) return fail(ctx, STEP_EINVAL, "request %d: block id %d outside the pool", j, blk);
+    }
+  }
+  const int max_slot = (c.num_blocks - 1) * 16;
+  int max_len = 1;
+  for (int j = 0; j < R; ++j)
+    for (int i = qsl[j]; i < qsl[j + 1]; ++i) {
+      const int t = hp->h_tokens[i], p = hp->h_positions[i], sl = hp->h_slot_mapping[i];
+      if (t < 0 || t >= c.vocab) return fail(ctx, STEP_EINVAL, "token row %d: id %d outside the vocabulary", i, t);
+      if (p < 0 || p >= hp->h_seq_lens[j]) return fail(ctx, STEP_EINVAL, "token row %d: position %d not below its seq_len", i, p);
+      if (sl < -1 || sl >= max_slot) return fail(ctx, STEP_EINVAL, "token row %d: slot %d outside the pool", i, sl);
+      max_len = std::max(max_len, p + 1);
+    }
+  for (int i = 0; i < NL; ++i)
+    if (hp->h_logits_indices[i] < 0 || hp->h_logits_indices[i] >= T)
+      return fail(ctx, STEP_EINVAL, "logits index %d outside the packed tokens", hp->h_logits_indices[i]);
+  if (hp->prefill_attention == 0 && c.dtype != STEP_F32) {
+    // packed causal prefill kernel: built in a later change; fall through to rows until then
+  }
+  int slot_i;
+  char* st = stage_slot(ctx, &slot_i);
+  if (!st) return fail(ctx, STEP_EHIP, "waiting for the staging buffer failed");
+  MixedMeta m = mixed_meta(st, ctx->lay, W);
+  m.rng[0] = hp->seed;
+  m.rng[1] = ctx->step_count;
+  for (int j = 0; j < R; ++j) {
+    for (int i = qsl[j]; i < qsl[j + 1]; ++i) {
+      m.tok[i] = hp->h_tokens[i];
+      m.pos[i] = hp->h_positions[i];
+      m.slot[i] = hp->h_slot_mapping[i];
+      m.row_req[i] = j;
+      m.row_len[i] = (j < Rp) ? hp->h_positions[i] + 1 : hp->h_seq_lens[j];
+    }
+    m.req_len[j] = hp->h_seq_lens[j];
+    int* row = m.bt + static_cast<size_t>(j) * W;
+    for (int b = 0; b < W; ++b) row[b] = b < hp->bt_width ? hp->h_block_table[static_cast<size_t>(j) * hp->bt_width + b] : -1;
+  }
+  for (int j = 0; j <= R; ++j) m.qsl[j] = qsl[j];
+  for (int i = 0; i < NL; ++i) {
+    m.lidx[i] = hp->h_logits_indices[i];
+    m.temp[i] = hp->h_temperature ? hp->h_temperature[i] : 0.f;
+  }
+  HIPCHK(ctx, hipMemcpyAsync(ctx->ws + ctx->lay.mmeta, st, ctx->lay.mmeta_bytes, hipMemcpyHostToDevice, ctx->stream));
+  HIPCHK(ctx, hipEventRecord(ctx->stage_ev[slot_i], ctx->stream));
+  MixedPlan p{T, qsl[Rp], Rp, Rd, NL, max_len, hp->prefill_attention};
+  ctx->launches = 0;
+  int rc = run_mixed_any(ctx, p);
+  if (rc != STEP_OK) return rc;
+  ctx->step_count++;
+  return STEP_OK;
+}
+
+extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, int32_t ld, int32_t vocab,
+                           const float* h_temperature, const float* d_uniforms, uint64_t seed, uint64_t counter,
+                           int32_t* d_tokens_out) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  if (!d_logits || !d_tokens_out) return fail(ctx, STEP_EINVAL, "NULL logits or tokens");
+  if (rows < 1 || rows > ctx->lay.LM) return fail(ctx, STEP_EINVAL, "rows %d outside [1, %d]", rows, ctx->lay.LM);
+  if (vocab < 1 || vocab > ctx->cfg.vocab || ld < vocab) return fail(ctx, STEP_EINVAL, "bad vocab %d / ld %d", vocab, ld);
+  float* temp = nullptr;
+  if (h_temperature) {
+    int slot_i;
+    char* st = stage_slot(ctx, &slot_i);
+    if (!st) return fail(ctx, STEP_EHIP, "waiting for the staging buffer failed");
+    std::memcpy(st, h_temperature, sizeof(float) * rows);
+    temp = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_temp);
+    HIPCHK(ctx, hipMemcpyAsync(temp, st, sizeof(float) * rows, hipMemcpyHostToDevice, ctx->stream));
+    HIPCHK(ctx, hipEventRecord(ctx->stage_ev[slot_i], ctx->stream));
+  }
+  return run_sample(ctx, d_logits, rows, ld, vocab, temp, d_uniforms, nullptr, seed, counter, d_tokens_out, 0, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0);
+}
+
+extern "C" int step_last_bucket(const step_ctx* ctx) { return ctx ? ctx->last_bucket : STEP_ESTATE; }
+
+extern "C" int step_kernels_per_decode(const step_ctx* ctx, int32_t bucket) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  const int bi = bucket_index(ctx->cfg, bucket);
+  if (bi < 0) return STEP_EINVAL;
+  return ctx->kernels_per_bucket[bi];
+}
+
+extern "C" const char* step_last_error(const step_ctx* ctx) { return ctx ? ctx->err.c_str() : "NULL context"; }
+
+extern "C" void step_destroy(step_ctx* ctx) {
+  if (!ctx) return;
+  // teardown is best effort: errors here have no caller left to report to
+  if (ctx->cap_stream) (void)hipStreamSynchronize(ctx->cap_stream);
+  if (ctx->stream || !ctx->dead) (void)hipStreamSynchronize(ctx->stream);
+  for (auto& x : ctx->execs)
+    if (x) (void)hipGraphExecDestroy(x);
+  for (auto& g : ctx->graphs)
+    if (g) (void)hipGraphDestroy(g);
+  for (int i = 0; i < 2; ++i) {
+    if (ctx->stage_ev[i]) (void)hipEventDestroy(ctx->stage_ev[i]);
+    if (ctx->h_stage[i]) (void)hipHostFree(ctx->h_stage[i]);
+  }
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  delete ctx;
+}

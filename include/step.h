@@ -1,0 +1,165 @@
+/* step.h - C ABI of libstep: one decode or mixed step of a dense decoder-only transformer
+ * (RMSNorm, fused QKV with optional bias and per-head QK-norm, rotate-half RoPE, paged KV,
+ * GQA attention, SwiGLU MLP, tied or untied LM head) on one AMD Instinct MI355X (gfx950).
+ *
+ * The method these calls implement is described on the pages:
+ *   - "Removing overhead: fusion, graphs and async scheduling", sections "Fewer, larger matmuls"
+ *     (stacked [W_Q | W_K | W_V] and [W_gate | W_up] projections, fused norm/activation) and
+ *     "CUDA graphs for a changing batch" (one graph per batch-size bucket over static buffers,
+ *     padding rows with slot -1 and length 0, eager fallback over the same buffers);
+ *   - "Fast decode: syncs, CUDA graphs and compilation", sections "Sampling without the CPU"
+ *     (Gumbel-max on the device), "Static shapes and a static cache" and "The fast decoder"
+ *     (the step touches only static buffers and advances token and position in place);
+ *   - "One forward per step", section "What changed" (prefill chunks first and decode rows last
+ *     in one packed forward; attention splits by kind inside the call).
+ *
+ * Conventions
+ *   - Every pointer named d_* is DEVICE memory; h_* is HOST memory. The caller owns all of it.
+ *     The library borrows the pointers passed to step_init for the context's lifetime and
+ *     allocates no device memory after step_init returns; it owns only the context, its
+ *     graphs and a small pinned host staging area.
+ *   - Matrices are row-major [out_features][in_features] in the model dtype.
+ *   - The KV pool of each layer is [num_blocks][kv_heads][block_size][head_dim] in the model
+ *     dtype, zero-filled by the caller. Block num_blocks-1 is the scratch block: it must never
+ *     appear in a block table; rows with slot -1 write there.
+ *   - A token at absolute position p of a request whose block-table row is bt lives at slot
+ *     bt[p / block_size] * block_size + p % block_size.
+ *   - seq_len of a decode row counts the keys the row attends to INCLUDING its own token
+ *     (cached + 1). A row with seq_len 0 is padding and produces a zero attention output.
+ *   - Calls only enqueue work on the context's stream; nothing synchronises the stream except
+ *     step_init (capture) and step_destroy. Outputs are valid once the stream reaches them.
+ *   - Every function returns STEP_OK (0) or a negative error code and never throws; the
+ *     message of the last error is in step_last_error(ctx).
+ */
+#ifndef GRAPH_REPLAY_AMD_STEP_H
+#define GRAPH_REPLAY_AMD_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  STEP_OK = 0,
+  STEP_EINVAL = -1,        /* bad sizes, counts, pointers or a row count above the largest bucket */
+  STEP_EUNSUPPORTED = -2,  /* a dtype / flag combination this build has no kernels for */
+  STEP_EHIP = -3,          /* a HIP runtime call failed (message holds hipGetErrorString) */
+  STEP_ECAPTURE = -4,      /* graph capture or instantiation failed */
+  STEP_ESTATE = -5         /* call on a NULL or destroyed context */
+};
+enum { STEP_F32 = 0, STEP_BF16 = 1, STEP_F16 = 2 };
+#define STEP_MAX_BUCKETS 16
+
+typedef struct step_ctx step_ctx;
+
+typedef struct {
+  int32_t dtype;                 /* STEP_F32 / STEP_BF16 / STEP_F16: weights, KV pool, matmul inputs */
+  int32_t layers, hidden, q_heads, kv_heads, head_dim, intermediate, vocab;
+  int32_t qk_norm;               /* 1: per-head RMSNorm of q and k (one gain [head_dim] each) before RoPE */
+  int32_t qkv_bias;              /* 1: bias [q_heads+2*kv_heads][head_dim] added after the QKV matmul */
+  float rms_eps, rope_theta;
+  int32_t block_size;            /* KV block size in tokens (16) */
+  int32_t num_blocks;            /* blocks per layer pool, including the scratch block */
+  int32_t max_blocks_per_seq;    /* block-table row width */
+  int32_t max_position;          /* positions are in [0, max_position) */
+  int32_t max_batch;             /* largest decode row count (== the largest bucket) */
+  int32_t max_tokens;            /* largest packed token count of a mixed step (0: no mixed steps) */
+  int32_t max_reqs;              /* largest request count of a mixed step */
+  int32_t max_logit_rows;        /* largest number of sampled rows of a mixed step */
+  int32_t num_buckets;           /* ascending decode batch sizes; the last must equal max_batch */
+  int32_t buckets[STEP_MAX_BUCKETS];
+  int32_t use_graphs;            /* 1: capture one hipGraph per bucket at init; 0: launch eagerly */
+} step_config;
+
+typedef struct {
+  const void *d_embed;           /* [vocab][hidden] */
+  const void *d_lm_head;         /* [vocab][hidden]; equal to d_embed for tied embeddings */
+  const void *d_final_norm;      /* [hidden] */
+  /* host arrays of `layers` device pointers each */
+  const void *const *d_in_norm;    /* [hidden] */
+  const void *const *d_qkv_w;      /* [(q_heads+2*kv_heads)*head_dim][hidden]: rows of W_Q, then W_K, then W_V */
+  const void *const *d_qkv_b;      /* [(q_heads+2*kv_heads)*head_dim] or NULL array when qkv_bias == 0 */
+  const void *const *d_q_norm;     /* [head_dim] or NULL array when qk_norm == 0 */
+  const void *const *d_k_norm;     /* [head_dim] or NULL array when qk_norm == 0 */
+  const void *const *d_o_w;        /* [hidden][q_heads*head_dim] */
+  const void *const *d_post_norm;  /* [hidden] */
+  const void *const *d_gate_up_w;  /* [2*intermediate][hidden]: rows of W_gate, then W_up */
+  const void *const *d_down_w;     /* [hidden][intermediate] */
+} step_weights;
+
+typedef struct {
+  void *const *d_k_pool;         /* host array of `layers` device pointers (pool layout above) */
+  void *const *d_v_pool;
+  float *d_logits;               /* [max(max_batch, max_logit_rows)][vocab] fp32 output */
+  int32_t *d_tokens;             /* [max(max_batch, max_logit_rows)] sampled token ids */
+  int32_t *d_history;            /* optional [max_batch][max_position]: decode row b's sampled token is
+                                    stored at [b][its input position]; NULL to skip */
+  void *d_workspace;             /* >= step_workspace_bytes(cfg) bytes, 256-byte aligned */
+  size_t workspace_bytes;
+} step_buffers;
+
+/* One decode step of r rows (host arrays of length r; block_table is r x bt_width). */
+typedef struct {
+  int32_t num_rows, bt_width;
+  const int32_t *h_tokens, *h_positions, *h_seq_lens, *h_slot_mapping, *h_block_table;
+  const float *h_temperature;    /* [num_rows]; NULL => all greedy; 0 => greedy row */
+  uint64_t seed;                 /* Philox key for the Gumbel noise of this and later continued steps */
+} step_batch;
+
+/* One packed mixed step: prefill requests first (their chunk tokens contiguous), decode requests
+ * last (one token each). Host arrays. */
+typedef struct {
+  int32_t num_tokens, num_prefill_reqs, num_decode_reqs, num_logits, bt_width;
+  const int32_t *h_query_start_loc;  /* [reqs+1] token offsets of each request in the packed sequence */
+  const int32_t *h_seq_lens;         /* [reqs] keys after this step (cached + new tokens) */
+  const int32_t *h_tokens, *h_positions, *h_slot_mapping;   /* [num_tokens] */
+  const int32_t *h_block_table;      /* [reqs][bt_width] */
+  const int32_t *h_logits_indices;   /* [num_logits] packed token rows whose logits are computed */
+  const float *h_temperature;        /* [num_logits] or NULL (greedy) */
+  uint64_t seed;
+  int32_t prefill_attention;         /* 0: packed MFMA kernel (16-bit dtypes); 1: one query row per token */
+} step_packed;
+
+/* Device bytes the workspace must hold for this configuration (0 if the configuration is invalid). */
+size_t step_workspace_bytes(const step_config *cfg);
+
+/* Validate, carve the workspace, build the RoPE table (fp64 angles rounded to fp32), zero the
+ * scratch block, and capture one graph per bucket (largest first, after two warm-up runs) when
+ * use_graphs is set. `stream` is a hipStream_t (NULL: the null stream). */
+int step_init(const step_config *cfg, const step_weights *w, const step_buffers *b, void *stream,
+              step_ctx **out);
+
+/* Decode step over r = h_batch->num_rows rows. 1 <= r <= max_batch, bt_width <= max_blocks_per_seq,
+ * else STEP_EINVAL. The rows are copied into the static buffers and padded up to the smallest
+ * bucket >= r (token 0, position 0, slot -1, seq_len 0, zero block-table row); the bucket's graph
+ * is replayed (or its kernels launched eagerly). h_batch == NULL continues on the device: the
+ * previous step's sampled tokens become the inputs, positions and seq_lens advance by one and the
+ * slots are recomputed from the block table; the padded row count stays that of the last batch.
+ * Logits rows [0, r) and tokens [0, r) are written. */
+int step_decode(step_ctx *ctx, const step_batch *h_batch);
+
+/* Mixed (or pure prefill) step, run eagerly: all tokens go through every layer once; prefill
+ * attention is packed and causal per request, decode rows attend one query row per request; logits
+ * and tokens are produced for h_logits_indices only (rows [0, num_logits) of the outputs). */
+int step_mixed(step_ctx *ctx, const step_packed *h_batch);
+
+/* Standalone sampler over d_logits [rows][ld] fp32: temperature h_temperature[row] (NULL: greedy);
+ * d_uniforms [rows][ld] fp32 supplies the uniforms (NULL: Philox-4x32-10 keyed by seed with step
+ * counter `counter`). Writes d_tokens_out[rows]. */
+int step_sample(step_ctx *ctx, const float *d_logits, int32_t rows, int32_t ld, int32_t vocab,
+                const float *h_temperature, const float *d_uniforms, uint64_t seed, uint64_t counter,
+                int32_t *d_tokens_out);
+
+/* Rows of the bucket the last decode step ran at, and kernels launched per decode step. */
+int step_last_bucket(const step_ctx *ctx);
+int step_kernels_per_decode(const step_ctx *ctx, int32_t bucket);
+
+const char *step_last_error(const step_ctx *ctx);
+void step_destroy(step_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
