@@ -1,0 +1,252 @@
+"""Decode-step throughput on one MI355X at the Qwen3-0.6B shape (bf16, random N(0, 0.02) weights).
+
+One "step" is one whole decode step (every layer, LM head, sampling, device-side advance), replayed
+as the bucket's hipGraph. The primary line is batch 1 with a 1,024-token context built by a real
+prefill; the same JSON line carries the batch-32 workload (contexts uniform in [128, 2048], shuffled
+paged KV, Gumbel-max at T = 1) under "bs32". Inputs are resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-bs32] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, vendor figure
+METRIC = "decode tokens/s/GPU at Qwen3-0.6B shape, bs 1 & 32; % of HBM roofline"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kind_bytes(shape, rows: int, seq_lens_sum: int) -> dict:
+    """Algorithmic HBM bytes of ONE launch of each kernel kind in a decode step of `rows` rows."""
+    eb = shape.elem_bytes
+    H, I, V, d = shape.hidden, shape.intermediate, shape.vocab, shape.head_dim
+    nq, nkv = shape.q_heads, shape.kv_heads
+    qkv = shape.qkv_out
+    return {
+        "qkv_proj": qkv * H * eb + rows * qkv * 4,
+        "o_proj": H * nq * d * eb + rows * H * 4,
+        "gate_up_silu": 2 * I * H * eb + rows * I * eb,
+        "down_proj": H * I * eb + rows * H * 4,
+        "lm_head": V * H * eb + rows * V * 4,
+        "attn_decode": seq_lens_sum * 2 * nkv * d * eb + rows * nq * d * (4 + eb),
+        "qknorm_rope_kvwrite": rows * (qkv * 4 + nq * d * 4 + 2 * nkv * d * eb),
+        "sample": rows * V * 4,
+        "add_rmsnorm": rows * H * (4 + 4 + 4 + eb),
+    }
+
+
+def step_bytes(shape, seq_lens_sum: int) -> int:
+    """Weights + KV read by one decode step (the roofline numerator)."""
+    weights = synth.num_params(shape) * shape.elem_bytes
+    kv = seq_lens_sum * shape.layers * 2 * shape.kv_heads * shape.head_dim * shape.elem_bytes
+    return weights + kv
+
+
+def timed_replays(dec, steps: int):
+    torch = dec.torch
+    s = dec.stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        dec.decode_continue()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int) -> dict:
+    prof = dec.profile_decode()
+    per = {}
+    for name, ms in prof:
+        t = per.setdefault(name, [0.0, 0])
+        t[0] += ms
+        t[1] += 1
+    dom = max(per, key=lambda k: per[k][0])
+    avg_ms = per[dom][0] / per[dom][1]
+    nbytes = kind_bytes(shape, rows, seq_lens_sum)[dom]
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    table = {k: {"launches": v[1], "total_us": round(v[0] * 1e3, 1), "avg_us": round(v[0] * 1e3 / v[1], 2)}
+             for k, v in sorted(per.items(), key=lambda kv: -kv[1][0])}
+    return {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_ms * 1e3, 2),
+            "profile_sum_us": round(sum(ms for _, ms in prof) * 1e3, 1), "kernels": table}
+
+
+def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024):
+    import graph_replay_amd as g
+    torch = __import__("torch")
+    total = ctx_len + 1 + warmup + steps + 2            # positions used, profile step included
+    table = synth.block_tables([total], -(-total // 16) + 2, 1002, shuffled=False)[0]
+    nb = len(table) + 2
+    dec = g.Decoder(shape, W, num_blocks=nb, max_blocks_per_seq=len(table), max_position=total + 16, max_batch=1,
+                    buckets=[1], max_tokens=ctx_len, max_reqs=1, max_logit_rows=1)
+    bt = np.asarray([table], np.int32)
+    prompt = synth.tokens(ctx_len, shape.vocab, 1002)
+    pos = np.arange(ctx_len, dtype=np.int32)
+    slots = (bt[0][pos // 16] * 16 + pos % 16).astype(np.int32)
+    log("prefill", ctx_len, "tokens")
+    dec.mixed([0, ctx_len], [ctx_len], prompt, pos, slots, bt, [ctx_len - 1], num_prefill_reqs=1)
+    torch.cuda.synchronize()
+    first = int(dec.tokens[0].item())
+    p = ctx_len
+    dec.decode([first], [p], [p + 1], [int(bt[0][p // 16] * 16 + p % 16)], bt)
+    for _ in range(warmup - 1):
+        dec.decode_continue()
+    torch.cuda.synchronize()
+    start_len = ctx_len + 1 + warmup                      # seq_len of the first timed step
+    log("timing", steps, "bs1 steps")
+    ms = timed_replays(dec, steps)
+    seq_sum_mean = start_len + (steps - 1) / 2.0
+    nbytes = step_bytes(shape, seq_sum_mean)
+    ms_step = ms / steps
+    roof = roofline_from_profile(shape, dec, 1, start_len + steps)
+    out = {
+        "tok_s": steps / (ms * 1e-3), "ms_per_step": ms_step, "bytes_per_step": int(nbytes),
+        "step_hbm_GBps": nbytes / (ms_step * 1e-3) / 1e9, "kernels_per_step": dec.kernels_per_decode(1),
+        "roofline": roof,
+    }
+    out["step_hbm_frac"] = out["step_hbm_GBps"] / PEAK_HBM_GBS
+    dec.close()
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_bs32(shape, W, steps: int, warmup: int):
+    import graph_replay_amd as g
+    torch = __import__("torch")
+    wl = synth.workload_q3_bs32()
+    ctx = wl.contexts
+    B = len(ctx)
+    need = [c + 1 + warmup + steps + 2 for c in ctx]
+    nb = sum(-(-n // 16) for n in need) + 2
+    tables = synth.block_tables(need, nb, 1003, shuffled=True)
+    width = max(len(t) for t in tables)
+    dec = g.Decoder(shape, W, num_blocks=nb, max_blocks_per_seq=width, max_position=max(need) + 16, max_batch=B,
+                    buckets=[1, 2, 4, 8, 16, 32])
+    gen = torch.Generator(device=dec.device)
+    gen.manual_seed(1003)
+    for l in range(shape.layers):                       # seeded N(0, 1) KV history, resident in HBM
+        dec.k_pool[l].normal_(generator=gen)
+        dec.v_pool[l].normal_(generator=gen)
+    bt = np.full((B, width), -1, np.int32)
+    for j, t in enumerate(tables):
+        bt[j, :len(t)] = t
+    pos = np.asarray(ctx, np.int32)
+    slots = np.array([bt[j][pos[j] // 16] * 16 + pos[j] % 16 for j in range(B)], np.int32)
+    toks = synth.tokens(B, shape.vocab, 1003)
+    dec.decode(toks, pos, pos + 1, slots, bt, temperature=np.ones(B, np.float32), seed=1003)
+    for _ in range(warmup - 1):
+        dec.decode_continue()
+    torch.cuda.synchronize()
+    log("timing", steps, "bs32 steps")
+    ms = timed_replays(dec, steps)
+    start_sum = sum(c + 1 + warmup for c in ctx)
+    seq_sum_mean = start_sum + B * (steps - 1) / 2.0
+    nbytes = step_bytes(shape, seq_sum_mean)
+    ms_step = ms / steps
+    roof = roofline_from_profile(shape, dec, B, start_sum + B * steps)
+    out = {"workload": wl.name, "batch": B, "tok_s": B * steps / (ms * 1e-3), "ms_per_step": ms_step,
+           "bytes_per_step": int(nbytes), "step_hbm_GBps": nbytes / (ms_step * 1e-3) / 1e9,
+           "kernels_per_step": dec.kernels_per_decode(32), "roofline": roof}
+    out["step_hbm_frac"] = out["step_hbm_GBps"] / PEAK_HBM_GBS
+    dec.close()
+    return out
+
+
+def cpu_baseline(shape, W, budget_s: float = 20.0, ctx_len: int = 1024) -> dict:
+    """The oracle (fp32 NumPy, unfused, per request) timed on this host on a bounded sample: decode
+    steps of one request over a 1,024-key injected history (same shape as the GPU workload)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    w32 = {"embed": W["embed"].float().numpy(), "final_norm": W["final_norm"].float().numpy(),
+           "layers": [{k: (None if v is None else v.float().numpy()) for k, v in l.items()} for l in W["layers"]]}
+    w32["lm_head"] = w32["embed"]
+    cache = oracle.RequestCache(shape.layers)
+    for l in range(shape.layers):
+        k, v = synth.injected_kv(shape, 1002, 0, l, ctx_len)
+        cache.set(l, k.float().numpy(), v.float().numpy())
+    tok = int(synth.tokens(1, shape.vocab, 5)[0])
+    times = []
+    t_start = time.perf_counter()
+    p = ctx_len
+    while True:
+        t0 = time.perf_counter()
+        hid = oracle.forward_request(shape, w32, cache, [tok], [p])
+        tok = int(oracle.sample(oracle.final_logits(w32, hid), 0.0)[0])
+        times.append(time.perf_counter() - t0)
+        p += 1
+        if time.perf_counter() - t_start > budget_s or len(times) >= 64:
+            break
+    med = float(np.median(times[1:] if len(times) > 2 else times))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    return {"value": round(1.0 / med, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} greedy decode steps of one request over a {ctx_len}-key injected history, "
+                      f"Qwen3-0.6B shape fp32 NumPy; median step {med * 1e3:.1f} ms",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-bs32", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by request, with no exchange between GPUs)", file=sys.stderr)
+        sys.exit(2)
+    warmup = max(1, args.warmup)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    import graph_replay_amd as g
+    g.load()
+    shape = synth.QWEN3_0_6B
+    log("weights")
+    W = synth.make_weights(shape, 0)
+    r1 = run_bs1(shape, W, args.steps, warmup)
+    r32 = None if args.no_bs32 else run_bs32(shape, W, args.steps, warmup)
+    cpu = None if args.no_cpu else cpu_baseline(shape, W)
+    line = {
+        "metric": METRIC, "value": round(r1["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": warmup, "ms_per_step": round(r1["ms_per_step"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3-0.6b-bf16-decode-bs1-ctx1024", "batch": 1, "context": 1024,
+                   "decode_steps": args.steps, "graph": "one hipGraph replay per step",
+                   "kernels_per_step": r1["kernels_per_step"]},
+        "step_hbm": {"bytes_per_step": r1["bytes_per_step"], "achieved": round(r1["step_hbm_GBps"], 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r1["step_hbm_frac"], 4)},
+        "roofline": r1["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if r32 is not None:
+        line["bs32"] = {"workload": r32["workload"], "value": round(r32["tok_s"], 1), "unit": "tokens/s",
+                        "ms_per_step": round(r32["ms_per_step"], 4), "kernels_per_step": r32["kernels_per_step"],
+                        "step_hbm": {"bytes_per_step": r32["bytes_per_step"], "achieved": round(r32["step_hbm_GBps"], 1),
+                                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r32["step_hbm_frac"], 4)},
+                        "roofline": r32["roofline"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -245,6 +245,17 @@ class Decoder:
                     uniforms.data_ptr() if uniforms is not None else None, seed, counter, out.data_ptr())
         return out
 
+    def profile_decode(self, max_kernels: int = 4096):
+        """One eager, event-timed decode step (advances the state). Returns [(kind name, ms), ...]."""
+        lib = _lib.load()
+        ms = np.zeros(max_kernels, np.float32)
+        kind = np.zeros(max_kernels, np.int32)
+        n = lib.step_profile_decode(self.ctx, max_kernels, _fp(ms), _ip(kind))
+        if n < 0:
+            _raise(n, self.ctx)
+        n = min(n, max_kernels)
+        return [(lib.step_kernel_kind_name(int(kind[i])).decode(), float(ms[i])) for i in range(n)]
+
     def last_bucket(self) -> int:
         return int(_lib.load().step_last_bucket(self.ctx))
 

@@ -56,6 +56,8 @@ EXPORTS = {
     "step_decode": (C.c_int, [P, C.POINTER(StepBatch)]),
     "step_mixed": (C.c_int, [P, C.POINTER(StepPacked)]),
     "step_sample": (C.c_int, [P, F32P, C.c_int32, C.c_int32, C.c_int32, F32P, F32P, C.c_uint64, C.c_uint64, I32P]),
+    "step_profile_decode": (C.c_int, [P, C.c_int32, F32P, I32P]),
+    "step_kernel_kind_name": (C.c_char_p, [C.c_int32]),
     "step_last_bucket": (C.c_int, [P]),
     "step_kernels_per_decode": (C.c_int, [P, C.c_int32]),
     "step_last_error": (C.c_char_p, [P]),

@@ -77,9 +77,22 @@ __global__ __launch_bounds__(64) void k_qkv_post(int nq, int nkv, int d, const f
 
 struct AttnRowsArgs {
   int nq, nkv;
-  const float* q;            // [rows][nq][D] fp32
-  const void* k_pool;
-  const void* v_pool;
+  const float* q;            // [rows][nq][D] fp32 (prepared queries), or nullptr when fused below
+  // fused decode prologue (q == nullptr): q, k from the QKV projection output (sum of n_parts
+  // fp32 partials [rows][(nq + 2 nkv) D]), QK-RMSNorm + RoPE here; the split holding key L-1 of
+  // a row writes the row's new K and V to its slot before any key of the split is read
+  const float* qkv;
+  int n_parts;
+  size_t part_stride;
+  const int* pos;
+  const int* slot;
+  const float* rope_cos;
+  const float* rope_sin;
+  const void* q_norm;
+  const void* k_norm;
+  float eps;
+  void* k_pool;
+  void* v_pool;
   const int* block_table;    // [reqs][bt_stride]
   int bt_stride;
   const int* row_req;        // row -> block-table row (nullptr: identity)
@@ -88,17 +101,38 @@ struct AttnRowsArgs {
   int max_splits;            // gridDim.z
   int num_blocks;            // pool blocks; a negative table entry reads the scratch block
   void* out;                 // [rows][nq * D] in the model dtype
-  float* partials;           // [rows][nq][max_splits][D + 2]
-  unsigned* counters;        // [rows][nkv], zero between launches
+  float* partials;           // [rows][nq][max_splits][D + 2]: (max, sum, unnormalised output)
   float scale;
 };
 
-// Decode attention with one query row per request ("One forward per step", section "What
-// changed"), split over the key range so that short batches still fill the GPU (the same page,
-// section "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers
-// keys [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends
-// on the bucket only and replays as captured. The splits of a (row, kv head) each write
-// (max, sum, unnormalised output) and the last to finish combines them in split order.
+// RMSNorm over one head (optional gain) then rotate-half RoPE: lane holds the pair (lane, lane+D/2).
+template <class T, int D>
+__device__ inline void norm_rope_pair(float& x0, float& x1, const void* gain, float eps, float c, float s) {
+  using S = typename T::S;
+  constexpr int half = D / 2;
+  const int lane = threadIdx.x & 63;
+  const bool act = lane < half;
+  if (gain) {
+    const float ss = wave_sum(act ? x0 * x0 + x1 * x1 : 0.f);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+    const S* gw = static_cast<const S*>(gain);
+    if (act) {
+      x0 = x0 * inv * T::to_f(gw[lane]);
+      x1 = x1 * inv * T::to_f(gw[lane + half]);
+    }
+  }
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x1 * c + x0 * s;
+  x0 = y0;
+  x1 = y1;
+}
+
+// Attention with one query row per request ("One forward per step", section "What changed"),
+// split over the key range so that short batches still fill the GPU (the same page, section
+// "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers keys
+// [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends on
+// the bucket only and replays as captured. A row with one split writes its output; otherwise each
+// split writes (max, sum, unnormalised output) and k_attn_combine merges them in split order.
 // Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv query
 // heads sharing the KV head are processed together.
 template <class T, int D, int G>
@@ -106,10 +140,11 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   using S = typename T::S;
   constexpr int KL = D / 8;          // dims per lane in the score phase (8 lanes per key)
   constexpr int VG = 64 / (D / 8);   // key groups in the value phase (lane owns 8 dims)
+  constexpr int half = D / 2;
   __shared__ float p_s[4][G][kBlk];
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wo[4][G][D];
-  __shared__ int last_flag;
+  __shared__ float qs[G][D];
   const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int L = a.seq_lens[row];
@@ -126,13 +161,57 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   const int req = a.row_req ? a.row_req[row] : row;
   const int* bt = a.block_table + static_cast<size_t>(req) * a.bt_stride;
 
-  // query heads g*G .. g*G+G-1, score-phase slice of this lane: dims (lane % 8) * KL .. + KL
+  // queries of heads g*G .. g*G+G-1 into LDS (scaled by 1/sqrt(D))
+  if (a.q) {
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+      qs[i / D][i % D] = a.q[(static_cast<size_t>(row) * a.nq + g * G) * D + i] * a.scale;
+  } else {
+    const int ld = (a.nq + 2 * a.nkv) * D;
+    const int p = a.pos[row];
+    const bool act = lane < half;
+    const float c = act ? a.rope_cos[static_cast<size_t>(p) * half + lane] : 0.f;
+    const float sn = act ? a.rope_sin[static_cast<size_t>(p) * half + lane] : 0.f;
+    auto fetch = [&](int col) -> float {
+      float v = 0.f;
+      for (int k = 0; k < a.n_parts; ++k) v += a.qkv[k * a.part_stride + static_cast<size_t>(row) * ld + col];
+      return v;
+    };
+    for (int j = wid; j < G; j += 4) {
+      const int col = (g * G + j) * D;
+      float x0 = act ? fetch(col + lane) : 0.f, x1 = act ? fetch(col + lane + half) : 0.f;
+      norm_rope_pair<T, D>(x0, x1, a.q_norm, a.eps, c, sn);
+      if (act) {
+        qs[j][lane] = x0 * a.scale;
+        qs[j][lane + half] = x1 * a.scale;
+      }
+    }
+    if (sp == nsplit - 1 && wid == 3) {
+      // this split holds key L-1: write the row's new K and V before reading any key
+      const int kcol = (a.nq + g) * D, vcol = (a.nq + a.nkv + g) * D;
+      float k0 = act ? fetch(kcol + lane) : 0.f, k1 = act ? fetch(kcol + lane + half) : 0.f;
+      norm_rope_pair<T, D>(k0, k1, a.k_norm, a.eps, c, sn);
+      const int sl = a.slot[row];
+      const int blk = sl >= 0 ? sl / kBlk : a.num_blocks - 1;
+      const size_t base = ((static_cast<size_t>(blk) * a.nkv + g) * kBlk + (sl >= 0 ? sl % kBlk : 0)) * D;
+      if (act) {
+        S* kp = static_cast<S*>(a.k_pool) + base;
+        S* vp = static_cast<S*>(a.v_pool) + base;
+        kp[lane] = T::from_f(k0);
+        kp[lane + half] = T::from_f(k1);
+        vp[lane] = T::from_f(fetch(vcol + lane));
+        vp[lane + half] = T::from_f(fetch(vcol + lane + half));
+      }
+    }
+  }
+  __syncthreads();
+
+  // score-phase slice of this lane: dims (lane % 8) * KL .. + KL of each query head
   float q[G][KL];
   const int sub = lane & 7, kt = lane >> 3;
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int e = 0; e < KL; ++e) q[j][e] = a.q[(static_cast<size_t>(row) * a.nq + g * G + j) * D + sub * KL + e] * a.scale;
+    for (int e = 0; e < KL; ++e) q[j][e] = qs[j][sub * KL + e];
 
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -268,33 +347,38 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
       if (dd == 0) { pp[0] = M; pp[1] = Ls; }
     }
   }
-  if (nsplit == 1) return;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* c = a.counters + static_cast<size_t>(row) * a.nkv + g;
-    const unsigned prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (prev == static_cast<unsigned>(nsplit - 1));
-    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = last;
+}
+
+// Merge the split partials of rows with more than one split: grid (rows, nq), block D threads
+// (thread = output dim). Split maxima and sums go through LDS; the weighted sum runs in split
+// order, so the result does not depend on which split finished first.
+template <class T, int D>
+__global__ __launch_bounds__(128) void k_attn_combine(int nq, const int* __restrict__ seq_lens, int split_tokens,
+                                                      int max_splits, const float* __restrict__ partials,
+                                                      void* __restrict__ out) {
+  extern __shared__ float sm_comb[];      // [2 * max_splits]
+  const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int L = seq_lens[row];
+  const int ns = (L + split_tokens - 1) / split_tokens;
+  if (L <= 0 || ns <= 1) return;
+  const float* part = partials + (static_cast<size_t>(row) * nq + h) * max_splits * (D + 2);
+  float* mx = sm_comb;
+  float* sl = sm_comb + max_splits;
+  for (int s = t; s < ns; s += blockDim.x) {
+    mx[s] = part[static_cast<size_t>(s) * (D + 2)];
+    sl[s] = part[static_cast<size_t>(s) * (D + 2) + 1];
   }
   __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int j = i / D, dd = i % D;
-    const float* pj = part + static_cast<size_t>(j) * a.max_splits * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pj[s * (D + 2)]);
-    float Ls = 0.f, O = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = pj + s * (D + 2);
-      const float f = __expf(ps[0] - M);
-      Ls += ps[1] * f;
-      O += ps[2 + dd] * f;
-    }
-    out[(g * G + j) * D + dd] = T::from_f(O / Ls);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, mx[s]);
+  float Ls = 0.f, O = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    const float f = __expf(mx[s] - M);
+    Ls += sl[s] * f;
+    O += part[static_cast<size_t>(s) * (D + 2) + 2 + t] * f;
   }
+  static_cast<typename T::S*>(out)[(static_cast<size_t>(row) * nq + h) * D + t] = T::from_f(O / Ls);
 }
 
 }  // namespace gr

@@ -80,17 +80,19 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const float* __restr
 
 // ------------------------------------------------------------------------------------------
 // VALU GEMV. Block = 4 waves; wave w owns ROWS weight rows (EPI_SILU: ROWS/2 gate rows and the
-// matching up rows). Lanes stride over K in 16-byte vectors. The block's MT token rows of x are
-// staged in LDS (as the weight dtype) in chunks of KC elements.
-template <class T, int MT, int ROWS>
+// matching up rows). Lanes stride over K in 16-byte vectors, U vectors per row in flight. The
+// first weight loads are issued before anything that depends on x, so the HBM stream starts at
+// once; x (MT token rows) is staged in LDS as the weight dtype in chunks of KC elements. With
+// norm == 1 (K <= 2048, one chunk) the prologue keeps r + deltas in registers, reduces the sums
+// of squares of all MT rows together and writes the normalised rows to LDS.
+template <class T, int MT, int ROWS, int U>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   using S = typename T::S;
   constexpr int EPV = T::kEPV;
-  constexpr int U = 2;                                   // vectors per lane per row in flight
   constexpr int KC = (32768 / (MT * static_cast<int>(sizeof(S)))) / (64 * EPV) * (64 * EPV);
+  constexpr int KPT = 8;                                  // norm prologue: K <= 256 * KPT
   __shared__ __align__(16) S xs[MT * KC];
-  __shared__ float red[8];
-  __shared__ float inv_rms[MT];
+  __shared__ float red[4][MT];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int m0 = blockIdx.y * MT;
@@ -98,7 +100,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   const int K = a.K;
   const S* W = static_cast<const S*>(a.W);
 
-  // weight rows of this wave
   int rows[ROWS];
   if (epi == EPI_SILU) {
     const int j0 = (blockIdx.x * 4 + wid) * (ROWS / 2);
@@ -111,26 +112,63 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   }
   const int nrows_total = (epi == EPI_SILU) ? 2 * a.N : a.N;
 
-  // prologue: RMSNorm statistics of the block's token rows
-  if (a.norm) {
-    for (int mm = 0; mm < mrows; ++mm) {
-      const int m = m0 + mm;
-      float ss = 0.f;
-      for (int k = threadIdx.x; k < K; k += blockDim.x) {
-        float v;
-        if (a.embed) {
-          v = T::to_f(static_cast<const S*>(a.embed)[static_cast<size_t>(a.tok[m]) * K + k]);
-        } else {
-          v = a.r_in[static_cast<size_t>(m) * K + k];
-          for (int s = 0; s < a.n_delta; ++s) v += a.delta[s * a.delta_stride + static_cast<size_t>(m) * K + k];
-        }
-        if (blockIdx.x == 0 && a.r_out) a.r_out[static_cast<size_t>(m) * K + k] = v;
-        ss += v * v;
+  uint4 wv[ROWS][U];
+  auto load_w = [&](int kc0, int nv, int v0) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int vv = v0 + lane + 64 * u;
+        if (vv < nv && rows[r] < nrows_total)
+          wv[r][u] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(rows[r]) * K + kc0 + vv * EPV);
+        else
+          wv[r][u] = make_uint4(0, 0, 0, 0);
       }
-      ss = block_sum(ss, red);
-      if (threadIdx.x == 0) inv_rms[mm] = 1.0f / sqrtf(ss / static_cast<float>(K) + a.eps);
+  };
+  // the first weight vectors go out before the prologue
+  load_w(0, min(KC, K) / EPV, 0);
+
+  if (a.norm) {
+    float v[MT][KPT];
+    float ss[MT];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      ss[mm] = 0.f;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        float x = 0.f;
+        if (mm < mrows && k < K) {
+          const int m = m0 + mm;
+          if (a.embed) {
+            x = T::to_f(static_cast<const S*>(a.embed)[static_cast<size_t>(a.tok[m]) * K + k]);
+          } else {
+            x = a.r_in[static_cast<size_t>(m) * K + k];
+            for (int s = 0; s < a.n_delta; ++s) x += a.delta[s * a.delta_stride + static_cast<size_t>(m) * K + k];
+          }
+          if (blockIdx.x == 0 && a.r_out) a.r_out[static_cast<size_t>(m) * K + k] = x;
+        }
+        v[mm][i] = x;
+        ss[mm] += x * x;
+      }
+      ss[mm] = wave_sum(ss[mm]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) red[wid][mm] = ss[mm];
     }
     __syncthreads();
+    const S* g = static_cast<const S*>(a.gain);
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      const float tot = red[0][mm] + red[1][mm] + red[2][mm] + red[3][mm];
+      const float inv = 1.0f / sqrtf(tot / static_cast<float>(K) + a.eps);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        if (k < K) xs[mm * KC + k] = T::from_f(mm < mrows ? v[mm][i] * inv * T::to_f(g[k]) : 0.f);
+      }
+    }
   }
 
   float acc[ROWS][MT];
@@ -139,50 +177,26 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.f;
 
+  bool preloaded = true;
   for (int kc0 = 0; kc0 < K; kc0 += KC) {
     const int kc = min(KC, K - kc0);
-    __syncthreads();
-    // stage x[m0 .. m0+mrows)[kc0 .. kc0+kc) into LDS
-    for (int i = threadIdx.x; i < MT * (kc / EPV); i += blockDim.x) {
-      const int mm = i / (kc / EPV), vv = i % (kc / EPV);
-      S* dst = xs + mm * KC + vv * EPV;
-      if (mm >= mrows) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-        continue;
-      }
-      const int m = m0 + mm, k = kc0 + vv * EPV;
-      if (!a.norm) {
-        *reinterpret_cast<uint4*>(dst) =
-            *reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) + static_cast<size_t>(m) * K + k);
-      } else {
-        const S* g = static_cast<const S*>(a.gain);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          float v;
-          if (a.embed) {
-            v = T::to_f(static_cast<const S*>(a.embed)[static_cast<size_t>(a.tok[m]) * K + k + e]);
-          } else {
-            v = a.r_in[static_cast<size_t>(m) * K + k + e];
-            for (int s = 0; s < a.n_delta; ++s) v += a.delta[s * a.delta_stride + static_cast<size_t>(m) * K + k + e];
-          }
-          dst[e] = T::from_f(v * inv_rms[mm] * T::to_f(g[k + e]));
-        }
+    const int nv = kc / EPV;  // vectors in this chunk
+    if (!a.norm) {
+      if (kc0) __syncthreads();
+      // stage x[m0 .. m0+mrows)[kc0 .. kc0+kc) into LDS
+      for (int i = threadIdx.x; i < MT * nv; i += blockDim.x) {
+        const int mm = i / nv, vv = i % nv;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (mm < mrows)
+          val = *reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) + static_cast<size_t>(m0 + mm) * K + kc0 +
+                                                vv * EPV);
+        *reinterpret_cast<uint4*>(xs + mm * KC + vv * EPV) = val;
       }
     }
     __syncthreads();
-    const int nv = kc / EPV;  // vectors in this chunk
     for (int v0 = 0; v0 < nv; v0 += 64 * U) {
-      uint4 wv[ROWS][U];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int vv = v0 + lane + 64 * u;
-          if (vv < nv && rows[r] < nrows_total)
-            wv[r][u] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(rows[r]) * K + kc0 + vv * EPV);
-          else
-            wv[r][u] = make_uint4(0, 0, 0, 0);
-        }
+      if (!preloaded) load_w(kc0, nv, v0);
+      preloaded = false;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int vv = v0 + lane + 64 * u;

@@ -34,7 +34,7 @@ struct Layout {  // byte offsets into the workspace
   size_t mmeta, mmeta_bytes;          // mixed step inputs
   size_t rope_cos, rope_sin;
   size_t resid[2], h, qkv, q, attn_o, d_o, d_d, act;
-  size_t attn_part, attn_cnt, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
+  size_t attn_part, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
   size_t total;
   int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
   int max_splits_alloc;               // splits per row the partial buffer holds (at 64 keys/split)
@@ -69,6 +69,10 @@ struct step_ctx {
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
   int stage_next = 0;
   size_t stage_bytes = 0;
+  // profiling: an event before every launch while prof_on
+  bool prof_on = false;
+  std::vector<hipEvent_t> prof_ev;
+  std::vector<int> prof_kind;
   std::string err;
   bool dead = false;
 };
@@ -98,6 +102,29 @@ int fail(step_ctx* c, int code, const char* fmt, ...) {
   } while (0)
 
 int elem_bytes(int dtype) { return dtype == STEP_F32 ? 4 : 2; }
+
+enum KernelKind {
+  KK_QKV = 0, KK_QKV_POST, KK_ATTN, KK_O, KK_GATE_UP, KK_DOWN, KK_LM_HEAD, KK_NORM, KK_SAMPLE, KK_PREFILL_ATTN,
+  KK_ATTN_COMBINE, KK_COUNT
+};
+const char* const kKindNames[KK_COUNT] = {"qkv_proj", "qknorm_rope_kvwrite", "attn_decode", "o_proj", "gate_up_silu",
+                                          "down_proj", "lm_head", "add_rmsnorm", "sample", "attn_prefill",
+                                          "attn_combine"};
+
+// Called before every kernel launch: counts it and, while profiling, marks its start.
+void pre_launch(step_ctx* ctx, int kind) {
+  if (ctx->prof_on && ctx->launches < static_cast<int>(ctx->prof_ev.size()) - 1) {
+    (void)hipEventRecord(ctx->prof_ev[ctx->launches], ctx->stream);
+    ctx->prof_kind[ctx->launches] = kind;
+  }
+  ctx->launches++;
+}
+
+// A bounded wait on the device (about iters * 3.4 us) that lets the host queue a whole step behind
+// it, so the profiled kernels run back to back.
+__global__ void k_hold(int iters) {
+  for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
+}
 
 // keys per attention split for a given row count (fixed per bucket, so the grid is too)
 int split_tokens_for(int rows) { return rows <= 8 ? 64 : (rows <= 32 ? 128 : 256); }
@@ -150,7 +177,6 @@ bool compute_layout(const step_config& c, Layout& L) {
   }
   L.max_splits_alloc = 0;
   L.attn_part = take(sizeof(float) * part_rows_splits * nq * (d + 2));
-  L.attn_cnt = take(sizeof(unsigned) * static_cast<size_t>(TM) * nkv);
   const int nch_max = (c.vocab + 1023) / 1024;
   L.samp_val = take(sizeof(float) * static_cast<size_t>(LM) * nch_max);
   L.samp_idx = take(sizeof(int) * static_cast<size_t>(LM) * nch_max);
@@ -221,27 +247,35 @@ struct Lin {
   float* r_out = nullptr;
   const void* gain = nullptr;
   float eps = 0.f;
+  int kind = KK_QKV;
   int ksplit_ok = 0;          // output may be split into fp32 partials (consumer sums them)
   int* ksplit_used = nullptr; // out: partial count
   size_t split_stride = 0;
 };
 
-template <class T, int MT, int ROWS>
-hipError_t launch_gemv_rows(const GemmArgs& a, int epi, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv<T, MT, ROWS>), grid, dim3(256), 0, s, a, epi);
+template <class T, int MT, int ROWS, int U>
+hipError_t launch_gemv_ru(const GemmArgs& a, int epi, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv<T, MT, ROWS, U>), grid, dim3(256), 0, s, a, epi);
   return hipGetLastError();
 }
 
+// (rows per wave, vectors per lane per row in flight): (1, 4|8), (2, 2|4), (4, 2), (8, 2)
 template <class T, int MT>
-hipError_t launch_gemv_mt(const GemmArgs& a, int epi, int rows_pw, dim3 grid, hipStream_t s) {
+hipError_t launch_gemv_mt(const GemmArgs& a, int epi, int rows_pw, int u, dim3 grid, hipStream_t s) {
   switch (rows_pw) {
-    case 1: return launch_gemv_rows<T, MT, 1>(a, epi, grid, s);
-    case 2: return launch_gemv_rows<T, MT, 2>(a, epi, grid, s);
-    case 4: return launch_gemv_rows<T, MT, 4>(a, epi, grid, s);
+    case 1: return u > 4 ? launch_gemv_ru<T, MT, 1, 8>(a, epi, grid, s) : launch_gemv_ru<T, MT, 1, 4>(a, epi, grid, s);
+    case 2: return u > 2 ? launch_gemv_ru<T, MT, 2, 4>(a, epi, grid, s) : launch_gemv_ru<T, MT, 2, 2>(a, epi, grid, s);
+    case 4: return launch_gemv_ru<T, MT, 4, 2>(a, epi, grid, s);
     default:
-      if constexpr (MT < 8) return launch_gemv_rows<T, MT, 8>(a, epi, grid, s);
+      if constexpr (MT < 8) return launch_gemv_ru<T, MT, 8, 2>(a, epi, grid, s);
       else return hipErrorInvalidValue;
   }
+}
+
+// K chunk the VALU GEMV stages in LDS (elements), as computed in the kernel
+int gemv_kc(int MT, int eb) {
+  const int epv = 16 / eb;
+  return (32768 / (MT * eb)) / (64 * epv) * (64 * epv);
 }
 
 template <class T>
@@ -255,12 +289,15 @@ int run_linear(step_ctx* ctx, const Lin& l) {
   hipStream_t s = ctx->stream;
   hipError_t e;
   const bool is_f32 = std::is_same<T, F32>::value;
+  pre_launch(ctx, l.kind);
   if (l.M <= 8 || is_f32 || l.norm) {
     const int MT = l.M <= 1 ? 1 : l.M <= 2 ? 2 : l.M <= 4 ? 4 : 8;
     const int units = l.N;  // output columns (EPI_SILU: gate/up pairs)
     const int ygrid = (l.M + MT - 1) / MT;
     int rows_pw = (MT >= 8) ? 4 : 8;   // 8 x 8 accumulators would spill
     const int min_rows = (l.epi == EPI_SILU) ? 2 : 1;
+    const int eb = static_cast<int>(sizeof(typename T::S));
+    const int nvl = (std::min(l.K, gemv_kc(MT, eb)) / (16 / eb) + 63) / 64;   // vectors per lane per row
     // largest rows-per-wave that still gives >= 512 blocks
     while (rows_pw > min_rows) {
       const int per_block = 4 * ((l.epi == EPI_SILU) ? rows_pw / 2 : rows_pw);
@@ -268,12 +305,14 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       rows_pw /= 2;
     }
     const int per_block = 4 * ((l.epi == EPI_SILU) ? rows_pw / 2 : rows_pw);
+    const int u = rows_pw == 1 ? (nvl > 4 ? 8 : 4) : rows_pw == 2 ? (nvl > 2 ? 4 : 2) : 2;
+    if (l.norm && (l.K > 2048 || l.K > gemv_kc(MT, eb))) e = hipErrorInvalidValue;   // one-chunk prologue only
     dim3 grid((units + per_block - 1) / per_block, ygrid);
-    switch (MT) {
-      case 1: e = launch_gemv_mt<T, 1>(a, l.epi, rows_pw, grid, s); break;
-      case 2: e = launch_gemv_mt<T, 2>(a, l.epi, rows_pw, grid, s); break;
-      case 4: e = launch_gemv_mt<T, 4>(a, l.epi, rows_pw, grid, s); break;
-      default: e = launch_gemv_mt<T, 8>(a, l.epi, rows_pw, grid, s); break;
+    if (!(l.norm && (l.K > 2048 || l.K > gemv_kc(MT, eb)))) switch (MT) {
+      case 1: e = launch_gemv_mt<T, 1>(a, l.epi, rows_pw, u, grid, s); break;
+      case 2: e = launch_gemv_mt<T, 2>(a, l.epi, rows_pw, u, grid, s); break;
+      case 4: e = launch_gemv_mt<T, 4>(a, l.epi, rows_pw, u, grid, s); break;
+      default: e = launch_gemv_mt<T, 8>(a, l.epi, rows_pw, u, grid, s); break;
     }
   } else if constexpr (!std::is_same<T, F32>::value) {
     if (l.M <= 32) {
@@ -307,7 +346,6 @@ int run_linear(step_ctx* ctx, const Lin& l) {
   } else {
     e = hipErrorInvalidValue;
   }
-  ctx->launches++;
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "linear launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
 }
@@ -317,9 +355,9 @@ int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_
              const void* embed, const int* tok, const int* row_map, float* r_out, const void* gain, void* h_out) {
   const int H = ctx->cfg.hidden;
   const size_t sm = sizeof(float) * (H + 8);
+  pre_launch(ctx, KK_NORM);
   hipLaunchKernelGGL((k_add_rmsnorm<T>), dim3(M), dim3(256), sm, ctx->stream, H, r_in, delta, n_delta, dstride, embed,
                      tok, row_map, r_out, gain, h_out, ctx->cfg.rms_eps);
-  ctx->launches++;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "norm launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
@@ -337,28 +375,51 @@ hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream
   return hipGetLastError();
 }
 
-// Row-attention over `rows` query rows; max_len bounds the keys of any row (sets the split grid).
+template <class T, int D>
+hipError_t launch_combine(step_ctx* ctx, int rows, const AttnRowsArgs& a) {
+  hipLaunchKernelGGL((k_attn_combine<T, D>), dim3(rows, a.nq), dim3(D), sizeof(float) * 2 * a.max_splits, ctx->stream,
+                     a.nq, a.seq_lens, a.split_tokens, a.max_splits, a.partials, a.out);
+  return hipGetLastError();
+}
+
+// Row attention over `rows` query rows; max_len bounds the keys of any row (sets the split grid).
+// q == nullptr: decode rows, whose QK-norm + RoPE + KV write run inside the attention kernel from
+// the n_qkv fp32 partial outputs of the QKV projection.
 template <class T>
-int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, const int* bt, int bt_stride, const int* row_req,
-                  const int* seq_lens, int max_len, void* out) {
+int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv, const int* pos, const int* slot,
+                  const int* bt, int bt_stride, const int* row_req, const int* seq_lens, int max_len, void* out) {
   const step_config& c = ctx->cfg;
+  const Layout& Ly = ctx->lay;
   AttnRowsArgs a{};
   a.nq = c.q_heads; a.nkv = c.kv_heads; a.q = q;
+  a.qkv = reinterpret_cast<const float*>(ctx->ws + Ly.qkv);
+  a.n_parts = n_qkv;
+  a.part_stride = static_cast<size_t>(Ly.TM) * (c.q_heads + 2 * c.kv_heads) * c.head_dim;
+  a.pos = pos; a.slot = slot;
+  a.rope_cos = reinterpret_cast<const float*>(ctx->ws + Ly.rope_cos);
+  a.rope_sin = reinterpret_cast<const float*>(ctx->ws + Ly.rope_sin);
+  a.q_norm = c.qk_norm ? ctx->q_norm[layer] : nullptr;
+  a.k_norm = c.qk_norm ? ctx->k_norm[layer] : nullptr;
+  a.eps = c.rms_eps;
   a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
   a.block_table = bt; a.bt_stride = bt_stride; a.row_req = row_req; a.seq_lens = seq_lens;
   a.split_tokens = split_tokens_for(rows);
   a.max_splits = std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
   a.num_blocks = c.num_blocks;
   a.out = out;
-  a.partials = reinterpret_cast<float*>(ctx->ws + ctx->lay.attn_part);
-  a.counters = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.attn_cnt);
+  a.partials = reinterpret_cast<float*>(ctx->ws + Ly.attn_part);
   a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
   const int G = c.q_heads / c.kv_heads;
   dim3 grid(rows, c.kv_heads, a.max_splits);
+  pre_launch(ctx, KK_ATTN);
   hipError_t e = (c.head_dim == 64) ? launch_attn_rows_d<T, 64>(a, G, grid, ctx->stream)
                                     : launch_attn_rows_d<T, 128>(a, G, grid, ctx->stream);
-  ctx->launches++;
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  if (a.max_splits > 1) {
+    pre_launch(ctx, KK_ATTN_COMBINE);
+    e = (c.head_dim == 64) ? launch_combine<T, 64>(ctx, rows, a) : launch_combine<T, 128>(ctx, rows, a);
+    if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention combine launch failed: %s", hipGetErrorString(e));
+  }
   return STEP_OK;
 }
 
@@ -366,13 +427,13 @@ template <class T>
 int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_stride, const int* pos, const int* slot) {
   const step_config& c = ctx->cfg;
   const Layout& L = ctx->lay;
+  pre_launch(ctx, KK_QKV_POST);
   hipLaunchKernelGGL((k_qkv_post<T>), dim3(rows, c.q_heads + c.kv_heads), dim3(64), 0, ctx->stream, c.q_heads,
                      c.kv_heads, c.head_dim, reinterpret_cast<const float*>(ctx->ws + L.qkv), n_parts, part_stride, pos,
                      slot, reinterpret_cast<const float*>(ctx->ws + L.rope_cos),
                      reinterpret_cast<const float*>(ctx->ws + L.rope_sin), c.qk_norm ? ctx->q_norm[layer] : nullptr,
                      c.qk_norm ? ctx->k_norm[layer] : nullptr, c.rms_eps, reinterpret_cast<float*>(ctx->ws + L.q),
                      ctx->k_pool[layer], ctx->v_pool[layer], c.num_blocks);
-  ctx->launches++;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "qkv_post launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
@@ -395,8 +456,8 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
   const int nch = (vocab + chunk - 1) / chunk;
+  pre_launch(ctx, KK_SAMPLE);
   hipLaunchKernelGGL(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
-  ctx->launches++;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
@@ -430,9 +491,11 @@ DecodeMeta decode_meta(char* base, int MB, int W) {
 
 // The transformer layers over M rows: embed -> layers -> final norm (rows of row_map) -> LM head.
 // attn(layer) enqueues the attention of one layer (rows or packed prefill + rows).
+// fused_rope: the attention kernel does QK-norm + RoPE + KV write itself (decode rows, one token per
+// request); otherwise k_qkv_post runs first so every chunk token's K and V are in the pool.
 template <class T, class AttnFn>
 int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* slot, int n_logits, const int* logit_rows,
-               AttnFn attn) {
+               bool fused_rope, AttnFn attn) {
   const step_config& c = ctx->cfg;
   const Layout& L = ctx->lay;
   const int H = c.hidden, d = c.head_dim, nq = c.q_heads, nkv = c.kv_heads, I = c.intermediate;
@@ -444,7 +507,9 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
   float* d_o = reinterpret_cast<float*>(ctx->ws + L.d_o);
   float* d_d = reinterpret_cast<float*>(ctx->ws + L.d_d);
   void* act = ctx->ws + L.act;
-  const bool fuse_norm = (M <= 8) || std::is_same<T, F32>::value;
+  const int MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  const bool fuse_norm = ((M <= 8) || std::is_same<T, F32>::value) && H <= 2048 &&
+                         H <= gemv_kc(MT, static_cast<int>(sizeof(typename T::S)));
   const size_t res_stride = static_cast<size_t>(L.TM) * H;     // floats between split-K partials of H-wide outputs
   const size_t qkv_stride = static_cast<size_t>(L.TM) * QKV;
   int n_dd = 0;                                                 // partial count of the previous down output
@@ -456,7 +521,7 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
     int n_qkv = 1;
     Lin lin{};
     lin.M = M; lin.N = QKV; lin.K = H; lin.W = ctx->qkv_w[l]; lin.bias = c.qkv_bias ? ctx->qkv_b[l] : nullptr;
-    lin.epi = EPI_F32; lin.out = qkv; lin.ldo = QKV; lin.ksplit_ok = 1; lin.ksplit_used = &n_qkv;
+    lin.epi = EPI_F32; lin.out = qkv; lin.ldo = QKV; lin.ksplit_ok = 1; lin.ksplit_used = &n_qkv; lin.kind = KK_QKV;
     lin.split_stride = qkv_stride;
     if (fuse_norm) {
       lin.norm = 1; lin.r_in = r_in; lin.delta = first ? nullptr : d_d; lin.n_delta = first ? 0 : n_dd;
@@ -468,17 +533,18 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
       lin.x = h;
     }
     TRY(run_linear<T>(ctx, lin));
-    TRY(run_qkv_post<T>(ctx, l, M, n_qkv, qkv_stride, pos, slot));
-    TRY(attn(l));
+    if (!fused_rope) TRY(run_qkv_post<T>(ctx, l, M, n_qkv, qkv_stride, pos, slot));
+    TRY(attn(l, n_qkv));
     // ---- O projection
     int n_o = 1;
     Lin lo{};
     lo.M = M; lo.N = H; lo.K = nq * d; lo.W = ctx->o_w[l]; lo.x = attn_o; lo.epi = EPI_F32; lo.out = d_o; lo.ldo = H;
-    lo.ksplit_ok = 1; lo.ksplit_used = &n_o; lo.split_stride = res_stride;
+    lo.ksplit_ok = 1; lo.ksplit_used = &n_o; lo.split_stride = res_stride; lo.kind = KK_O;
     TRY(run_linear<T>(ctx, lo));
     // ---- MLP half: r0 = r1 + o; h = RMSNorm(r0) * post_norm; a = SiLU(h Wg^T) * (h Wu^T); down
     Lin lg{};
     lg.M = M; lg.N = I; lg.K = H; lg.W = ctx->gate_up_w[l]; lg.epi = EPI_SILU; lg.out = act; lg.ldo = I;
+    lg.kind = KK_GATE_UP;
     if (fuse_norm) {
       lg.norm = 1; lg.r_in = r_out; lg.delta = d_o; lg.n_delta = n_o; lg.delta_stride = res_stride; lg.r_out = resid[0];
       lg.gain = ctx->post_norm[l]; lg.eps = c.rms_eps;
@@ -489,12 +555,13 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
     TRY(run_linear<T>(ctx, lg));
     Lin ld{};
     ld.M = M; ld.N = H; ld.K = I; ld.W = ctx->down_w[l]; ld.x = act; ld.epi = EPI_F32; ld.out = d_d; ld.ldo = H;
-    ld.ksplit_ok = 1; ld.ksplit_used = &n_dd; ld.split_stride = res_stride;
+    ld.ksplit_ok = 1; ld.ksplit_used = &n_dd; ld.split_stride = res_stride; ld.kind = KK_DOWN;
     TRY(run_linear<T>(ctx, ld));
   }
   // ---- final norm + LM head on the sampled rows
   Lin lh{};
   lh.N = c.vocab; lh.K = H; lh.W = c_lm_head_of(ctx); lh.epi = EPI_F32; lh.out = ctx->logits; lh.ldo = c.vocab;
+  lh.kind = KK_LM_HEAD;
   if (logit_rows == nullptr && fuse_norm) {
     lh.M = M; lh.norm = 1; lh.r_in = resid[0]; lh.delta = d_d; lh.n_delta = n_dd; lh.delta_stride = res_stride;
     lh.gain = c_final_norm_of(ctx); lh.eps = c.rms_eps;
@@ -549,10 +616,11 @@ int run_decode(step_ctx* ctx, int B) {
   DecodeMeta m = decode_meta(ctx->ws + L.dmeta, c.max_batch, W);
   const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
   void* attn_o = ctx->ws + L.attn_o;
-  auto attn = [&](int l) {
-    return run_attn_rows<T>(ctx, l, B, q, m.bt, W, nullptr, m.len, c.max_position, attn_o);
+  (void)q;
+  auto attn = [&](int l, int n_qkv) {
+    return run_attn_rows<T>(ctx, l, B, nullptr, n_qkv, m.pos, m.slot, m.bt, W, nullptr, m.len, c.max_position, attn_o);
   };
-  TRY(run_layers<T>(ctx, B, m.ids, m.pos, m.slot, 0, nullptr, attn));
+  TRY(run_layers<T>(ctx, B, m.ids, m.pos, m.slot, 0, nullptr, true, attn));
   return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
                     m.len, m.slot, m.bt, W, ctx->history, c.max_position);
 }
@@ -577,11 +645,11 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
   MixedMeta m = mixed_meta(ctx->ws + L.mmeta, L, W);
   const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
   void* attn_o = ctx->ws + L.attn_o;
-  auto attn = [&](int l) -> int {
+  auto attn = [&](int l, int) -> int {
     // one query row per token: prefill rows see keys [0, pos], decode rows their request's keys
-    return run_attn_rows<T>(ctx, l, p.T, q, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
+    return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
   };
-  TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, attn));
+  TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, false, attn));
   return run_sample(ctx, ctx->logits, p.n_logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
                     nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0);
 }
@@ -809,6 +877,12 @@ extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) {
         if (blk < -1 || blk >= c.num_blocks - 1) return fail(ctx, STEP_EINVAL, "row %d: block id %d outside the pool", i, blk);
         if (blk < 0 && j < (len + 15) / 16) return fail(ctx, STEP_EINVAL, "row %d: missing block %d of its keys", i, j);
       }
+      // a decode row's new token is its last key, stored at the slot its block table gives
+      if (len > 0) {
+        if (len != p + 1) return fail(ctx, STEP_EINVAL, "row %d: seq_len %d must be position + 1 = %d", i, len, p + 1);
+        const int want = hb->h_block_table[static_cast<size_t>(i) * hb->bt_width + p / 16] * 16 + p % 16;
+        if (sl != want) return fail(ctx, STEP_EINVAL, "row %d: slot %d is not the table's slot %d", i, sl, want);
+      }
     }
     int slot_i;
     char* st = stage_slot(ctx, &slot_i);
@@ -945,6 +1019,41 @@ extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, i
                     nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0);
 }
 
+extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_ms, int32_t* h_kind) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  if (!ctx->have_batch) return fail(ctx, STEP_EINVAL, "profile step before any batch");
+  if (max_kernels < 1 || !h_ms || !h_kind) return fail(ctx, STEP_EINVAL, "bad profile buffers");
+  const size_t nev = static_cast<size_t>(max_kernels) + 1;
+  while (ctx->prof_ev.size() < nev) {
+    hipEvent_t e;
+    HIPCHK(ctx, hipEventCreate(&e));
+    ctx->prof_ev.push_back(e);
+  }
+  ctx->prof_kind.assign(ctx->prof_ev.size(), -1);
+  hipLaunchKernelGGL(k_hold, dim3(1), dim3(64), 0, ctx->stream, 1000);
+  HIPCHK(ctx, hipGetLastError());
+  ctx->launches = 0;
+  ctx->prof_on = true;
+  const int rc = run_decode_any(ctx, ctx->last_bucket);
+  ctx->prof_on = false;
+  if (rc != STEP_OK) return rc;
+  const int n = std::min(ctx->launches, max_kernels);
+  HIPCHK(ctx, hipEventRecord(ctx->prof_ev[n], ctx->stream));
+  HIPCHK(ctx, hipEventSynchronize(ctx->prof_ev[n]));
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    HIPCHK(ctx, hipEventElapsedTime(&ms, ctx->prof_ev[i], ctx->prof_ev[i + 1]));
+    h_ms[i] = ms;
+    h_kind[i] = ctx->prof_kind[i];
+  }
+  ctx->step_count++;
+  return ctx->launches;
+}
+
+extern "C" const char* step_kernel_kind_name(int32_t kind) {
+  return (kind >= 0 && kind < KK_COUNT) ? kKindNames[kind] : "unknown";
+}
+
 extern "C" int step_last_bucket(const step_ctx* ctx) { return ctx ? ctx->last_bucket : STEP_ESTATE; }
 
 extern "C" int step_kernels_per_decode(const step_ctx* ctx, int32_t bucket) {
@@ -970,5 +1079,6 @@ extern "C" void step_destroy(step_ctx* ctx) {
     if (ctx->h_stage[i]) (void)hipHostFree(ctx->h_stage[i]);
   }
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
   delete ctx;
 }

@@ -132,7 +132,9 @@ int step_init(const step_config *cfg, const step_weights *w, const step_buffers 
               step_ctx **out);
 
 /* Decode step over r = h_batch->num_rows rows. 1 <= r <= max_batch, bt_width <= max_blocks_per_seq,
- * else STEP_EINVAL. The rows are copied into the static buffers and padded up to the smallest
+ * else STEP_EINVAL. A row with seq_len > 0 must have seq_len == position + 1 and the slot its block
+ * table gives for that position (STEP_EINVAL otherwise): its new K and V are written by the attention
+ * kernel itself. The rows are copied into the static buffers and padded up to the smallest
  * bucket >= r (token 0, position 0, slot -1, seq_len 0, zero block-table row); the bucket's graph
  * is replayed (or its kernels launched eagerly). h_batch == NULL continues on the device: the
  * previous step's sampled tokens become the inputs, positions and seq_lens advance by one and the
@@ -151,6 +153,15 @@ int step_mixed(step_ctx *ctx, const step_packed *h_batch);
 int step_sample(step_ctx *ctx, const float *d_logits, int32_t rows, int32_t ld, int32_t vocab,
                 const float *h_temperature, const float *d_uniforms, uint64_t seed, uint64_t counter,
                 int32_t *d_tokens_out);
+
+/* Profiling (a debug aid, not part of the graphed path): runs one decode step at the bucket of the last
+ * batch EAGERLY over the current static state, behind a short bounded device-side wait so the kernels
+ * run back to back, with a hipEvent before every kernel, and waits for it. Writes the duration (ms,
+ * start of one kernel to the start of the next) and the kind (see step_kernel_kind_name) of up to
+ * max_kernels kernels into host arrays. Returns the number of kernels of the step, or a negative code.
+ * It is a real step: the decode state advances exactly as in step_decode(ctx, NULL). */
+int step_profile_decode(step_ctx *ctx, int32_t max_kernels, float *h_ms, int32_t *h_kind);
+const char *step_kernel_kind_name(int32_t kind);
 
 /* Rows of the bucket the last decode step ran at, and kernels launched per decode step. */
 int step_last_bucket(const step_ctx *ctx);
