@@ -160,6 +160,38 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   const int t0 = sp * a.split_tokens, t1 = min(L, t0 + a.split_tokens);
   const int req = a.row_req ? a.row_req[row] : row;
   const int* bt = a.block_table + static_cast<size_t>(req) * a.bt_stride;
+  const int sub = lane & 7, kt = lane >> 3;
+  const int vd = (lane % (D / 8)) * 8;  // value-phase dims of this lane
+  const int vg = lane / (D / 8);        // value-phase key group
+  const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+
+  // K and V tiles of one 16-key block, loaded straight into registers
+  constexpr int KV16 = KL * sizeof(S) / 16;               // 16-byte vectors per lane per key pass
+  constexpr int VV = 8 * sizeof(S) / 16;                  // 16-byte vectors per 8 dims
+  uint4 kr[2][KV16 > 0 ? KV16 : 1], vr[kBlk / VG][VV];
+  auto load_kv = [&](int bi, uint4 (&kk)[2][KV16 > 0 ? KV16 : 1], uint4 (&vv)[kBlk / VG][VV]) {
+    const int tb = t0 + bi * kBlk;
+    const int pb0 = (tb / kBlk < a.bt_stride) ? bt[tb / kBlk] : -1;
+    const int pb = pb0 >= 0 ? pb0 : a.num_blocks - 1;
+    const size_t tile = (static_cast<size_t>(pb) * a.nkv + g) * kBlk * D;
+    const S* kp = static_cast<const S*>(a.k_pool) + tile;
+    const S* vp = static_cast<const S*>(a.v_pool) + tile;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int v = 0; v < KV16; ++v)
+        kk[ps][v] = *reinterpret_cast<const uint4*>(kp + (ps * 8 + kt) * D + sub * KL + v * (16 / sizeof(S)));
+#pragma unroll
+    for (int i = 0; i < kBlk / VG; ++i)
+#pragma unroll
+      for (int v = 0; v < VV; ++v)
+        vv[i][v] = *reinterpret_cast<const uint4*>(vp + (vg + i * VG) * D + vd + v * (16 / sizeof(S)));
+  };
+  // The first block of this wave is loaded before the query prologue, unless it holds key L-1 of
+  // a fused decode row (the prologue writes that key first).
+  const bool writes_new = (a.q == nullptr) && (sp == nsplit - 1);
+  const bool pre = (wid < nblk) && !(writes_new && wid == nblk - 1);
+  if (pre) load_kv(wid, kr, vr);
 
   // queries of heads g*G .. g*G+G-1 into LDS (scaled by 1/sqrt(D))
   if (a.q) {
@@ -207,7 +239,6 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
 
   // score-phase slice of this lane: dims (lane % 8) * KL .. + KL of each query head
   float q[G][KL];
-  const int sub = lane & 7, kt = lane >> 3;
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -221,32 +252,9 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
   }
-  const int vd = (lane % (D / 8)) * 8;  // value-phase dims of this lane
-  const int vg = lane / (D / 8);        // value-phase key group
-
-  const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
   for (int bi = wid; bi < nblk; bi += 4) {
     const int tb = t0 + bi * kBlk;                          // first key of the block
-    const int pb0 = (tb / kBlk < a.bt_stride) ? bt[tb / kBlk] : -1;
-    const int pb = pb0 >= 0 ? pb0 : a.num_blocks - 1;
-    const size_t tile = (static_cast<size_t>(pb) * a.nkv + g) * kBlk * D;
-    const S* kt_ptr = static_cast<const S*>(a.k_pool) + tile;
-    const S* vt_ptr = static_cast<const S*>(a.v_pool) + tile;
-    // issue all loads of the block up front
-    constexpr int KV16 = KL * sizeof(S) / 16;               // 16-byte vectors per lane per key pass
-    uint4 kr[2][KV16 > 0 ? KV16 : 1];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-      for (int v = 0; v < KV16; ++v)
-        kr[ps][v] = *reinterpret_cast<const uint4*>(kt_ptr + (ps * 8 + kt) * D + sub * KL + v * (16 / sizeof(S)));
-    constexpr int VV = 8 * sizeof(S) / 16;                  // 16-byte vectors per 8 dims
-    uint4 vr[kBlk / VG][VV];
-#pragma unroll
-    for (int i = 0; i < kBlk / VG; ++i)
-#pragma unroll
-      for (int v = 0; v < VV; ++v)
-        vr[i][v] = *reinterpret_cast<const uint4*>(vt_ptr + (vg + i * VG) * D + vd + v * (16 / sizeof(S)));
+    if (bi != wid || !pre) load_kv(bi, kr, vr);
 
     // scores: 8 lanes per key, two passes of 8 keys
     float sc[2][G];
@@ -299,11 +307,13 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
       float vf[8];
 #pragma unroll
       for (int v = 0; v < VV; ++v) cvt_vec<T>(vr[i][v], vf + v * (16 / sizeof(S)));
+      // a masked key adds nothing, even if its slot holds NaN (0 * NaN would not be 0)
+      const bool live = tb + vg + i * VG < t1;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float p = p_s[wid][j][vg + i * VG];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = fmaf(p, vf[e], o[j][e]);
+        for (int e = 0; e < 8; ++e) o[j][e] = live ? fmaf(p, vf[e], o[j][e]) : o[j][e];
       }
     }
     __builtin_amdgcn_wave_barrier();

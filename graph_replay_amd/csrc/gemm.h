@@ -42,7 +42,9 @@ struct GemmArgs {
 
 // ------------------------------------------------------------------------------------------
 // Residual-add + RMSNorm as a kernel of its own (used when the row count is too large to redo the
-// norm in every projection block). One block per row.
+// norm in every projection block). One block of 256 threads per row, H <= 2048; every load of a
+// phase is issued before any use and the row stays in registers. Same reduction order as the
+// fused prologue of k_gemv, so both give the same bits.
 template <class T>
 __global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const float* __restrict__ r_in,
                                                      const float* __restrict__ delta, int n_delta,
@@ -51,30 +53,47 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const float* __restr
                                                      float* __restrict__ r_out, const void* __restrict__ gain,
                                                      void* __restrict__ h_out, float eps) {
   using S = typename T::S;
-  extern __shared__ float sm_norm[];
-  float* v = sm_norm;          // [H]
-  float* red = sm_norm + H;    // [8]
+  constexpr int KPT = 8;
+  __shared__ float red[8];
   const int m = blockIdx.x;
   const int src = row_map ? row_map[m] : m;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < H; k += blockDim.x) {
-    float x;
-    if (embed) {
-      x = T::to_f(static_cast<const S*>(embed)[static_cast<size_t>(tok[src]) * H + k]);
-    } else {
-      x = r_in[static_cast<size_t>(src) * H + k];
-      for (int s = 0; s < n_delta; ++s) x += delta[s * delta_stride + static_cast<size_t>(src) * H + k];
+  const S* g = static_cast<const S*>(gain);
+  float v[KPT], gk[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) gk[i] = T::to_f(g[min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)]);
+  if (embed) {
+    const size_t eo = static_cast<size_t>(tok[src]) * H;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) v[i] = T::to_f(static_cast<const S*>(embed)[eo + min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)]);
+  } else {
+    const size_t ro = static_cast<size_t>(src) * H;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) v[i] = r_in[ro + min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)];
+    for (int s = 0; s < n_delta; ++s) {
+      float dv[KPT];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) dv[i] = delta[s * delta_stride + ro + min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) v[i] += dv[i];
     }
-    v[k] = x;
-    ss += x * x;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int k = threadIdx.x + 256 * i;
+    v[i] = (k < H) ? v[i] : 0.f;
+    ss += v[i] * v[i];
   }
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
-  const S* g = static_cast<const S*>(gain);
   S* h = static_cast<S*>(h_out) + static_cast<size_t>(m) * H;
-  for (int k = threadIdx.x; k < H; k += blockDim.x) {
-    if (r_out) r_out[static_cast<size_t>(m) * H + k] = v[k];
-    h[k] = T::from_f(v[k] * inv * T::to_f(g[k]));
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int k = threadIdx.x + 256 * i;
+    if (k < H) {
+      if (r_out) r_out[static_cast<size_t>(m) * H + k] = v[i];
+      h[k] = T::from_f(v[i] * inv * gk[i]);
+    }
   }
 }
 
@@ -112,24 +131,62 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   }
   const int nrows_total = (epi == EPI_SILU) ? 2 * a.N : a.N;
 
+  // Loads are unconditional from clamped (always in-bounds) addresses, so the compiler can keep
+  // them all in flight; vectors past the row end are skipped in the compute loop and rows past N
+  // are never stored.
   uint4 wv[ROWS][U];
   auto load_w = [&](int kc0, int nv, int v0) {
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r)
+    for (int r = 0; r < ROWS; ++r) {
+      const size_t rb = static_cast<size_t>(min(rows[r], nrows_total - 1)) * K + kc0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int vv = v0 + lane + 64 * u;
-        if (vv < nv && rows[r] < nrows_total)
-          wv[r][u] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(rows[r]) * K + kc0 + vv * EPV);
-        else
-          wv[r][u] = make_uint4(0, 0, 0, 0);
+        const int vv = min(v0 + lane + 64 * u, nv - 1);
+        wv[r][u] = *reinterpret_cast<const uint4*>(W + rb + vv * EPV);
       }
+    }
   };
   // the first weight vectors go out before the prologue
   load_w(0, min(KC, K) / EPV, 0);
 
   if (a.norm) {
+    const S* g = static_cast<const S*>(a.gain);
+    float gk[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) gk[i] = T::to_f(g[min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)]);
+    // v = r + sum of deltas (or the embedding row), every load of a phase issued before any use;
+    // indices are clamped so all loads are in bounds, out-of-range lanes are zeroed afterwards
     float v[MT][KPT];
+    size_t rowoff[MT];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) rowoff[mm] = static_cast<size_t>(m0 + min(mm, mrows - 1)) * K;
+    if (a.embed) {
+      size_t eoff[MT];
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) eoff[mm] = static_cast<size_t>(a.tok[m0 + min(mm, mrows - 1)]) * K;
+      const S* E = static_cast<const S*>(a.embed);
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) v[mm][i] = T::to_f(E[eoff[mm] + min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)]);
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) v[mm][i] = a.r_in[rowoff[mm] + min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)];
+      for (int s = 0; s < a.n_delta; ++s) {
+        const float* dp = a.delta + s * a.delta_stride;
+        float dv[MT][KPT];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) dv[mm][i] = dp[rowoff[mm] + min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) v[mm][i] += dv[mm][i];
+      }
+    }
     float ss[MT];
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
@@ -137,19 +194,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int k = threadIdx.x + 256 * i;
-        float x = 0.f;
-        if (mm < mrows && k < K) {
-          const int m = m0 + mm;
-          if (a.embed) {
-            x = T::to_f(static_cast<const S*>(a.embed)[static_cast<size_t>(a.tok[m]) * K + k]);
-          } else {
-            x = a.r_in[static_cast<size_t>(m) * K + k];
-            for (int s = 0; s < a.n_delta; ++s) x += a.delta[s * a.delta_stride + static_cast<size_t>(m) * K + k];
-          }
-          if (blockIdx.x == 0 && a.r_out) a.r_out[static_cast<size_t>(m) * K + k] = x;
-        }
-        v[mm][i] = x;
-        ss[mm] += x * x;
+        const bool ok = mm < mrows && k < K;
+        v[mm][i] = ok ? v[mm][i] : 0.f;
+        if (ok && blockIdx.x == 0 && a.r_out) a.r_out[rowoff[mm] + k] = v[mm][i];
+        ss[mm] += v[mm][i] * v[mm][i];
       }
       ss[mm] = wave_sum(ss[mm]);
     }
@@ -158,7 +206,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
       for (int mm = 0; mm < MT; ++mm) red[wid][mm] = ss[mm];
     }
     __syncthreads();
-    const S* g = static_cast<const S*>(a.gain);
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
       const float tot = red[0][mm] + red[1][mm] + red[2][mm] + red[3][mm];
@@ -166,7 +213,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int k = threadIdx.x + 256 * i;
-        if (k < K) xs[mm * KC + k] = T::from_f(mm < mrows ? v[mm][i] * inv * T::to_f(g[k]) : 0.f);
+        if (k < K) xs[mm * KC + k] = T::from_f(mm < mrows ? v[mm][i] * inv * gk[i] : 0.f);
       }
     }
   }
@@ -186,10 +233,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
       // stage x[m0 .. m0+mrows)[kc0 .. kc0+kc) into LDS
       for (int i = threadIdx.x; i < MT * nv; i += blockDim.x) {
         const int mm = i / nv, vv = i % nv;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (mm < mrows)
-          val = *reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) + static_cast<size_t>(m0 + mm) * K + kc0 +
-                                                vv * EPV);
+        uint4 val = *reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) +
+                                                    static_cast<size_t>(m0 + min(mm, mrows - 1)) * K + kc0 + vv * EPV);
+        if (mm >= mrows) val = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(xs + mm * KC + vv * EPV) = val;
       }
     }
@@ -291,6 +337,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
 #pragma unroll
   for (int t = 0; t < MB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // clamped rows: loads are unconditional and in bounds; out-of-range rows are zeroed by select
   const S* wp = W + static_cast<size_t>(wrow_ok ? wrow : 0) * K + koff;
   const S* xp[MB];
   bool xok[MB];
@@ -298,8 +345,9 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
   for (int t = 0; t < MB; ++t) {
     const int m = t * 16 + (lane & 15);
     xok[t] = m < a.M;
-    xp[t] = X + static_cast<size_t>(xok[t] ? m : 0) * K + koff;
+    xp[t] = X + static_cast<size_t>(xok[t] ? m : a.M - 1) * K + koff;
   }
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
   constexpr int UN = 4;
   int ks = ks0 + wid;
   for (; ks + 4 * (UN - 1) < ks1; ks += 4 * UN) {
@@ -307,9 +355,13 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int k = (ks + 4 * u) * 32;
-      av[u] = wrow_ok ? *reinterpret_cast<const uint4*>(wp + k) : make_uint4(0, 0, 0, 0);
+      av[u] = *reinterpret_cast<const uint4*>(wp + k);
+      if (!wrow_ok) av[u] = zero4;
 #pragma unroll
-      for (int t = 0; t < MB; ++t) bv[u][t] = xok[t] ? *reinterpret_cast<const uint4*>(xp[t] + k) : make_uint4(0, 0, 0, 0);
+      for (int t = 0; t < MB; ++t) {
+        bv[u][t] = *reinterpret_cast<const uint4*>(xp[t] + k);
+        if (!xok[t]) bv[u][t] = zero4;
+      }
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u)
@@ -318,10 +370,12 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
   }
   for (; ks < ks1; ks += 4) {
     const int k = ks * 32;
-    uint4 av = wrow_ok ? *reinterpret_cast<const uint4*>(wp + k) : make_uint4(0, 0, 0, 0);
+    uint4 av = *reinterpret_cast<const uint4*>(wp + k);
+    if (!wrow_ok) av = zero4;
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
-      uint4 bv = xok[t] ? *reinterpret_cast<const uint4*>(xp[t] + k) : make_uint4(0, 0, 0, 0);
+      uint4 bv = *reinterpret_cast<const uint4*>(xp[t] + k);
+      if (!xok[t]) bv = zero4;
       acc[t] = mfma16x16x32<T>(av, bv, acc[t]);
     }
   }
@@ -416,15 +470,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int epi) {
     for (int i = 0; i < WV; ++i) {
       const int idx = threadIdx.x + 256 * i, r = idx >> 2, c = (idx & 3) * 8;
       const int wr = wrow_of(r);
-      wreg[i] = (wr < nrows_total) ? *reinterpret_cast<const uint4*>(W + static_cast<size_t>(wr) * K + k0 + c)
-                                   : make_uint4(0, 0, 0, 0);
+      wreg[i] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(min(wr, nrows_total - 1)) * K + k0 + c);
+      if (wr >= nrows_total) wreg[i] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
       const int idx = threadIdx.x + 256 * i, r = idx >> 2, c = (idx & 3) * 8;
       const int m = m0 + r;
-      xreg[i] = (m < a.M) ? *reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + k0 + c)
-                          : make_uint4(0, 0, 0, 0);
+      xreg[i] = *reinterpret_cast<const uint4*>(X + static_cast<size_t>(min(m, a.M - 1)) * K + k0 + c);
+      if (m >= a.M) xreg[i] = make_uint4(0, 0, 0, 0);
     }
   };
   auto store_tiles = [&](int buf) {

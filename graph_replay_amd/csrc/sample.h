@@ -42,8 +42,6 @@ struct SampleArgs {
   uint64_t seed, step;                // used when rng == nullptr
   float* part_val;                    // [rows][nchunks]
   int* part_idx;
-  unsigned* row_cnt;                  // [rows], zero between launches
-  unsigned* done_cnt;                 // [1], zero between launches
   int* tokens_out;                    // [rows]
   // decode advance (advance != 0)
   int advance;
@@ -77,12 +75,11 @@ __device__ inline void block_best(float& v, int& i, float* sv, int* si) {
   for (int w = 1; w < nw; ++w) best_merge(v, i, sv[w], si[w]);
 }
 
-// Grid (rows, nchunks), block 256. Each block scores its columns of one row; the last block of a
-// row merges the chunk winners in chunk order, writes the token and advances the row.
+// Grid (rows, nchunks), block 256: each block scores its columns of one row and writes the chunk
+// winner (value, index) to part_val / part_idx.
 __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  __shared__ int last_flag;
   const int row = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const float T = a.temperature ? a.temperature[row] : 0.f;
   const uint64_t seed = a.rng ? a.rng[0] : a.seed;
@@ -92,11 +89,13 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   for (int c = c0 + 4 * threadIdx.x; c < c1; c += 4 * blockDim.x) {
-    float u[4] = {1.f, 1.f, 1.f, 1.f};
+    float zz[4], u[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zz[j] = z[min(c + j, c1 - 1)];
     if (T > 0.f) {
       if (a.uniforms) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = (c + j < c1) ? a.uniforms[static_cast<size_t>(row) * a.ld + c + j] : 1.f;
+        for (int j = 0; j < 4; ++j) u[j] = a.uniforms[static_cast<size_t>(row) * a.ld + min(c + j, c1 - 1)];
       } else {
         uint32_t w[4] = {static_cast<uint32_t>(c >> 2), static_cast<uint32_t>(row), static_cast<uint32_t>(step),
                          static_cast<uint32_t>(step >> 32)};
@@ -108,39 +107,34 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (c + j >= c1) break;
-      float s = z[c + j];
+      float sc = zz[j];
       if (T > 0.f) {
         const float uu = fminf(fmaxf(u[j], 1e-10f), 1.0f);
-        s = s / T - logf(-logf(uu));
+        sc = sc / T - logf(-logf(uu));
       }
-      best_merge(bv, bi, s, c + j);
+      best_merge(bv, bi, sc, c + j);
     }
   }
   block_best(bv, bi, sv, si);
-  if (nch > 1) {
-    if (threadIdx.x == 0) {
-      a.part_val[static_cast<size_t>(row) * nch + ch] = bv;
-      a.part_idx[static_cast<size_t>(row) * nch + ch] = bi;
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(a.row_cnt + row, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      last_flag = (prev == static_cast<unsigned>(nch - 1));
-      if (last_flag) __hip_atomic_store(a.row_cnt + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-    if (threadIdx.x != 0) return;
-    bv = a.part_val[static_cast<size_t>(row) * nch];
-    bi = a.part_idx[static_cast<size_t>(row) * nch];
-    for (int c = 1; c < nch; ++c)
-      best_merge(bv, bi, a.part_val[static_cast<size_t>(row) * nch + c], a.part_idx[static_cast<size_t>(row) * nch + c]);
-  } else if (threadIdx.x != 0) {
-    return;
+  if (threadIdx.x == 0) {
+    a.part_val[static_cast<size_t>(row) * nch + ch] = bv;
+    a.part_idx[static_cast<size_t>(row) * nch + ch] = bi;
   }
-  // thread 0 of the row's last block
+}
+
+// Grid (rows), block 256: merge a row's chunk winners (the order (value desc, index asc) is total, so
+// the merge order does not change the winner), write the token and advance the row. Block 0 moves
+// the Philox step counter on; every read of it happened in k_sample.
+__global__ __launch_bounds__(256) void k_sample_final(SampleArgs a, int nch) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int row = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int c = threadIdx.x; c < nch; c += blockDim.x)
+    best_merge(bv, bi, a.part_val[static_cast<size_t>(row) * nch + c], a.part_idx[static_cast<size_t>(row) * nch + c]);
+  block_best(bv, bi, sv, si);
+  if (threadIdx.x != 0) return;
   const int tok = bi;
   a.tokens_out[row] = tok;
   if (a.advance) {
@@ -165,15 +159,9 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       }
     }
   }
-  if (a.rng) {
-    // the last row to finish moves the Philox step counter on for the next step
-    __threadfence();
-    const unsigned prev = __hip_atomic_fetch_add(a.done_cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1) {
-      __hip_atomic_store(a.done_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint64_t* r = const_cast<uint64_t*>(a.rng);
-      r[1] = step + 1;
-    }
+  if (a.rng && row == 0) {
+    uint64_t* r = const_cast<uint64_t*>(a.rng);
+    r[1] = r[1] + 1;
   }
 }
 

@@ -19,6 +19,7 @@
 #include "attention.h"
 #include "common.h"
 #include "gemm.h"
+#include "prefill.h"
 #include "sample.h"
 #include "../../include/step.h"
 
@@ -205,6 +206,7 @@ int validate_config(step_ctx* ctx, const step_config* c) {
   if (c->hidden % (c->dtype == STEP_F32 ? 4 : 32) || c->intermediate % 32 || (c->q_heads * c->head_dim) % 32)
     return fail(ctx, STEP_EUNSUPPORTED, "hidden, intermediate and q_heads*head_dim must be multiples of 32");
   (void)epv;
+  if (c->hidden > 2048) return fail(ctx, STEP_EUNSUPPORTED, "hidden %d: norm kernels are built for <= 2048", c->hidden);
   if (c->block_size != 16) return fail(ctx, STEP_EUNSUPPORTED, "block_size must be 16");
   if (c->num_blocks < 2) return fail(ctx, STEP_EINVAL, "num_blocks must be >= 2 (one is the scratch block)");
   if (c->max_blocks_per_seq <= 0 || c->max_position <= 0) return fail(ctx, STEP_EINVAL, "bad max_blocks_per_seq / max_position");
@@ -354,9 +356,8 @@ template <class T>
 int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_delta, size_t dstride,
              const void* embed, const int* tok, const int* row_map, float* r_out, const void* gain, void* h_out) {
   const int H = ctx->cfg.hidden;
-  const size_t sm = sizeof(float) * (H + 8);
   pre_launch(ctx, KK_NORM);
-  hipLaunchKernelGGL((k_add_rmsnorm<T>), dim3(M), dim3(256), sm, ctx->stream, H, r_in, delta, n_delta, dstride, embed,
+  hipLaunchKernelGGL((k_add_rmsnorm<T>), dim3(M), dim3(256), 0, ctx->stream, H, r_in, delta, n_delta, dstride, embed,
                      tok, row_map, r_out, gain, h_out, ctx->cfg.rms_eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "norm launch failed: %s", hipGetErrorString(e));
@@ -450,8 +451,6 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.temperature = temp; a.uniforms = uniforms; a.rng = rng; a.seed = seed; a.step = stepc;
   a.part_val = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_val);
   a.part_idx = reinterpret_cast<int*>(ctx->ws + ctx->lay.samp_idx);
-  a.row_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_cnt);
-  a.done_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_done);
   a.tokens_out = tokens_out;
   a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
@@ -459,6 +458,10 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   pre_launch(ctx, KK_SAMPLE);
   hipLaunchKernelGGL(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
+  pre_launch(ctx, KK_SAMPLE);
+  hipLaunchKernelGGL(k_sample_final, dim3(rows), dim3(256), 0, ctx->stream, a, nch);
+  e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
 }
@@ -634,8 +637,28 @@ int run_decode_any(step_ctx* ctx, int B) {
 }
 
 struct MixedPlan {
-  int T, n_pre_tok, n_pre_req, n_dec, n_logits, max_len, mode;
+  int T, n_pre_tok, n_pre_req, n_dec, n_logits, max_len, mode, n_tiles;
 };
+
+template <class T>
+int run_attn_prefill(step_ctx* ctx, int layer, const MixedPlan& p, const MixedMeta& m, const float* q, void* out) {
+  const step_config& c = ctx->cfg;
+  PrefillArgs a{};
+  a.nq = c.q_heads; a.nkv = c.kv_heads; a.q = q;
+  a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
+  a.block_table = m.bt; a.bt_stride = c.max_blocks_per_seq;
+  a.tile_req = m.tile_req; a.tile_q0 = m.tile_q0; a.qsl = m.qsl; a.pos = m.pos;
+  a.num_blocks = c.num_blocks;
+  a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+  a.out = out;
+  dim3 grid(p.n_tiles, (c.q_heads + 3) / 4);
+  pre_launch(ctx, KK_PREFILL_ATTN);
+  if (c.head_dim == 64) hipLaunchKernelGGL((k_attn_prefill<T, 64>), grid, dim3(256), 0, ctx->stream, a);
+  else hipLaunchKernelGGL((k_attn_prefill<T, 128>), grid, dim3(256), 0, ctx->stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "prefill attention launch failed: %s", hipGetErrorString(e));
+  return STEP_OK;
+}
 
 template <class T>
 int run_mixed(step_ctx* ctx, const MixedPlan& p) {
@@ -645,9 +668,22 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
   MixedMeta m = mixed_meta(ctx->ws + L.mmeta, L, W);
   const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
   void* attn_o = ctx->ws + L.attn_o;
+  const size_t row_elems = static_cast<size_t>(c.q_heads) * c.head_dim;
   auto attn = [&](int l, int) -> int {
-    // one query row per token: prefill rows see keys [0, pos], decode rows their request's keys
-    return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
+    if (p.mode == 1 || p.n_pre_tok == 0 || std::is_same<T, F32>::value) {
+      // one query row per token: prefill rows see keys [0, pos], decode rows their request's keys
+      return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
+    }
+    if constexpr (!std::is_same<T, F32>::value) {
+      // chunk tokens packed on MFMA, decode rows one query row each, into disjoint output rows
+      TRY(run_attn_prefill<T>(ctx, l, p, m, q, attn_o));
+      if (p.T > p.n_pre_tok) {
+        const int off = p.n_pre_tok;
+        return run_attn_rows<T>(ctx, l, p.T - off, q + off * row_elems, 0, nullptr, nullptr, m.bt, W, m.row_req + off,
+                                m.row_len + off, p.max_len, static_cast<typename T::S*>(attn_o) + off * row_elems);
+      }
+    }
+    return STEP_OK;
   };
   TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, false, attn));
   return run_sample(ctx, ctx->logits, p.n_logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
@@ -962,8 +998,12 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
   for (int i = 0; i < NL; ++i)
     if (hp->h_logits_indices[i] < 0 || hp->h_logits_indices[i] >= T)
       return fail(ctx, STEP_EINVAL, "logits index %d outside the packed tokens", hp->h_logits_indices[i]);
-  if (hp->prefill_attention == 0 && c.dtype != STEP_F32) {
-    // packed causal prefill kernel: built in a later change; fall through to rows until then
+  // a prefill chunk holds the last positions of its request: pos = seq_len - n + i
+  for (int j = 0; j < Rp; ++j) {
+    const int n = qsl[j + 1] - qsl[j];
+    for (int i = qsl[j]; i < qsl[j + 1]; ++i)
+      if (hp->h_positions[i] != hp->h_seq_lens[j] - n + (i - qsl[j]))
+        return fail(ctx, STEP_EINVAL, "request %d: chunk positions must be seq_len - %d .. seq_len - 1", j, n);
   }
   int slot_i;
   char* st = stage_slot(ctx, &slot_i);
@@ -984,13 +1024,20 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
     for (int b = 0; b < W; ++b) row[b] = b < hp->bt_width ? hp->h_block_table[static_cast<size_t>(j) * hp->bt_width + b] : -1;
   }
   for (int j = 0; j <= R; ++j) m.qsl[j] = qsl[j];
+  int n_tiles = 0;
+  for (int j = 0; j < Rp; ++j)
+    for (int q0 = qsl[j]; q0 < qsl[j + 1]; q0 += 16) {
+      m.tile_req[n_tiles] = j;
+      m.tile_q0[n_tiles] = q0;
+      ++n_tiles;
+    }
   for (int i = 0; i < NL; ++i) {
     m.lidx[i] = hp->h_logits_indices[i];
     m.temp[i] = hp->h_temperature ? hp->h_temperature[i] : 0.f;
   }
   HIPCHK(ctx, hipMemcpyAsync(ctx->ws + ctx->lay.mmeta, st, ctx->lay.mmeta_bytes, hipMemcpyHostToDevice, ctx->stream));
   HIPCHK(ctx, hipEventRecord(ctx->stage_ev[slot_i], ctx->stream));
-  MixedPlan p{T, qsl[Rp], Rp, Rd, NL, max_len, hp->prefill_attention};
+  MixedPlan p{T, qsl[Rp], Rp, Rd, NL, max_len, hp->prefill_attention, n_tiles};
   ctx->launches = 0;
   int rc = run_mixed_any(ctx, p);
   if (rc != STEP_OK) return rc;
