@@ -208,6 +208,8 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-bs32", action="store_true")
+    ap.add_argument("--workload", choices=["both", "bs1", "bs32"], default="both",
+                    help="bs1: the primary line only; bs32: the batch-32 workload only (for profiling)")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -224,8 +226,14 @@ def main():
     shape = synth.QWEN3_0_6B
     log("weights")
     W = synth.make_weights(shape, 0)
+    if args.workload == "bs32":
+        r32 = run_bs32(shape, W, args.steps, warmup)
+        print(json.dumps({"metric": METRIC, "workload": r32["workload"], "value": round(r32["tok_s"], 1),
+                          "unit": "tokens/s", "ms_per_step": round(r32["ms_per_step"], 4),
+                          "kernels_per_step": r32["kernels_per_step"], "roofline": r32["roofline"]}), flush=True)
+        return
     r1 = run_bs1(shape, W, args.steps, warmup)
-    r32 = None if args.no_bs32 else run_bs32(shape, W, args.steps, warmup)
+    r32 = None if (args.no_bs32 or args.workload == "bs1") else run_bs32(shape, W, args.steps, warmup)
     cpu = None if args.no_cpu else cpu_baseline(shape, W)
     line = {
         "metric": METRIC, "value": round(r1["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
