@@ -69,6 +69,20 @@ def timed_replays(dec, steps: int):
     return e0.elapsed_time(e1)
 
 
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per launch of `kind` from the committed rocprofv3 counter runs (profiles/), or None
+    when there is no such run or the kernels changed since it was taken."""
+    from graph_replay_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    k = t.get("kinds", {}).get(kind)
+    if t.get("source_hash") != profiling.source_hash() or not k:
+        return None
+    return int(k.get("fetch_bytes", 0) + k.get("write_bytes", 0))
+
+
 def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int) -> dict:
     prof = dec.profile_decode()
     per = {}
@@ -116,6 +130,7 @@ def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024):
     nbytes = step_bytes(shape, seq_sum_mean)
     ms_step = ms / steps
     roof = roofline_from_profile(shape, dec, 1, start_len + steps)
+    roof["traffic"] = measured_traffic("qwen3-0.6b_bs1", roof["kernel"])
     out = {
         "tok_s": steps / (ms * 1e-3), "ms_per_step": ms_step, "bytes_per_step": int(nbytes),
         "step_hbm_GBps": nbytes / (ms_step * 1e-3) / 1e9, "kernels_per_step": dec.kernels_per_decode(1),
@@ -210,6 +225,8 @@ def main():
     ap.add_argument("--no-bs32", action="store_true")
     ap.add_argument("--workload", choices=["both", "bs1", "bs32"], default="both",
                     help="bs1: the primary line only; bs32: the batch-32 workload only (for profiling)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy a 1 GiB device buffer 4 times (calibrates the HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -221,6 +238,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 1 << 30, "copies": 4}), flush=True)
+        return
     import graph_replay_amd as g
     g.load()
     shape = synth.QWEN3_0_6B

@@ -105,6 +105,8 @@ struct AttnRowsArgs {
   float scale;
 };
 
+constexpr int kMaxSplits = 128;   // splits per row one launch may use (the host sizes P for it)
+
 // RMSNorm over one head (optional gain) then rotate-half RoPE: lane holds the pair (lane, lane+D/2).
 template <class T, int D>
 __device__ inline void norm_rope_pair(float& x0, float& x1, const void* gain, float eps, float c, float s) {

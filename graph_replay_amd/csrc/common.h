@@ -81,4 +81,28 @@ __device__ inline float block_sum(float v, float* red) {
 
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Cross-block hand-off inside one kernel, without whole-cache writeback or invalidate: the data is
+// written and read with device-scope (agent) relaxed atomic stores / loads, the writer waits for
+// its stores to complete (s_waitcnt) before it bumps a device-scope counter, and the reader issues
+// its loads only after seeing the count. This is the memory model's agent-scope release / acquire
+// for atomic data.
+__device__ inline void st_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float ld_dev(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline int ld_dev(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// all of this thread's stores have completed (are visible at device scope for device-scope stores)
+__device__ inline void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+// counts this block in; true for exactly one block: the last of `expected` to arrive (the counter
+// is reset to 0 for the next launch). Call from one thread after stores_done() + __syncthreads().
+__device__ inline bool arrive_last(unsigned* counter, unsigned expected) {
+  const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = (prev == expected - 1);
+  if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
 }  // namespace gr

@@ -102,8 +102,9 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const float* __restr
 // matching up rows). Lanes stride over K in 16-byte vectors, U vectors per row in flight. The
 // first weight loads are issued before anything that depends on x, so the HBM stream starts at
 // once; x (MT token rows) is staged in LDS as the weight dtype in chunks of KC elements. With
-// norm == 1 (K <= 2048, one chunk) the prologue keeps r + deltas in registers, reduces the sums
-// of squares of all MT rows together and writes the normalised rows to LDS.
+// norm == 1 (K <= 2048, one chunk) the prologue keeps v = r + deltas in registers, stages gain * v
+// and reduces the sums of squares of all MT rows alongside; RMSNorm's 1 / rms is a per-row scalar
+// of the dot product (W (g * v / rms) = (W (g * v)) / rms) and is applied in the epilogue.
 template <class T, int MT, int ROWS, int U>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   using S = typename T::S;
@@ -205,17 +206,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) red[wid][mm] = ss[mm];
     }
-    __syncthreads();
+    // x = gain * v goes to LDS now; the 1 / rms factor is a per-row scalar, applied to the dot
+    // products in the epilogue, so no barrier waits for the sum of squares before the matmul
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm) {
-      const float tot = red[0][mm] + red[1][mm] + red[2][mm] + red[3][mm];
-      const float inv = 1.0f / sqrtf(tot / static_cast<float>(K) + a.eps);
+    for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int k = threadIdx.x + 256 * i;
-        if (k < K) xs[mm * KC + k] = T::from_f(mm < mrows ? v[mm][i] * inv * gk[i] : 0.f);
+        if (k < K) xs[mm * KC + k] = T::from_f(mm < mrows ? v[mm][i] * gk[i] : 0.f);
       }
-    }
   }
 
   float acc[ROWS][MT];
@@ -267,6 +266,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   for (int r = 0; r < ROWS; ++r)
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) acc[r][mm] = wave_sum(acc[r][mm]);
+  if (a.norm) {
+    // red[][] was written before the staging barrier
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      const float inv = 1.0f / sqrtf((red[0][mm] + red[1][mm] + red[2][mm] + red[3][mm]) / static_cast<float>(K) + a.eps);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) acc[r][mm] *= inv;
+    }
+  }
 
   if (lane == 0) {
     if (epi == EPI_SILU) {
@@ -307,38 +315,50 @@ __device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c
   }
 }
 
-// Skinny MFMA GEMV: block = 4 waves, 16 weight rows (EPI_SILU: 8 gate + the 8 matching up rows),
-// MB 16-token tiles; wave w accumulates k-steps w, w+4, ... and the partial tiles are summed in
-// wave order through LDS. gridDim.y splits K into a.ksplit ranges (EPI_F32 only) whose fp32
-// partials go to out + split * out_split_stride.
-template <class T, int MB>
+// Skinny MFMA GEMV: block = 4 waves over RT tiles of 16 weight rows (EPI_SILU: each tile is 8 gate
+// rows and the matching 8 up rows) and MB 16-token tiles; wave w accumulates k-steps w, w+4, ... and
+// the partial tiles are summed in wave order through LDS. One activation fragment feeds RT MFMAs,
+// so the activation loads (from L2) are amortised over RT weight tiles. gridDim.y splits K into
+// a.ksplit ranges (EPI_F32 only) whose fp32 partials go to out + split * out_split_stride. UN k-steps
+// per wave are loaded at once.
+template <class T, int MB, int UN, int RT>
 __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
   using S = typename T::S;
-  __shared__ f32x4_t part[4][MB][64];
+  __shared__ f32x4_t part[4][RT][MB][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int K = a.K;
   const S* W = static_cast<const S*>(a.W);
   const S* X = static_cast<const S*>(a.x);
-  int wrow;
-  if (epi == EPI_SILU) {
-    const int j = blockIdx.x * 8 + (lane & 7);
-    wrow = ((lane & 15) < 8) ? j : a.N + j;
-  } else {
-    wrow = blockIdx.x * 16 + (lane & 15);
-  }
   const int nrows_total = (epi == EPI_SILU) ? 2 * a.N : a.N;
-  const bool wrow_ok = wrow < nrows_total;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  // weight row of this lane in each tile (clamped, so every load is in bounds; out-of-range rows are
+  // zeroed by select and never stored)
+  const S* wp[RT];
+  bool wok[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int wrow;
+    if (epi == EPI_SILU) {
+      const int j = (blockIdx.x * RT + r) * 8 + (lane & 7);
+      wrow = ((lane & 15) < 8) ? j : a.N + j;
+      wok[r] = j < a.N;
+    } else {
+      wrow = (blockIdx.x * RT + r) * 16 + (lane & 15);
+      wok[r] = wrow < a.N;
+    }
+    wp[r] = W + static_cast<size_t>(min(wrow, nrows_total - 1)) * K + 8 * (lane >> 4);
+  }
   const int ksteps = K / 32;
   const int per = (ksteps + a.ksplit - 1) / a.ksplit;
   const int ks0 = blockIdx.y * per, ks1 = min(ksteps, ks0 + per);
   const int koff = 8 * (lane >> 4);
 
-  f32x4_t acc[MB];
+  f32x4_t acc[RT][MB];
 #pragma unroll
-  for (int t = 0; t < MB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // clamped rows: loads are unconditional and in bounds; out-of-range rows are zeroed by select
-  const S* wp = W + static_cast<size_t>(wrow_ok ? wrow : 0) * K + koff;
   const S* xp[MB];
   bool xok[MB];
 #pragma unroll
@@ -347,16 +367,17 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
     xok[t] = m < a.M;
     xp[t] = X + static_cast<size_t>(xok[t] ? m : a.M - 1) * K + koff;
   }
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  constexpr int UN = 4;
   int ks = ks0 + wid;
   for (; ks + 4 * (UN - 1) < ks1; ks += 4 * UN) {
-    uint4 av[UN], bv[UN][MB];
+    uint4 av[UN][RT], bv[UN][MB];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int k = (ks + 4 * u) * 32;
-      av[u] = *reinterpret_cast<const uint4*>(wp + k);
-      if (!wrow_ok) av[u] = zero4;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        av[u][r] = *reinterpret_cast<const uint4*>(wp[r] + k);
+        if (!wok[r]) av[u][r] = zero4;
+      }
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
         bv[u][t] = *reinterpret_cast<const uint4*>(xp[t] + k);
@@ -366,29 +387,42 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int t = 0; t < MB; ++t) acc[t] = mfma16x16x32<T>(av[u], bv[u][t], acc[t]);
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < MB; ++t) acc[r][t] = mfma16x16x32<T>(av[u][r], bv[u][t], acc[r][t]);
   }
   for (; ks < ks1; ks += 4) {
     const int k = ks * 32;
-    uint4 av = *reinterpret_cast<const uint4*>(wp + k);
-    if (!wrow_ok) av = zero4;
+    uint4 av[RT], bv[MB];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      av[r] = *reinterpret_cast<const uint4*>(wp[r] + k);
+      if (!wok[r]) av[r] = zero4;
+    }
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
-      uint4 bv = *reinterpret_cast<const uint4*>(xp[t] + k);
-      if (!xok[t]) bv = zero4;
-      acc[t] = mfma16x16x32<T>(av, bv, acc[t]);
+      bv[t] = *reinterpret_cast<const uint4*>(xp[t] + k);
+      if (!xok[t]) bv[t] = zero4;
     }
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int t = 0; t < MB; ++t) acc[r][t] = mfma16x16x32<T>(av[r], bv[t], acc[r][t]);
   }
 #pragma unroll
-  for (int t = 0; t < MB; ++t) part[wid][t][lane] = acc[t];
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MB; ++t) part[wid][r][t][lane] = acc[r][t];
   __syncthreads();
-  if (wid != 0) return;
+  // wave r' of the block finishes tile r' (RT <= 4), summing the four waves in order
+  const int r = wid;
+  if (r >= RT) return;
 #pragma unroll
   for (int t = 0; t < MB; ++t) {
-    f32x4_t s = part[0][t][lane];
+    f32x4_t sum = part[0][r][t][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s += part[w][t][lane];
-    acc[t] = s;
+    for (int w = 1; w < 4; ++w) sum += part[w][r][t][lane];
+    acc[0][t] = sum;
   }
   const int col = lane & 15;          // token within the tile
   const int rbase = 4 * (lane >> 4);  // first of the 4 weight rows this lane holds
@@ -399,13 +433,13 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
     for (int t = 0; t < MB; ++t) {
       f32x4_t up;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) up[i] = __shfl(acc[t][i], lane + 32, 64);
+      for (int i = 0; i < 4; ++i) up[i] = __shfl(acc[0][t][i], lane + 32, 64);
       const int m = t * 16 + col;
       if (lane < 32 && m < a.M) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = blockIdx.x * 8 + rbase + i;
-          if (j < a.N) out[static_cast<size_t>(m) * a.ldo + j] = T::from_f(silu(acc[t][i]) * up[i]);
+          const int j = (blockIdx.x * RT + r) * 8 + rbase + i;
+          if (j < a.N) out[static_cast<size_t>(m) * a.ldo + j] = T::from_f(silu(acc[0][t][i]) * up[i]);
         }
       }
     }
@@ -418,8 +452,8 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
       if (m >= a.M) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = blockIdx.x * 16 + rbase + i;
-        if (n < a.N) out[static_cast<size_t>(m) * a.ldo + n] = acc[t][i] + (b ? T::to_f(b[n]) : 0.f);
+        const int n = (blockIdx.x * RT + r) * 16 + rbase + i;
+        if (n < a.N) out[static_cast<size_t>(m) * a.ldo + n] = acc[0][t][i] + (b ? T::to_f(b[n]) : 0.f);
       }
     }
   }

@@ -42,6 +42,8 @@ struct SampleArgs {
   uint64_t seed, step;                // used when rng == nullptr
   float* part_val;                    // [rows][nchunks]
   int* part_idx;
+  unsigned* row_cnt;                  // [rows], zero between launches (reset by the row's last block)
+  unsigned* done_cnt;                 // [1], zero between launches (reset by the last row)
   int* tokens_out;                    // [rows]
   // decode advance (advance != 0)
   int advance;
@@ -75,11 +77,14 @@ __device__ inline void block_best(float& v, int& i, float* sv, int* si) {
   for (int w = 1; w < nw; ++w) best_merge(v, i, sv[w], si[w]);
 }
 
-// Grid (rows, nchunks), block 256: each block scores its columns of one row and writes the chunk
-// winner (value, index) to part_val / part_idx.
+// Grid (rows, nchunks), block 256. Each block scores its columns of one row; the last block of a
+// row to finish merges the chunk winners (the order (value desc, index asc) is total, so the merge
+// order cannot change the winner), writes the token and advances the row. The last row to finish
+// moves the Philox step counter on: every block read it before it counted itself in.
 __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
+  __shared__ int last_flag;
   const int row = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const float T = a.temperature ? a.temperature[row] : 0.f;
   const uint64_t seed = a.rng ? a.rng[0] : a.seed;
@@ -116,24 +121,22 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     }
   }
   block_best(bv, bi, sv, si);
-  if (threadIdx.x == 0) {
-    a.part_val[static_cast<size_t>(row) * nch + ch] = bv;
-    a.part_idx[static_cast<size_t>(row) * nch + ch] = bi;
+  if (nch > 1) {
+    if (threadIdx.x == 0) {
+      st_dev(a.part_val + static_cast<size_t>(row) * nch + ch, bv);
+      st_dev(a.part_idx + static_cast<size_t>(row) * nch + ch, bi);
+      stores_done();
+      last_flag = arrive_last(a.row_cnt + row, nch);
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    bv = -INFINITY;
+    bi = 0x7fffffff;
+    for (int c = threadIdx.x; c < nch; c += blockDim.x)
+      best_merge(bv, bi, ld_dev(a.part_val + static_cast<size_t>(row) * nch + c),
+                 ld_dev(a.part_idx + static_cast<size_t>(row) * nch + c));
+    block_best(bv, bi, sv, si);
   }
-}
-
-// Grid (rows), block 256: merge a row's chunk winners (the order (value desc, index asc) is total, so
-// the merge order does not change the winner), write the token and advance the row. Block 0 moves
-// the Philox step counter on; every read of it happened in k_sample.
-__global__ __launch_bounds__(256) void k_sample_final(SampleArgs a, int nch) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  const int row = blockIdx.x;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int c = threadIdx.x; c < nch; c += blockDim.x)
-    best_merge(bv, bi, a.part_val[static_cast<size_t>(row) * nch + c], a.part_idx[static_cast<size_t>(row) * nch + c]);
-  block_best(bv, bi, sv, si);
   if (threadIdx.x != 0) return;
   const int tok = bi;
   a.tokens_out[row] = tok;
@@ -159,9 +162,9 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a, int nch) {
       }
     }
   }
-  if (a.rng && row == 0) {
+  if (a.rng && arrive_last(a.done_cnt, gridDim.x)) {
     uint64_t* r = const_cast<uint64_t*>(a.rng);
-    r[1] = r[1] + 1;
+    r[1] = step + 1;
   }
 }
 

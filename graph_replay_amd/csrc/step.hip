@@ -127,8 +127,13 @@ __global__ void k_hold(int iters) {
   for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
-// keys per attention split for a given row count (fixed per bucket, so the grid is too)
-int split_tokens_for(int rows) { return rows <= 8 ? 64 : (rows <= 32 ? 128 : 256); }
+// keys per attention split for a row count and key bound (fixed per bucket, so the grid is too):
+// short splits keep a few rows busy on all CUs, long splits amortise each split's fixed cost
+int split_tokens_for(int rows, int max_len) {
+  int P = rows <= 8 ? 64 : 512;
+  while ((max_len + P - 1) / P > gr::kMaxSplits) P *= 2;
+  return P;
+}
 
 // copies of split-K partial outputs the workspace holds
 constexpr int kMaxKsplit = 8;
@@ -171,10 +176,10 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.act = take(static_cast<size_t>(eb) * TM * I);
   // attention partials: rows * ceil(max_position / split) splits, maximised over row classes
   size_t part_rows_splits = 0;
-  for (int rows : {8, 32, TM}) {
+  for (int rows : {8, TM}) {
     const int r = std::min(rows, TM);
-    const int s = (c.max_position + split_tokens_for(r) - 1) / split_tokens_for(r);
-    part_rows_splits = std::max(part_rows_splits, static_cast<size_t>(r) * s);
+    const int P = split_tokens_for(r, c.max_position);
+    part_rows_splits = std::max(part_rows_splits, static_cast<size_t>(r) * ((c.max_position + P - 1) / P));
   }
   L.max_splits_alloc = 0;
   L.attn_part = take(sizeof(float) * part_rows_splits * nq * (d + 2));
@@ -318,16 +323,21 @@ int run_linear(step_ctx* ctx, const Lin& l) {
     }
   } else if constexpr (!std::is_same<T, F32>::value) {
     if (l.M <= 32) {
-      const int bx = (l.epi == EPI_SILU) ? (l.N + 7) / 8 : (l.N + 15) / 16;
+      // two 16-row weight tiles per wave share each activation fragment where the output is wide
+      // enough (QKV, gate|up); narrow outputs (O, down) keep one tile and split K instead
+      const int rt = (l.M > 16 && l.N >= 2048) ? 2 : 1;
+      const int bx = (l.epi == EPI_SILU) ? (l.N + 8 * rt - 1) / (8 * rt) : (l.N + 16 * rt - 1) / (16 * rt);
       int ks = 1;
       if (l.ksplit_ok && l.epi == EPI_F32) {
-        while (ks < kMaxKsplit && bx * ks < 256 && (l.K / 32) / (ks * 2) >= 4) ks *= 2;
+        const int target = 256;
+        while (ks < kMaxKsplit && bx * ks < target && (l.K / 32) / (ks * 2) >= 2) ks *= 2;
       }
       a.ksplit = ks;
       if (l.ksplit_used) *l.ksplit_used = ks;
       dim3 grid(bx, ks);
-      if (l.M <= 16) hipLaunchKernelGGL((k_gemv_mfma<T, 1>), grid, dim3(256), 0, s, a, l.epi);
-      else hipLaunchKernelGGL((k_gemv_mfma<T, 2>), grid, dim3(256), 0, s, a, l.epi);
+      if (l.M <= 16) hipLaunchKernelGGL((k_gemv_mfma<T, 1, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
+      else if (rt == 2) hipLaunchKernelGGL((k_gemv_mfma<T, 2, 4, 2>), grid, dim3(256), 0, s, a, l.epi);
+      else hipLaunchKernelGGL((k_gemv_mfma<T, 2, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
       e = hipGetLastError();
     } else {
       const bool big = l.M > 64;
@@ -404,7 +414,7 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.eps = c.rms_eps;
   a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
   a.block_table = bt; a.bt_stride = bt_stride; a.row_req = row_req; a.seq_lens = seq_lens;
-  a.split_tokens = split_tokens_for(rows);
+  a.split_tokens = split_tokens_for(rows, max_len);
   a.max_splits = std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
   a.num_blocks = c.num_blocks;
   a.out = out;
@@ -451,6 +461,8 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.temperature = temp; a.uniforms = uniforms; a.rng = rng; a.seed = seed; a.step = stepc;
   a.part_val = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_val);
   a.part_idx = reinterpret_cast<int*>(ctx->ws + ctx->lay.samp_idx);
+  a.row_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_cnt);
+  a.done_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_done);
   a.tokens_out = tokens_out;
   a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
@@ -458,10 +470,6 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   pre_launch(ctx, KK_SAMPLE);
   hipLaunchKernelGGL(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
-  pre_launch(ctx, KK_SAMPLE);
-  hipLaunchKernelGGL(k_sample_final, dim3(rows), dim3(256), 0, ctx->stream, a, nch);
-  e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
 }

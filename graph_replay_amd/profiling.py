@@ -1,0 +1,99 @@
+"""Summaries of rocprofv3 output for profiles/ (measurement tooling, not the step itself).
+
+    python -m graph_replay_amd.profiling stats <run>_kernel_stats.csv "<command>" > profiles/<name>.md
+    python -m graph_replay_amd.profiling traffic <copy FETCH dir> <copy WRITE dir> <FETCH dir> <WRITE dir> \\
+        <workload> "<command>" > profiles/hbm_traffic.json
+
+`traffic` turns two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs into HBM bytes per launch:
+each counter (KiB per dispatch) is scaled by what it reads for a plain 1 GiB device copy
+(`bench.py --copy-probe`), so the figure is in true bytes. Dispatches are named by the decode-step
+kernel kind they belong to; the JSON carries a hash of the kernel sources, and bench.py reports the
+traffic only while the sources still hash the same.
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stats(path: str, cmd: str) -> None:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print("# rocprofv3 kernel statistics\n")
+    print("Command (run from /tmp with TMPDIR=/tmp on one MI355X):\n")
+    print("```\n" + cmd + "\n```\n")
+    print("| calls | avg (us) | min (us) | max (us) | total (ms) | % | kernel |")
+    print("|---:|---:|---:|---:|---:|---:|---|")
+    for r in rows[:25]:
+        name = r["Name"].replace("|", "\\|")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        print(f"| {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+              f"{float(r['Percentage']):.2f} | `{name}` |")
+
+
+def _counter_rows(d: str):
+    return list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+
+
+def _copy_factor(d: str) -> float:
+    vals = [float(r["Counter_Value"]) * 1024 for r in _counter_rows(d) if "copyBuffer" in r["Kernel_Name"]]
+    return COPY_BYTES / (sum(vals) / len(vals))
+
+
+# Which decode-step kernel kind a (kernel, grid size) dispatch of the batch-1 Qwen3-0.6B step is.
+def _kind_bs1(name: str, grid: int) -> str:
+    if "k_attn_rows" in name:
+        return "attn_decode"
+    if "k_attn_combine" in name:
+        return "attn_combine"
+    if "k_sample" in name:
+        return "sample"
+    if "k_gemv<gr::BF16, 1, 8, 2>" in name:
+        return "lm_head"
+    if "k_gemv<gr::BF16, 1, 1, 8>" in name:
+        return "down_proj"
+    if "k_gemv<gr::BF16, 1, 1, 4>" in name:
+        return "o_proj"
+    if "k_gemv<gr::BF16, 1, 2, 2>" in name:
+        return "gate_up_silu" if grid == 196608 else "qkv_proj"
+    return ""
+
+
+def traffic(cf: str, cw: str, f: str, w: str, workload: str, cmd: str) -> None:
+    ff, wf = _copy_factor(cf), _copy_factor(cw)
+    kinds = {}
+    for d, fac, key in ((f, ff, "fetch_bytes"), (w, wf, "write_bytes")):
+        acc = {}
+        for r in _counter_rows(d):
+            k = _kind_bs1(r["Kernel_Name"], int(r["Grid_Size"]))
+            if k:
+                acc.setdefault(k, []).append(float(r["Counter_Value"]) * 1024 * fac)
+        for k, v in acc.items():
+            kinds.setdefault(k, {})[key] = round(sum(v) / len(v))
+            kinds[k]["dispatches"] = len(v)
+    print(json.dumps({"source_hash": source_hash(), "workload": workload, "command": cmd,
+                      "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "kinds": kinds}, indent=1))
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:8])
+    else:
+        raise SystemExit(__doc__)
