@@ -162,10 +162,12 @@ class Decoder:
             setattr(w, "d_" + n, parr(per[n]) if has else None)
         self.weights_struct = w
 
-        # KV pools: zero-filled, [num_blocks][kv_heads][16][head_dim] per layer
-        pool_shape = (num_blocks, shape.kv_heads, 16, shape.head_dim)
-        self.k_pool = [torch.zeros(pool_shape, dtype=dt, device=dev) for _ in range(L)]
-        self.v_pool = [torch.zeros(pool_shape, dtype=dt, device=dev) for _ in range(L)]
+        # KV pools, zero-filled, per layer: K [num_blocks][kv_heads][16][head_dim] (key-major) and
+        # V [num_blocks][kv_heads][head_dim][16] (dim-major)
+        k_shape = (num_blocks, shape.kv_heads, 16, shape.head_dim)
+        v_shape = (num_blocks, shape.kv_heads, shape.head_dim, 16)
+        self.k_pool = [torch.zeros(k_shape, dtype=dt, device=dev) for _ in range(L)]
+        self.v_pool = [torch.zeros(v_shape, dtype=dt, device=dev) for _ in range(L)]
         rows = max(max_batch, max_logit_rows)
         self.logits = torch.zeros((rows, shape.vocab), dtype=torch.float32, device=dev)
         self.tokens = torch.zeros(rows, dtype=torch.int32, device=dev)

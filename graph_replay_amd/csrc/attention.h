@@ -1,16 +1,28 @@
 // QK-norm + RoPE + paged KV write, and attention over the paged KV pool.
 //
-// Pool layout per layer: [num_blocks][kv_heads][block_size = 16][head_dim], so one (block, kv head)
-// tile is contiguous (4 KiB at head_dim 128 in 16-bit types) and is read with 16-byte loads.
+// Pool layout per layer: K is [num_blocks][kv_heads][block_size = 16][head_dim] (key-major) and V is
+// [num_blocks][kv_heads][head_dim][block_size = 16] (dim-major), so one (block, kv head) tile of
+// either is contiguous (4 KiB at head_dim 128 in 16-bit types). Key-major K rows are the row
+// operand of the score product; dim-major V gives each lane four consecutive keys of one dim in a
+// single 8-byte load, the operand layout of the value product.
 // A row with slot -1 (padding) writes its K and V to the scratch block num_blocks - 1, which no
 // block table holds ("Removing overhead: fusion, graphs and async scheduling", section "CUDA
 // graphs for a changing batch"). A row with seq_len 0 gets a zero attention output.
 #pragma once
 #include "common.h"
+#include "gemm.h"
 
 namespace gr {
 
 constexpr int kBlk = 16;  // tokens per KV block
+
+// element offsets in one layer's pools of token `off` of block `blk`, kv head g: K row start, V dim 0
+__device__ inline size_t pool_k_at(int blk, int nkv, int g, int off, int d) {
+  return ((static_cast<size_t>(blk) * nkv + g) * kBlk + off) * d;
+}
+__device__ inline size_t pool_v_at(int blk, int nkv, int g, int off, int d) {
+  return (static_cast<size_t>(blk) * nkv + g) * kBlk * d + off;   // dim i at + i * kBlk
+}
 
 // One wave per (row, head). Heads [0, nq) are query heads: RMSNorm over head_dim (qk_norm), then
 // rotate-half RoPE at the row's position, stored fp32 to q_out. Heads [nq, nq + nkv) are KV heads:
@@ -63,15 +75,14 @@ __global__ __launch_bounds__(64) void k_qkv_post(int nq, int nkv, int d, const f
   const int sl = slot[row];
   const int blk = sl >= 0 ? sl / kBlk : num_blocks - 1;
   const int off = sl >= 0 ? sl % kBlk : 0;
-  const size_t base = ((static_cast<size_t>(blk) * nkv + g) * kBlk + off) * d;
   if (act) {
-    S* kp = static_cast<S*>(k_pool) + base;
-    S* vp = static_cast<S*>(v_pool) + base;
+    S* kp = static_cast<S*>(k_pool) + pool_k_at(blk, nkv, g, off, d);
+    S* vp = static_cast<S*>(v_pool) + pool_v_at(blk, nkv, g, off, d);
     kp[lane] = T::from_f(y0);
     kp[lane + half] = T::from_f(y1);
     const int vcol = (nq + nkv + g) * d;
-    vp[lane] = T::from_f(fetch(vcol + lane));
-    vp[lane + half] = T::from_f(fetch(vcol + lane + half));
+    vp[lane * kBlk] = T::from_f(fetch(vcol + lane));
+    vp[(lane + half) * kBlk] = T::from_f(fetch(vcol + lane + half));
   }
 }
 
@@ -129,73 +140,15 @@ __device__ inline void norm_rope_pair(float& x0, float& x1, const void* gain, fl
   x1 = y1;
 }
 
-// Attention with one query row per request ("One forward per step", section "What changed"),
-// split over the key range so that short batches still fill the GPU (the same page, section
-// "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers keys
-// [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends on
-// the bucket only and replays as captured. A row with one split writes its output; otherwise each
-// split writes (max, sum, unnormalised output) and k_attn_combine merges them in split order.
-// Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv query
-// heads sharing the KV head are processed together.
+// Queries of heads g*G .. g*G+G-1 of `row` into qs, scaled by 1/sqrt(D). With the fused decode
+// prologue (a.q == nullptr) they are built from the QKV projection output here, and the split that
+// holds key L-1 (holds_new) also writes the row's new K and V to its slot. Ends with a block barrier,
+// so every key of the split is readable afterwards.
 template <class T, int D, int G>
-__global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
+__device__ inline void attn_prologue(const AttnRowsArgs& a, int row, int g, bool holds_new, float (*qs)[D]) {
   using S = typename T::S;
-  constexpr int KL = D / 8;          // dims per lane in the score phase (8 lanes per key)
-  constexpr int VG = 64 / (D / 8);   // key groups in the value phase (lane owns 8 dims)
   constexpr int half = D / 2;
-  __shared__ float p_s[4][G][kBlk];
-  __shared__ float wm[4][G], wl[4][G];
-  __shared__ float wo[4][G][D];
-  __shared__ float qs[G][D];
-  const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int L = a.seq_lens[row];
-  const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
-  S* out = static_cast<S*>(a.out) + static_cast<size_t>(row) * a.nq * D;
-  if (L <= 0) {
-    if (sp == 0) {
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x) out[(g * G) * D + i] = T::from_f(0.f);
-    }
-    return;
-  }
-  if (sp >= nsplit) return;
-  const int t0 = sp * a.split_tokens, t1 = min(L, t0 + a.split_tokens);
-  const int req = a.row_req ? a.row_req[row] : row;
-  const int* bt = a.block_table + static_cast<size_t>(req) * a.bt_stride;
-  const int sub = lane & 7, kt = lane >> 3;
-  const int vd = (lane % (D / 8)) * 8;  // value-phase dims of this lane
-  const int vg = lane / (D / 8);        // value-phase key group
-  const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
-
-  // K and V tiles of one 16-key block, loaded straight into registers
-  constexpr int KV16 = KL * sizeof(S) / 16;               // 16-byte vectors per lane per key pass
-  constexpr int VV = 8 * sizeof(S) / 16;                  // 16-byte vectors per 8 dims
-  uint4 kr[2][KV16 > 0 ? KV16 : 1], vr[kBlk / VG][VV];
-  auto load_kv = [&](int bi, uint4 (&kk)[2][KV16 > 0 ? KV16 : 1], uint4 (&vv)[kBlk / VG][VV]) {
-    const int tb = t0 + bi * kBlk;
-    const int pb0 = (tb / kBlk < a.bt_stride) ? bt[tb / kBlk] : -1;
-    const int pb = pb0 >= 0 ? pb0 : a.num_blocks - 1;
-    const size_t tile = (static_cast<size_t>(pb) * a.nkv + g) * kBlk * D;
-    const S* kp = static_cast<const S*>(a.k_pool) + tile;
-    const S* vp = static_cast<const S*>(a.v_pool) + tile;
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-      for (int v = 0; v < KV16; ++v)
-        kk[ps][v] = *reinterpret_cast<const uint4*>(kp + (ps * 8 + kt) * D + sub * KL + v * (16 / sizeof(S)));
-#pragma unroll
-    for (int i = 0; i < kBlk / VG; ++i)
-#pragma unroll
-      for (int v = 0; v < VV; ++v)
-        vv[i][v] = *reinterpret_cast<const uint4*>(vp + (vg + i * VG) * D + vd + v * (16 / sizeof(S)));
-  };
-  // The first block of this wave is loaded before the query prologue, unless it holds key L-1 of
-  // a fused decode row (the prologue writes that key first).
-  const bool writes_new = (a.q == nullptr) && (sp == nsplit - 1);
-  const bool pre = (wid < nblk) && !(writes_new && wid == nblk - 1);
-  if (pre) load_kv(wid, kr, vr);
-
-  // queries of heads g*G .. g*G+G-1 into LDS (scaled by 1/sqrt(D))
   if (a.q) {
     for (int i = threadIdx.x; i < G * D; i += blockDim.x)
       qs[i / D][i % D] = a.q[(static_cast<size_t>(row) * a.nq + g * G) * D + i] * a.scale;
@@ -219,25 +172,123 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
         qs[j][lane + half] = x1 * a.scale;
       }
     }
-    if (sp == nsplit - 1 && wid == 3) {
-      // this split holds key L-1: write the row's new K and V before reading any key
+    if (holds_new && wid == 3) {
+      // write the row's new K and V before any key of the split is read
       const int kcol = (a.nq + g) * D, vcol = (a.nq + a.nkv + g) * D;
       float k0 = act ? fetch(kcol + lane) : 0.f, k1 = act ? fetch(kcol + lane + half) : 0.f;
       norm_rope_pair<T, D>(k0, k1, a.k_norm, a.eps, c, sn);
       const int sl = a.slot[row];
       const int blk = sl >= 0 ? sl / kBlk : a.num_blocks - 1;
-      const size_t base = ((static_cast<size_t>(blk) * a.nkv + g) * kBlk + (sl >= 0 ? sl % kBlk : 0)) * D;
+      const int off = sl >= 0 ? sl % kBlk : 0;
       if (act) {
-        S* kp = static_cast<S*>(a.k_pool) + base;
-        S* vp = static_cast<S*>(a.v_pool) + base;
+        S* kp = static_cast<S*>(a.k_pool) + pool_k_at(blk, a.nkv, g, off, D);
+        S* vp = static_cast<S*>(a.v_pool) + pool_v_at(blk, a.nkv, g, off, D);
         kp[lane] = T::from_f(k0);
         kp[lane + half] = T::from_f(k1);
-        vp[lane] = T::from_f(fetch(vcol + lane));
-        vp[lane + half] = T::from_f(fetch(vcol + lane + half));
+        vp[lane * kBlk] = T::from_f(fetch(vcol + lane));
+        vp[(lane + half) * kBlk] = T::from_f(fetch(vcol + lane + half));
       }
     }
   }
   __syncthreads();
+}
+
+// Combine the four waves' (max, sum, unnormalised output) in wave order, then write the output
+// (single split) or this split's partial. Call after a block barrier that follows the LDS writes.
+template <class T, int D, int G>
+__device__ inline void attn_finish(const AttnRowsArgs& a, int row, int g, int sp, int nsplit, const float (*wm)[G],
+                                   const float (*wl)[G], const float (*wo)[G][D]) {
+  using S = typename T::S;
+  S* out = static_cast<S*>(a.out) + static_cast<size_t>(row) * a.nq * D;
+  float* part = a.partials + (static_cast<size_t>(row) * a.nq + g * G) * a.max_splits * (D + 2);
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int j = i / D, dd = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][j]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (wm[w][j] == -INFINITY) ? 0.f : __expf(wm[w][j] - M);
+      Ls += wl[w][j] * f;
+      O += wo[w][j][dd] * f;
+    }
+    if (nsplit == 1) {
+      out[(g * G + j) * D + dd] = T::from_f(O / Ls);
+    } else {
+      float* pp = part + (static_cast<size_t>(j) * a.max_splits + sp) * (D + 2);
+      pp[2 + dd] = O;
+      if (dd == 0) { pp[0] = M; pp[1] = Ls; }
+    }
+  }
+}
+
+// Attention with one query row per request ("One forward per step", section "What changed"),
+// split over the key range so that short batches still fill the GPU (the same page, section
+// "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers keys
+// [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends on
+// the bucket only and replays as captured. A row with one split writes its output; otherwise each
+// split writes (max, sum, unnormalised output) and k_attn_combine merges them in split order.
+// Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv query
+// heads sharing the KV head are processed together. Two kernels share this contract:
+// k_attn_rows_mfma (16-bit types, matrix cores) and k_attn_rows (any type, fp32 FMA; fp32 models).
+
+// fp32 FMA version: 8 lanes per key in the score phase, a lane owns 8 dims in the value phase.
+template <class T, int D, int G>
+__global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
+  using S = typename T::S;
+  constexpr int KL = D / 8;          // dims per lane in the score phase (8 lanes per key)
+  constexpr int VG = 64 / (D / 8);   // key groups in the value phase (lane owns 8 dims)
+  __shared__ float p_s[4][G][kBlk];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wo[4][G][D];
+  __shared__ float qs[G][D];
+  const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int L = a.seq_lens[row];
+  const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
+  if (L <= 0) {
+    if (sp == 0) {
+      S* out = static_cast<S*>(a.out) + static_cast<size_t>(row) * a.nq * D;
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x) out[(g * G) * D + i] = T::from_f(0.f);
+    }
+    return;
+  }
+  if (sp >= nsplit) return;
+  const int t0 = sp * a.split_tokens, t1 = min(L, t0 + a.split_tokens);
+  const int req = a.row_req ? a.row_req[row] : row;
+  const int* bt = a.block_table + static_cast<size_t>(req) * a.bt_stride;
+  const int sub = lane & 7, kt = lane >> 3;
+  const int vd = (lane % (D / 8)) * 8;  // value-phase dims of this lane
+  const int vg = lane / (D / 8);        // value-phase key group
+  const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+
+  // K and V of one 16-key block, loaded straight into registers
+  constexpr int KV16 = KL * sizeof(S) / 16;               // 16-byte vectors per lane per key pass
+  uint4 kr[2][KV16 > 0 ? KV16 : 1];
+  S vr[kBlk / VG][8];
+  auto load_kv = [&](int bi) {
+    const int tb = t0 + bi * kBlk;
+    const int pb0 = (tb / kBlk < a.bt_stride) ? bt[tb / kBlk] : -1;
+    const int pb = pb0 >= 0 ? pb0 : a.num_blocks - 1;
+    const S* kp = static_cast<const S*>(a.k_pool) + pool_k_at(pb, a.nkv, g, 0, D);
+    const S* vp = static_cast<const S*>(a.v_pool) + pool_v_at(pb, a.nkv, g, 0, D);
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int v = 0; v < KV16; ++v)
+        kr[ps][v] = *reinterpret_cast<const uint4*>(kp + (ps * 8 + kt) * D + sub * KL + v * (16 / sizeof(S)));
+#pragma unroll
+    for (int i = 0; i < kBlk / VG; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vr[i][e] = vp[(vd + e) * kBlk + vg + i * VG];
+  };
+  // The first block of this wave is loaded before the query prologue, unless it holds key L-1 of
+  // a fused decode row (the prologue writes that key first).
+  const bool holds_new = sp == nsplit - 1;
+  const bool pre = (wid < nblk) && !(a.q == nullptr && holds_new && wid == nblk - 1);
+  if (pre) load_kv(wid);
+  attn_prologue<T, D, G>(a, row, g, holds_new, qs);
 
   // score-phase slice of this lane: dims (lane % 8) * KL .. + KL of each query head
   float q[G][KL];
@@ -256,7 +307,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   }
   for (int bi = wid; bi < nblk; bi += 4) {
     const int tb = t0 + bi * kBlk;                          // first key of the block
-    if (bi != wid || !pre) load_kv(bi, kr, vr);
+    if (bi != wid || !pre) load_kv(bi);
 
     // scores: 8 lanes per key, two passes of 8 keys
     float sc[2][G];
@@ -306,16 +357,13 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
     // values: lane owns dims vd .. vd+7 for keys vg, vg + VG, ...
 #pragma unroll
     for (int i = 0; i < kBlk / VG; ++i) {
-      float vf[8];
-#pragma unroll
-      for (int v = 0; v < VV; ++v) cvt_vec<T>(vr[i][v], vf + v * (16 / sizeof(S)));
       // a masked key adds nothing, even if its slot holds NaN (0 * NaN would not be 0)
       const bool live = tb + vg + i * VG < t1;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float p = p_s[wid][j][vg + i * VG];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = live ? fmaf(p, vf[e], o[j][e]) : o[j][e];
+        for (int e = 0; e < 8; ++e) o[j][e] = live ? fmaf(p, T::to_f(vr[i][e]), o[j][e]) : o[j][e];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -337,28 +385,196 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
     for (int j = 0; j < G; ++j) { wm[wid][j] = m[j]; wl[wid][j] = l[j]; }
   }
   __syncthreads();
-  // combine the four waves (fixed order); thread t handles (head, dim) pairs
-  float* part = a.partials + (static_cast<size_t>(row) * a.nq + g * G) * a.max_splits * (D + 2);
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int j = i / D, dd = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][j]);
-    float Ls = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = (wm[w][j] == -INFINITY) ? 0.f : __expf(wm[w][j] - M);
-      Ls += wl[w][j] * f;
-      O += wo[w][j][dd] * f;
+  attn_finish<T, D, G>(a, row, g, sp, nsplit, wm, wl, wo);
+}
+
+// Matrix-core version for 16-bit K/V (G <= 16 query heads per KV head). Per 16-key block a wave
+// computes S^T[key][head] = K Q^T with v_mfma_f32_16x16x32 (K rows straight from the pool, Q^T
+// rounded to the storage type and held in registers, columns past G zero), runs the online softmax
+// on the accumulator (lane: keys 4*(l/16)+i of head l%16), and adds O^T[dim][head] += V^T P^T with
+// v_mfma_f32_16x16x16, whose P^T operand is that accumulator rounded to the storage type and whose
+// V^T operand is one 8-byte load of four consecutive keys from the dim-major V tile. A wave takes
+// KB blocks per step (blocks b, b+4, ..., b+4(KB-1)) under one softmax update, so KB tiles are in
+// flight at once; the next step's K is requested once the score products have issued and its V
+// once the value products have. The block-table entries of the wave's blocks are fetched up front.
+template <class T, int D, int G, int KB>
+__global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRowsArgs a) {
+  using S = typename T::S;
+  static_assert(sizeof(S) == 2 && G <= 16 && D % 32 == 0, "16-bit types, at most 16 heads per KV head");
+  constexpr int KS = D / 32;   // k-steps of the score product
+  constexpr int DT = D / 16;   // 16-dim tiles of the value product
+  __shared__ __align__(16) float qs[G][D];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wo[4][G][D];
+  const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int req = a.row_req ? a.row_req[row] : row;
+  const int* bt = a.block_table + static_cast<size_t>(req) * a.bt_stride;
+  const int t0 = sp * a.split_tokens;
+  // table entries of this wave's blocks wid + 4k (lane k), fetched together with seq_len so that
+  // no key load waits on a table load inside the loop
+  const int bt_lane = t0 / kBlk + wid + 4 * lane;
+  const int bt_pre = bt_lane < a.bt_stride ? bt[bt_lane] : -1;
+  const int L = a.seq_lens[row];
+  const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
+  if (L <= 0) {
+    if (sp == 0) {
+      S* out = static_cast<S*>(a.out) + static_cast<size_t>(row) * a.nq * D;
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x) out[(g * G) * D + i] = T::from_f(0.f);
     }
-    if (nsplit == 1) {
-      out[(g * G + j) * D + dd] = T::from_f(O / Ls);
-    } else {
-      float* pp = part + (static_cast<size_t>(j) * a.max_splits + sp) * (D + 2);
-      pp[2 + dd] = O;
-      if (dd == 0) { pp[0] = M; pp[1] = Ls; }
+    return;
+  }
+  if (sp >= nsplit) return;
+  const int t1 = min(L, t0 + a.split_tokens);
+  const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
+
+  uint4 kf[KB][KS];   // K fragment: key col, dims ks*32 + 8*grp .. + 8
+  uint2 vf[KB][DT];   // V^T fragment: dim t*16 + col, keys 4*grp .. + 4
+  // pool block of the split's block bi (scratch if unmapped or past the split)
+  auto tile_of = [&](int bi) -> int {
+    const int k = (bi - wid) / 4;       // wave-uniform
+    int pb0 = -1;
+    if (bi < nblk) {
+      if (k < 64) {
+        pb0 = __builtin_amdgcn_readlane(bt_pre, k);
+      } else {
+        const int tb = t0 + bi * kBlk;
+        pb0 = (tb / kBlk < a.bt_stride) ? bt[tb / kBlk] : -1;
+      }
+    }
+    return pb0 >= 0 ? pb0 : a.num_blocks - 1;
+  };
+  auto load_k = [&](int kb, int pb) {
+    const S* kp = static_cast<const S*>(a.k_pool) + pool_k_at(pb, a.nkv, g, col, D) + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *reinterpret_cast<const uint4*>(kp + ks * 32);
+  };
+  auto load_v = [&](int kb, int pb) {
+    const S* vp = static_cast<const S*>(a.v_pool) + pool_v_at(pb, a.nkv, g, 4 * grp, D) + col * kBlk;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) vf[kb][t] = *reinterpret_cast<const uint2*>(vp + t * 16 * kBlk);
+  };
+  // The first step's blocks are loaded before the query prologue, except in the split that holds
+  // key L-1 of a fused decode row (the prologue writes that key first).
+  const bool holds_new = sp == nsplit - 1;
+  const bool pre = (wid < nblk) && !(a.q == nullptr && holds_new);
+  if (pre) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int pb = tile_of(wid + 4 * kb);
+      load_k(kb, pb);
+      load_v(kb, pb);
     }
   }
+  attn_prologue<T, D, G>(a, row, g, holds_new, qs);
+  if (wid < nblk && !pre) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int pb = tile_of(wid + 4 * kb);
+      load_k(kb, pb);
+      load_v(kb, pb);
+    }
+  }
+  // Q^T fragments: column = query head col (zero past G), k slots = dims ks*32 + 8*grp .. + 8
+  uint4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (col < G) {
+      const float* src = &qs[col < G ? col : 0][ks * 32 + 8 * grp];
+      qf[ks] = make_uint4(pack2<T>(src[0], src[1]), pack2<T>(src[2], src[3]), pack2<T>(src[4], src[5]),
+                          pack2<T>(src[6], src[7]));
+    } else {
+      qf[ks] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  f32x4_t acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+  for (int b0 = wid; b0 < nblk; b0 += 4 * KB) {
+    const bool more = b0 + 4 * KB < nblk;
+    f32x4_t s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma16x16x32<T>(kf[kb][ks], qf[ks], s[kb]);
+    }
+    if (more) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) load_k(kb, tile_of(b0 + 4 * KB + 4 * kb));
+    }
+    // this lane holds keys tb + 4*grp + i of head col (tb: first key of block b0 + 4kb); keys past
+    // the split end, and blocks past the split, are masked
+    float bm = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int tb = t0 + (b0 + 4 * kb) * kBlk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[kb][i] = (tb + 4 * grp + i < t1) ? s[kb][i] : -INFINITY;
+        bm = fmaxf(bm, s[kb][i]);
+      }
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);                          // finite: block b0 has a live key
+    const float corr = __expf(m - mn);
+    float ps = 0.f;
+    uint2 pt[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __expf(s[kb][i] - mn);
+        ps += p[i];
+      }
+      pt[kb] = make_uint2(pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]));
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * corr + ps;
+    m = mn;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] *= corr;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int tb = t0 + (b0 + 4 * kb) * kBlk;
+      if (tb + kBlk > t1) {
+        // a masked key adds nothing, even if its slot holds NaN (0 * NaN would not be 0)
+        const int k0 = tb + 4 * grp;
+        const uint32_t m0 = (k0 < t1 ? 0xffffu : 0u) | (k0 + 1 < t1 ? 0xffff0000u : 0u);
+        const uint32_t m1 = (k0 + 2 < t1 ? 0xffffu : 0u) | (k0 + 3 < t1 ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          vf[kb][t].x &= m0;
+          vf[kb][t].y &= m1;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] = mfma16x16x16<T>(vf[kb][t], pt[kb], acc[t]);
+    }
+    if (more) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) load_v(kb, tile_of(b0 + 4 * KB + 4 * kb));
+    }
+  }
+  // per-wave state of head col: rows 4*grp + i of each 16-dim tile t
+  if (col < G) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[wid][col < G ? col : 0][t * 16 + 4 * grp + i] = acc[t][i];
+    if (grp == 0) {
+      wm[wid][col < G ? col : 0] = m;
+      wl[wid][col < G ? col : 0] = lsum;
+    }
+  }
+  __syncthreads();
+  attn_finish<T, D, G>(a, row, g, sp, nsplit, wm, wl, wo);
 }
 
 // Merge the split partials of rows with more than one split: grid (rows, nq), block D threads

@@ -16,12 +16,8 @@ struct BF16 {
   using S = uint16_t;
   static constexpr int kEPV = 8;
   __device__ static inline float to_f(S x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
-  __device__ static inline S from_f(float f) {  // round to nearest even, NaN kept quiet
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<S>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<S>(u >> 16);
-  }
+  // round to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32)
+  __device__ static inline S from_f(float f) { return __builtin_bit_cast(S, static_cast<__bf16>(f)); }
 };
 struct F16 {
   using S = _Float16;

@@ -110,7 +110,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   using S = typename T::S;
   constexpr int EPV = T::kEPV;
   constexpr int KC = (32768 / (MT * static_cast<int>(sizeof(S)))) / (64 * EPV) * (64 * EPV);
-  constexpr int KPT = 8;                                  // norm prologue: K <= 256 * KPT
   __shared__ __align__(16) S xs[MT * KC];
   __shared__ float red[4][MT];
 
@@ -151,41 +150,69 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
   load_w(0, min(KC, K) / EPV, 0);
 
   if (a.norm) {
+    // thread t owns elements 4t .. 4t+3 of each 1024-wide slice (16-byte loads); K <= 2048
+    constexpr int NS = 2;                                   // slices
     const S* g = static_cast<const S*>(a.gain);
-    float gk[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) gk[i] = T::to_f(g[min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)]);
-    // v = r + sum of deltas (or the embedding row), every load of a phase issued before any use;
-    // indices are clamped so all loads are in bounds, out-of-range lanes are zeroed afterwards
-    float v[MT][KPT];
+    const int e0 = 4 * threadIdx.x;
+    float gk[NS][4], v[MT][NS][4];
     size_t rowoff[MT];
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) rowoff[mm] = static_cast<size_t>(m0 + min(mm, mrows - 1)) * K;
-    if (a.embed) {
-      size_t eoff[MT];
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) eoff[mm] = static_cast<size_t>(a.tok[m0 + min(mm, mrows - 1)]) * K;
+    for (int sl = 0; sl < NS; ++sl) {
+      const int k = min(e0 + 1024 * sl, K - 4);             // clamped: always in bounds
+      if constexpr (sizeof(S) == 2) {
+        const uint2 gv = *reinterpret_cast<const uint2*>(g + k);
+        const S* ge = reinterpret_cast<const S*>(&gv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gk[sl][e] = T::to_f(ge[e]);
+      } else {
+        const float4 gv = *reinterpret_cast<const float4*>(g + k);
+        gk[sl][0] = gv.x; gk[sl][1] = gv.y; gk[sl][2] = gv.z; gk[sl][3] = gv.w;
+      }
+    }
+    if (a.embed) {
       const S* E = static_cast<const S*>(a.embed);
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm)
+      for (int mm = 0; mm < MT; ++mm) {
+        const size_t eo = static_cast<size_t>(a.tok[m0 + min(mm, mrows - 1)]) * K;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) v[mm][i] = T::to_f(E[eoff[mm] + min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)]);
+        for (int sl = 0; sl < NS; ++sl) {
+          const int k = min(e0 + 1024 * sl, K - 4);
+          if constexpr (sizeof(S) == 2) {
+            const uint2 ev = *reinterpret_cast<const uint2*>(E + eo + k);
+            const S* ee = reinterpret_cast<const S*>(&ev);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[mm][sl][e] = T::to_f(ee[e]);
+          } else {
+            const float4 ev = *reinterpret_cast<const float4*>(E + eo + k);
+            v[mm][sl][0] = ev.x; v[mm][sl][1] = ev.y; v[mm][sl][2] = ev.z; v[mm][sl][3] = ev.w;
+          }
+        }
+      }
     } else {
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) v[mm][i] = a.r_in[rowoff[mm] + min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)];
+        for (int sl = 0; sl < NS; ++sl) {
+          const float4 rv = *reinterpret_cast<const float4*>(a.r_in + rowoff[mm] + min(e0 + 1024 * sl, K - 4));
+          v[mm][sl][0] = rv.x; v[mm][sl][1] = rv.y; v[mm][sl][2] = rv.z; v[mm][sl][3] = rv.w;
+        }
       for (int s = 0; s < a.n_delta; ++s) {
         const float* dp = a.delta + s * a.delta_stride;
-        float dv[MT][KPT];
+        float4 dv[MT][NS];
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-          for (int i = 0; i < KPT; ++i) dv[mm][i] = dp[rowoff[mm] + min(static_cast<int>(threadIdx.x) + 256 * i, K - 1)];
+          for (int sl = 0; sl < NS; ++sl)
+            dv[mm][sl] = *reinterpret_cast<const float4*>(dp + rowoff[mm] + min(e0 + 1024 * sl, K - 4));
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-          for (int i = 0; i < KPT; ++i) v[mm][i] += dv[mm][i];
+          for (int sl = 0; sl < NS; ++sl) {
+            v[mm][sl][0] += dv[mm][sl].x; v[mm][sl][1] += dv[mm][sl].y;
+            v[mm][sl][2] += dv[mm][sl].z; v[mm][sl][3] += dv[mm][sl].w;
+          }
       }
     }
     float ss[MT];
@@ -193,12 +220,22 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
     for (int mm = 0; mm < MT; ++mm) {
       ss[mm] = 0.f;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int k = threadIdx.x + 256 * i;
+      for (int sl = 0; sl < NS; ++sl) {
+        const int k = e0 + 1024 * sl;
         const bool ok = mm < mrows && k < K;
-        v[mm][i] = ok ? v[mm][i] : 0.f;
-        if (ok && blockIdx.x == 0 && a.r_out) a.r_out[rowoff[mm] + k] = v[mm][i];
-        ss[mm] += v[mm][i] * v[mm][i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[mm][sl][e] = ok ? v[mm][sl][e] : 0.f;
+          ss[mm] += v[mm][sl][e] * v[mm][sl][e];
+        }
+        if (ok && blockIdx.x == 0 && a.r_out)
+          *reinterpret_cast<float4*>(a.r_out + rowoff[mm] + k) =
+              make_float4(v[mm][sl][0], v[mm][sl][1], v[mm][sl][2], v[mm][sl][3]);
+        if (k < K) {
+          // x = gain * v to LDS; the 1 / rms factor is applied to the dot products in the epilogue
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xs[mm * KC + k + e] = T::from_f(mm < mrows ? v[mm][sl][e] * gk[sl][e] : 0.f);
+        }
       }
       ss[mm] = wave_sum(ss[mm]);
     }
@@ -206,15 +243,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) red[wid][mm] = ss[mm];
     }
-    // x = gain * v goes to LDS now; the 1 / rms factor is a per-row scalar, applied to the dot
-    // products in the epilogue, so no barrier waits for the sum of squares before the matmul
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int k = threadIdx.x + 256 * i;
-        if (k < K) xs[mm * KC + k] = T::from_f(mm < mrows ? v[mm][i] * gk[i] : 0.f);
-      }
   }
 
   float acc[ROWS][MT];
@@ -312,6 +340,32 @@ __device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   } else {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// 16x16x16 variant: lane l holds k = 4 * (l / 16) .. + 4 of its row (A) or column (B)
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ inline f32x4_t mfma16x16x16(const uint2& a, const uint2& b, f32x4_t c) {
+  if constexpr (__is_same(T, BF16)) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+}
+
+// two fp32 values rounded to the 16-bit storage type, packed low then high
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <class T>
+__device__ inline uint32_t pack2(float x, float y) {
+  if constexpr (__is_same(T, BF16)) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, f16x2_t));
   }
 }
 

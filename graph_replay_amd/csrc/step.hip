@@ -374,14 +374,24 @@ int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_
   return STEP_OK;
 }
 
+// fp32 K/V: FMA kernel; 16-bit K/V: matrix-core kernel, two blocks per wave step for long splits
+template <class T, int D, int G>
+void launch_attn_rows_g(const AttnRowsArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (std::is_same<T, F32>::value) {
+    hipLaunchKernelGGL((k_attn_rows<T, D, G>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.split_tokens >= 256) hipLaunchKernelGGL((k_attn_rows_mfma<T, D, G, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_rows_mfma<T, D, G, 1>), grid, dim3(256), 0, s, a);
+  }
+}
 template <class T, int D>
 hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream_t s) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn_rows<T, D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_rows<T, D, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_rows<T, D, 4>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_rows<T, D, 6>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_attn_rows<T, D, 8>), grid, dim3(256), 0, s, a); break;
+    case 1: launch_attn_rows_g<T, D, 1>(a, grid, s); break;
+    case 2: launch_attn_rows_g<T, D, 2>(a, grid, s); break;
+    case 4: launch_attn_rows_g<T, D, 4>(a, grid, s); break;
+    case 6: launch_attn_rows_g<T, D, 6>(a, grid, s); break;
+    default: launch_attn_rows_g<T, D, 8>(a, grid, s); break;
   }
   return hipGetLastError();
 }

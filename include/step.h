@@ -19,9 +19,12 @@
  *     allocates no device memory after step_init returns; it owns only the context, its
  *     graphs and a small pinned host staging area.
  *   - Matrices are row-major [out_features][in_features] in the model dtype.
- *   - The KV pool of each layer is [num_blocks][kv_heads][block_size][head_dim] in the model
- *     dtype, zero-filled by the caller. Block num_blocks-1 is the scratch block: it must never
- *     appear in a block table; rows with slot -1 write there.
+ *   - The KV pools of each layer are in the model dtype, zero-filled by the caller. The K pool is
+ *     [num_blocks][kv_heads][block_size][head_dim] (key-major); the V pool is
+ *     [num_blocks][kv_heads][head_dim][block_size] (dim-major), so element (token t of a block,
+ *     dim i) of a (block, kv head) tile is at t * head_dim + i in K and at i * block_size + t in V.
+ *     Block num_blocks-1 is the scratch block: it must never appear in a block table; rows with
+ *     slot -1 write there.
  *   - A token at absolute position p of a request whose block-table row is bt lives at slot
  *     bt[p / block_size] * block_size + p % block_size.
  *   - seq_len of a decode row counts the keys the row attends to INCLUDING its own token

@@ -62,7 +62,7 @@ class Scenario:
             bi = torch.as_tensor(np.concatenate(blk), device=dec.device, dtype=torch.long)
             oi = torch.as_tensor(np.concatenate(off), device=dec.device, dtype=torch.long)
             dec.k_pool[l][bi, :, oi, :] = torch.cat(ks).to(dec.device)
-            dec.v_pool[l][bi, :, oi, :] = torch.cat(vs).to(dec.device)
+            dec.v_pool[l][bi, :, :, oi] = torch.cat(vs).to(dec.device)   # V is dim-major
         torch.cuda.synchronize(dec.device)
 
     def table_array(self, rows: Optional[Sequence[int]] = None) -> np.ndarray:

@@ -201,7 +201,7 @@ def test_bs256_sampled_rows_vs_oracle_and_padding(torch_cuda):
             blk = torch.as_tensor(np.asarray(sc.tables[j])[p // 16], device=dec.device)
             off = torch.as_tensor(p % 16, device=dec.device)
             dec.k_pool[l][blk, :, off, :] = k.to(dec.device)
-            dec.v_pool[l][blk, :, off, :] = v.to(dec.device)
+            dec.v_pool[l][blk, :, :, off] = v.to(dec.device)   # V is dim-major
     toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
     temp = np.full(256, 0.7, np.float32)
     seed = 0xC0FFEE
@@ -280,7 +280,7 @@ def test_nan_poisoned_foreign_blocks_change_nothing(torch_cuda):
             if c % 16:
                 blk = sc.tables[j][(c - 1) // 16]
                 dec.k_pool[l][blk, :, c % 16:, :] = float("nan")
-                dec.v_pool[l][blk, :, c % 16:, :] = float("nan")
+                dec.v_pool[l][blk, :, :, c % 16:] = float("nan")
     # the step writes K/V at the same slots again, so rerun from the same inputs
     dec.decode(toks[:r], pos[:r], lens[:r], slots[:r], bt[:r])
     torch.cuda.synchronize()
