@@ -7,6 +7,7 @@
 // the same kernels when no graph exists), and the eager packed mixed step ("One forward per step",
 // section "What changed").
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -70,9 +71,9 @@ struct step_ctx {
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
   int stage_next = 0;
   size_t stage_bytes = 0;
-  // profiling: an event before every launch while prof_on
+  // profiling: start/stop events of every launch while prof_on
   bool prof_on = false;
-  std::vector<hipEvent_t> prof_ev;
+  std::vector<hipEvent_t> prof_ev, prof_ev_end;
   std::vector<int> prof_kind;
   std::string err;
   bool dead = false;
@@ -113,12 +114,34 @@ const char* const kKindNames[KK_COUNT] = {"qkv_proj", "qknorm_rope_kvwrite", "at
                                           "attn_combine"};
 
 // Called before every kernel launch: counts it and, while profiling, marks its start.
+// Profile events for the next launch: set by pre_launch during a profile step, taken by launch().
+struct ProfSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local ProfSlot g_prof_next;
+
 void pre_launch(step_ctx* ctx, int kind) {
-  if (ctx->prof_on && ctx->launches < static_cast<int>(ctx->prof_ev.size()) - 1) {
-    (void)hipEventRecord(ctx->prof_ev[ctx->launches], ctx->stream);
+  if (ctx->prof_on && ctx->launches < static_cast<int>(ctx->prof_ev.size())) {
+    g_prof_next = ProfSlot{ctx->prof_ev[ctx->launches], ctx->prof_ev_end[ctx->launches]};
     ctx->prof_kind[ctx->launches] = kind;
   }
   ctx->launches++;
+}
+
+// Every kernel of a step is launched here. During a profile step the launch carries start/stop
+// events, which HIP stamps with the dispatch's own begin and end times (the kernel's execution,
+// without the queueing around it); otherwise it is a plain launch, as captured into the graphs.
+template <typename... KArgs, typename... Args>
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  if (g_prof_next.start) {
+    const ProfSlot p = g_prof_next;
+    g_prof_next = ProfSlot{};
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(shmem), s, p.start, p.stop, 0u,
+                          static_cast<KArgs>(args)...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, static_cast<KArgs>(args)...);
+  }
 }
 
 // A bounded wait on the device (about iters * 3.4 us) that lets the host queue a whole step behind
@@ -262,7 +285,7 @@ struct Lin {
 
 template <class T, int MT, int ROWS, int U>
 hipError_t launch_gemv_ru(const GemmArgs& a, int epi, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv<T, MT, ROWS, U>), grid, dim3(256), 0, s, a, epi);
+  launch((k_gemv<T, MT, ROWS, U>), grid, dim3(256), 0, s, a, epi);
   return hipGetLastError();
 }
 
@@ -335,9 +358,9 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       a.ksplit = ks;
       if (l.ksplit_used) *l.ksplit_used = ks;
       dim3 grid(bx, ks);
-      if (l.M <= 16) hipLaunchKernelGGL((k_gemv_mfma<T, 1, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
-      else if (rt == 2) hipLaunchKernelGGL((k_gemv_mfma<T, 2, 4, 2>), grid, dim3(256), 0, s, a, l.epi);
-      else hipLaunchKernelGGL((k_gemv_mfma<T, 2, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
+      if (l.M <= 16) launch((k_gemv_mfma<T, 1, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
+      else if (rt == 2) launch((k_gemv_mfma<T, 2, 4, 2>), grid, dim3(256), 0, s, a, l.epi);
+      else launch((k_gemv_mfma<T, 2, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
       e = hipGetLastError();
     } else {
       const bool big = l.M > 64;
@@ -351,8 +374,8 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       a.ksplit = ks;
       if (l.ksplit_used) *l.ksplit_used = ks;
       dim3 grid(bx, by, ks);
-      if (big) hipLaunchKernelGGL((k_gemm<T, 128, 128>), grid, dim3(256), 0, s, a, l.epi);
-      else hipLaunchKernelGGL((k_gemm<T, 64, 64>), grid, dim3(256), 0, s, a, l.epi);
+      if (big) launch((k_gemm<T, 128, 128>), grid, dim3(256), 0, s, a, l.epi);
+      else launch((k_gemm<T, 64, 64>), grid, dim3(256), 0, s, a, l.epi);
       e = hipGetLastError();
     }
   } else {
@@ -367,7 +390,7 @@ int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_
              const void* embed, const int* tok, const int* row_map, float* r_out, const void* gain, void* h_out) {
   const int H = ctx->cfg.hidden;
   pre_launch(ctx, KK_NORM);
-  hipLaunchKernelGGL((k_add_rmsnorm<T>), dim3(M), dim3(256), 0, ctx->stream, H, r_in, delta, n_delta, dstride, embed,
+  launch((k_add_rmsnorm<T>), dim3(M), dim3(256), 0, ctx->stream, H, r_in, delta, n_delta, dstride, embed,
                      tok, row_map, r_out, gain, h_out, ctx->cfg.rms_eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "norm launch failed: %s", hipGetErrorString(e));
@@ -378,10 +401,10 @@ int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_
 template <class T, int D, int G>
 void launch_attn_rows_g(const AttnRowsArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (std::is_same<T, F32>::value) {
-    hipLaunchKernelGGL((k_attn_rows<T, D, G>), grid, dim3(256), 0, s, a);
+    launch((k_attn_rows<T, D, G>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.split_tokens >= 256) hipLaunchKernelGGL((k_attn_rows_mfma<T, D, G, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_rows_mfma<T, D, G, 1>), grid, dim3(256), 0, s, a);
+    if (a.split_tokens >= 256) launch((k_attn_rows_mfma<T, D, G, 2>), grid, dim3(256), 0, s, a);
+    else launch((k_attn_rows_mfma<T, D, G, 1>), grid, dim3(256), 0, s, a);
   }
 }
 template <class T, int D>
@@ -398,7 +421,7 @@ hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream
 
 template <class T, int D>
 hipError_t launch_combine(step_ctx* ctx, int rows, const AttnRowsArgs& a) {
-  hipLaunchKernelGGL((k_attn_combine<T, D>), dim3(rows, a.nq), dim3(D), sizeof(float) * 2 * a.max_splits, ctx->stream,
+  launch((k_attn_combine<T, D>), dim3(rows, a.nq), dim3(D), sizeof(float) * 2 * a.max_splits, ctx->stream,
                      a.nq, a.seq_lens, a.split_tokens, a.max_splits, a.partials, a.out);
   return hipGetLastError();
 }
@@ -449,7 +472,7 @@ int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_st
   const step_config& c = ctx->cfg;
   const Layout& L = ctx->lay;
   pre_launch(ctx, KK_QKV_POST);
-  hipLaunchKernelGGL((k_qkv_post<T>), dim3(rows, c.q_heads + c.kv_heads), dim3(64), 0, ctx->stream, c.q_heads,
+  launch((k_qkv_post<T>), dim3(rows, c.q_heads + c.kv_heads), dim3(64), 0, ctx->stream, c.q_heads,
                      c.kv_heads, c.head_dim, reinterpret_cast<const float*>(ctx->ws + L.qkv), n_parts, part_stride, pos,
                      slot, reinterpret_cast<const float*>(ctx->ws + L.rope_cos),
                      reinterpret_cast<const float*>(ctx->ws + L.rope_sin), c.qk_norm ? ctx->q_norm[layer] : nullptr,
@@ -478,7 +501,7 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
   const int nch = (vocab + chunk - 1) / chunk;
   pre_launch(ctx, KK_SAMPLE);
-  hipLaunchKernelGGL(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
+  launch(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
@@ -671,8 +694,8 @@ int run_attn_prefill(step_ctx* ctx, int layer, const MixedPlan& p, const MixedMe
   a.out = out;
   dim3 grid(p.n_tiles, (c.q_heads + 3) / 4);
   pre_launch(ctx, KK_PREFILL_ATTN);
-  if (c.head_dim == 64) hipLaunchKernelGGL((k_attn_prefill<T, 64>), grid, dim3(256), 0, ctx->stream, a);
-  else hipLaunchKernelGGL((k_attn_prefill<T, 128>), grid, dim3(256), 0, ctx->stream, a);
+  if (c.head_dim == 64) launch((k_attn_prefill<T, 64>), grid, dim3(256), 0, ctx->stream, a);
+  else launch((k_attn_prefill<T, 128>), grid, dim3(256), 0, ctx->stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "prefill attention launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
@@ -1088,11 +1111,13 @@ extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_
   if (!ctx || ctx->dead) return STEP_ESTATE;
   if (!ctx->have_batch) return fail(ctx, STEP_EINVAL, "profile step before any batch");
   if (max_kernels < 1 || !h_ms || !h_kind) return fail(ctx, STEP_EINVAL, "bad profile buffers");
-  const size_t nev = static_cast<size_t>(max_kernels) + 1;
+  const size_t nev = static_cast<size_t>(max_kernels);
   while (ctx->prof_ev.size() < nev) {
-    hipEvent_t e;
-    HIPCHK(ctx, hipEventCreate(&e));
-    ctx->prof_ev.push_back(e);
+    hipEvent_t e0, e1;
+    HIPCHK(ctx, hipEventCreate(&e0));
+    ctx->prof_ev.push_back(e0);
+    HIPCHK(ctx, hipEventCreate(&e1));
+    ctx->prof_ev_end.push_back(e1);
   }
   ctx->prof_kind.assign(ctx->prof_ev.size(), -1);
   hipLaunchKernelGGL(k_hold, dim3(1), dim3(64), 0, ctx->stream, 1000);
@@ -1101,13 +1126,13 @@ extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_
   ctx->prof_on = true;
   const int rc = run_decode_any(ctx, ctx->last_bucket);
   ctx->prof_on = false;
+  g_prof_next = ProfSlot{};
   if (rc != STEP_OK) return rc;
   const int n = std::min(ctx->launches, max_kernels);
-  HIPCHK(ctx, hipEventRecord(ctx->prof_ev[n], ctx->stream));
-  HIPCHK(ctx, hipEventSynchronize(ctx->prof_ev[n]));
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
   for (int i = 0; i < n; ++i) {
     float ms = 0.f;
-    HIPCHK(ctx, hipEventElapsedTime(&ms, ctx->prof_ev[i], ctx->prof_ev[i + 1]));
+    HIPCHK(ctx, hipEventElapsedTime(&ms, ctx->prof_ev[i], ctx->prof_ev_end[i]));
     h_ms[i] = ms;
     h_kind[i] = ctx->prof_kind[i];
   }
@@ -1145,5 +1170,6 @@ extern "C" void step_destroy(step_ctx* ctx) {
   }
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
+  for (auto& e : ctx->prof_ev_end) (void)hipEventDestroy(e);
   delete ctx;
 }

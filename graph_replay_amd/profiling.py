@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for profiles/ (measurement tooling, not the step itself).
 
     python -m graph_replay_amd.profiling stats <run>_kernel_stats.csv "<command>" > profiles/<name>.md
+    python -m graph_replay_amd.profiling kinds <run>_kernel_trace.csv >> profiles/<name>.md
     python -m graph_replay_amd.profiling traffic <copy FETCH dir> <copy WRITE dir> <FETCH dir> <WRITE dir> \\
         <workload> "<command>" > profiles/hbm_traffic.json
 
@@ -44,6 +45,24 @@ def stats(path: str, cmd: str) -> None:
         print(f"| {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
               f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
               f"{float(r['Percentage']):.2f} | `{name}` |")
+
+
+def kinds(trace: str) -> None:
+    """Markdown table of kernel durations per decode-step kind (batch-1 Qwen3-0.6B dispatches,
+    told apart by kernel name and grid size) from a rocprofv3 kernel trace."""
+    acc = {}
+    for r in csv.DictReader(open(trace)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        k = _kind_bs1(r["Kernel_Name"], grid)
+        if k:
+            acc.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("\nPer decode-step kind (kernel trace of the same run; the two projections that share the")
+    print("`k_gemv<BF16, 1, 2, 2>` instantiation are told apart by grid size):\n")
+    print("| kind | calls | avg (us) | median (us) |")
+    print("|---|---:|---:|---:|")
+    for k, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        print(f"| {k} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {v[len(v) // 2] / 1e3:.2f} |")
 
 
 def _counter_rows(d: str):
@@ -93,6 +112,8 @@ def traffic(cf: str, cw: str, f: str, w: str, workload: str, cmd: str) -> None:
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "kinds":
+        kinds(sys.argv[2])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:8])
     else:

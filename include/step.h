@@ -159,10 +159,11 @@ int step_sample(step_ctx *ctx, const float *d_logits, int32_t rows, int32_t ld, 
 
 /* Profiling (a debug aid, not part of the graphed path): runs one decode step at the bucket of the last
  * batch EAGERLY over the current static state, behind a short bounded device-side wait so the kernels
- * run back to back, with a hipEvent before every kernel, and waits for it. Writes the duration (ms,
- * start of one kernel to the start of the next) and the kind (see step_kernel_kind_name) of up to
- * max_kernels kernels into host arrays. Returns the number of kernels of the step, or a negative code.
- * It is a real step: the decode state advances exactly as in step_decode(ctx, NULL). */
+ * run back to back, launching every kernel with start/stop hipEvents that carry the dispatch's own
+ * begin and end timestamps, and waits for it. Writes the execution time (ms) and the kind (see
+ * step_kernel_kind_name) of up to max_kernels kernels into host arrays. Returns the number of kernels
+ * of the step, or a negative code. It is a real step: the decode state advances exactly as in
+ * step_decode(ctx, NULL). */
 int step_profile_decode(step_ctx *ctx, int32_t max_kernels, float *h_ms, int32_t *h_kind);
 const char *step_kernel_kind_name(int32_t kind);
 
