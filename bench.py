@@ -5,7 +5,10 @@ as the bucket's hipGraph. The primary line is batch 1 with a 1,024-token context
 prefill; the same JSON line carries the batch-32 workload (contexts uniform in [128, 2048], shuffled
 paged KV, Gumbel-max at T = 1) under "bs32". Inputs are resident in HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-bs32] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-bs32] [--no-mixed] [--no-cpu]
+
+The line also carries the Qwen2.5-1.5B-shape mixed step (prefill chunks + decode rows, 544 packed
+tokens) under "mixed": the bucketed plan replayed as a hipGraph against the exact-size eager plan.
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, vendor figure
+PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix cores, vendor figure
 METRIC = "decode tokens/s/GPU at Qwen3-0.6B shape, bs 1 & 32; % of HBM roofline"
 
 
@@ -185,6 +189,85 @@ def run_bs32(shape, W, steps: int, warmup: int):
     return out
 
 
+def mixed_flops(shape, prefill_lens, decode_ctx, n_logits: int) -> float:
+    """Algorithmic FLOPs of one mixed step: linears over every packed token, the LM head over the
+    sampled rows, causal attention of each prefill chunk and one query row per decode request."""
+    H, I, d, nq, nkv = shape.hidden, shape.intermediate, shape.head_dim, shape.q_heads, shape.kv_heads
+    lin = shape.layers * ((nq + 2 * nkv) * d * H + H * nq * d + 2 * I * H + H * I)
+    T = sum(prefill_lens) + len(decode_ctx)
+    att = sum(n * (n + 1) // 2 for n in prefill_lens) + sum(c + 1 for c in decode_ctx)
+    return 2.0 * lin * T + 2.0 * shape.vocab * H * n_logits + 4.0 * d * nq * att * shape.layers
+
+
+def run_mixed(steps: int = 20, warmup: int = 2) -> dict:
+    """The Qwen2.5-1.5B-shape mixed step (prefill chunks 16/240/256 + 32 decode rows, 544 packed
+    tokens, 35 sampled rows), median step time over `steps` steps: the bucketed plan replayed as a
+    hipGraph (bucket 576) and the exact-size plan launched eagerly."""
+    import graph_replay_amd as g
+    torch = __import__("torch")
+    wl = synth.workload_q25_mixed()
+    shape = wl.shape
+    log("mixed weights")
+    W = synth.make_weights(shape, 0)
+    P = len(wl.prefill_lens)
+    need = [n + 1 for n in wl.prefill_lens] + [c + 1 for c in wl.decode_contexts]
+    nb = sum(-(-n // 16) for n in need) + 2
+    tables = synth.block_tables(need, nb, wl.input_seed, shuffled=True)
+    width = max(len(t) for t in tables)
+    bt = np.full((len(tables), width), -1, np.int32)
+    for j, t in enumerate(tables):
+        bt[j, :len(t)] = t
+    toks, pos, slots, qsl, lens, lidx = [], [], [], [0], [], []
+    for j, n in enumerate(wl.prefill_lens):
+        toks += list(synth.tokens(n, shape.vocab, wl.input_seed + 10 + j))
+        pos += list(range(n))
+        slots += [int(bt[j][p // 16] * 16 + p % 16) for p in range(n)]
+        qsl.append(qsl[-1] + n); lens.append(n); lidx.append(qsl[-1] - 1)
+    dtok = synth.tokens(len(wl.decode_contexts), shape.vocab, wl.input_seed + 99)
+    for i, c in enumerate(wl.decode_contexts):
+        j = P + i
+        toks.append(int(dtok[i])); pos.append(c); slots.append(int(bt[j][c // 16] * 16 + c % 16))
+        qsl.append(qsl[-1] + 1); lens.append(c + 1); lidx.append(qsl[-1] - 1)
+    T, R = qsl[-1], len(lens)
+    out = {"workload": wl.name, "tokens": T, "sampled_rows": len(lidx)}
+    for name, buckets in (("graph", [T + (-T) % 64]), ("eager", None)):
+        dec = g.Decoder(shape, W, num_blocks=nb, max_blocks_per_seq=width, max_position=max(need) + 16, max_batch=1,
+                        buckets=[1], max_tokens=T + (-T) % 64, max_reqs=R, max_logit_rows=R,
+                        mixed_buckets=buckets)
+        gen = torch.Generator(device=dec.device)
+        gen.manual_seed(wl.input_seed)
+        for l in range(shape.layers):                   # seeded N(0, 1) KV history, resident in HBM
+            dec.k_pool[l].normal_(generator=gen)
+            dec.v_pool[l].normal_(generator=gen)
+        args = dict(query_start_loc=qsl, seq_lens=lens, tokens=toks, positions=pos, slots=slots, block_table=bt,
+                    logits_indices=lidx, num_prefill_reqs=P)
+        for _ in range(warmup):
+            dec.mixed(**args)
+        torch.cuda.synchronize()
+        log("timing", steps, "mixed steps,", name)
+        times = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(dec.stream)
+            dec.mixed(**args)
+            e1.record(dec.stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        out[f"{name}_bucket"] = dec.last_mixed_bucket()
+        out[f"ms_per_step_{name}"] = round(float(np.median(times)), 4)
+        dec.close()
+        del dec
+        torch.cuda.empty_cache()
+    flops = mixed_flops(shape, wl.prefill_lens, wl.decode_contexts, len(lidx))
+    ms = out["ms_per_step_graph"]
+    out["value"] = round(T / (ms * 1e-3), 1)
+    out["unit"] = "tokens/s"
+    out["step_mfma"] = {"flops_per_step": flops, "achieved": round(flops / (ms * 1e-3) / 1e12, 1),
+                        "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
+    return out
+
+
 def cpu_baseline(shape, W, budget_s: float = 20.0, ctx_len: int = 1024) -> dict:
     """The oracle (fp32 NumPy, unfused, per request) timed on this host on a bounded sample: decode
     steps of one request over a 1,024-key injected history (same shape as the GPU workload)."""
@@ -223,8 +306,9 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-bs32", action="store_true")
-    ap.add_argument("--workload", choices=["both", "bs1", "bs32"], default="both",
-                    help="bs1: the primary line only; bs32: the batch-32 workload only (for profiling)")
+    ap.add_argument("--workload", choices=["both", "bs1", "bs32", "mixed"], default="both",
+                    help="bs1: the primary line only; bs32 / mixed: that workload only (for profiling)")
+    ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy a 1 GiB device buffer 4 times (calibrates the HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -257,8 +341,12 @@ def main():
                           "unit": "tokens/s", "ms_per_step": round(r32["ms_per_step"], 4),
                           "kernels_per_step": r32["kernels_per_step"], "roofline": r32["roofline"]}), flush=True)
         return
+    if args.workload == "mixed":
+        print(json.dumps({"metric": METRIC, **run_mixed()}), flush=True)
+        return
     r1 = run_bs1(shape, W, args.steps, warmup)
     r32 = None if (args.no_bs32 or args.workload == "bs1") else run_bs32(shape, W, args.steps, warmup)
+    rmix = None if (args.no_mixed or args.workload == "bs1") else run_mixed()
     cpu = None if args.no_cpu else cpu_baseline(shape, W)
     line = {
         "metric": METRIC, "value": round(r1["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -278,6 +366,8 @@ def main():
                         "step_hbm": {"bytes_per_step": r32["bytes_per_step"], "achieved": round(r32["step_hbm_GBps"], 1),
                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r32["step_hbm_frac"], 4)},
                         "roofline": r32["roofline"]}
+    if rmix is not None:
+        line["mixed"] = rmix
     print(json.dumps(line), flush=True)
 
 

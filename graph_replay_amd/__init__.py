@@ -115,7 +115,7 @@ class Decoder:
     def __init__(self, shape, weights: dict, *, num_blocks: int, max_blocks_per_seq: int, max_position: int,
                  max_batch: int = 1, buckets: Optional[Sequence[int]] = None, max_tokens: int = 0,
                  max_reqs: int = 0, max_logit_rows: int = 0, use_graphs: bool = True, history: bool = False,
-                 device: str = "cuda:0"):
+                 mixed_buckets: Optional[Sequence[int]] = None, device: str = "cuda:0"):
         import torch
         lib = _lib.load()
         self.torch = torch
@@ -190,6 +190,12 @@ class Decoder:
         for i, b in enumerate(buckets):
             cfg.buckets[i] = int(b)
         cfg.use_graphs = int(use_graphs)
+        mixed_buckets = list(mixed_buckets) if mixed_buckets else []
+        if len(mixed_buckets) > _lib.MAX_BUCKETS:
+            raise ValueError("too many mixed buckets")
+        cfg.num_mixed_buckets = len(mixed_buckets)
+        for i, b in enumerate(mixed_buckets):
+            cfg.mixed_buckets[i] = int(b)
         self.cfg = cfg
         self.buckets = buckets
         nbytes = step_workspace_bytes(cfg)
@@ -263,6 +269,9 @@ class Decoder:
 
     def kernels_per_decode(self, bucket: int) -> int:
         return int(_lib.load().step_kernels_per_decode(self.ctx, bucket))
+
+    def last_mixed_bucket(self) -> int:
+        return int(_lib.load().step_last_mixed_bucket(self.ctx))
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

@@ -21,7 +21,8 @@ class StepConfig(C.Structure):
         ("rms_eps", C.c_float), ("rope_theta", C.c_float)] + [
         (n, C.c_int32) for n in ("block_size", "num_blocks", "max_blocks_per_seq", "max_position", "max_batch",
                                  "max_tokens", "max_reqs", "max_logit_rows", "num_buckets")] + [
-        ("buckets", C.c_int32 * MAX_BUCKETS), ("use_graphs", C.c_int32)]
+        ("buckets", C.c_int32 * MAX_BUCKETS), ("use_graphs", C.c_int32),
+        ("num_mixed_buckets", C.c_int32), ("mixed_buckets", C.c_int32 * MAX_BUCKETS)]
 
 
 class StepWeights(C.Structure):
@@ -60,6 +61,7 @@ EXPORTS = {
     "step_kernel_kind_name": (C.c_char_p, [C.c_int32]),
     "step_last_bucket": (C.c_int, [P]),
     "step_kernels_per_decode": (C.c_int, [P, C.c_int32]),
+    "step_last_mixed_bucket": (C.c_int, [P]),
     "step_last_error": (C.c_char_p, [P]),
     "step_destroy": (None, [P]),
 }

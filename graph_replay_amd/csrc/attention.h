@@ -106,6 +106,8 @@ struct AttnRowsArgs {
   void* v_pool;
   const int* block_table;    // [reqs][bt_stride]
   int bt_stride;
+  const int* row_ids;        // grid row -> row of q / out / seq_lens / row_req (nullptr: identity);
+                             // a negative entry is an idle grid row. Partials are kept per grid row.
   const int* row_req;        // row -> block-table row (nullptr: identity)
   const int* seq_lens;       // [rows] keys visible to the row, its own token included
   int split_tokens;          // P: keys per split (multiple of 64)
@@ -196,11 +198,11 @@ __device__ inline void attn_prologue(const AttnRowsArgs& a, int row, int g, bool
 // Combine the four waves' (max, sum, unnormalised output) in wave order, then write the output
 // (single split) or this split's partial. Call after a block barrier that follows the LDS writes.
 template <class T, int D, int G>
-__device__ inline void attn_finish(const AttnRowsArgs& a, int row, int g, int sp, int nsplit, const float (*wm)[G],
-                                   const float (*wl)[G], const float (*wo)[G][D]) {
+__device__ inline void attn_finish(const AttnRowsArgs& a, int row, int prow, int g, int sp, int nsplit,
+                                   const float (*wm)[G], const float (*wl)[G], const float (*wo)[G][D]) {
   using S = typename T::S;
   S* out = static_cast<S*>(a.out) + static_cast<size_t>(row) * a.nq * D;
-  float* part = a.partials + (static_cast<size_t>(row) * a.nq + g * G) * a.max_splits * (D + 2);
+  float* part = a.partials + (static_cast<size_t>(prow) * a.nq + g * G) * a.max_splits * (D + 2);
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int j = i / D, dd = i % D;
     float M = -INFINITY;
@@ -243,7 +245,9 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wo[4][G][D];
   __shared__ float qs[G][D];
-  const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int prow = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int row = a.row_ids ? a.row_ids[prow] : prow;
+  if (row < 0) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int L = a.seq_lens[row];
   const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
     for (int j = 0; j < G; ++j) { wm[wid][j] = m[j]; wl[wid][j] = l[j]; }
   }
   __syncthreads();
-  attn_finish<T, D, G>(a, row, g, sp, nsplit, wm, wl, wo);
+  attn_finish<T, D, G>(a, row, prow, g, sp, nsplit, wm, wl, wo);
 }
 
 // Matrix-core version for 16-bit K/V (G <= 16 query heads per KV head). Per 16-key block a wave
@@ -406,7 +410,9 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
   __shared__ __align__(16) float qs[G][D];
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wo[4][G][D];
-  const int row = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int prow = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int row = a.row_ids ? a.row_ids[prow] : prow;
+  if (row < 0) return;
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int req = a.row_req ? a.row_req[row] : row;
@@ -574,22 +580,25 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
     }
   }
   __syncthreads();
-  attn_finish<T, D, G>(a, row, g, sp, nsplit, wm, wl, wo);
+  attn_finish<T, D, G>(a, row, prow, g, sp, nsplit, wm, wl, wo);
 }
 
-// Merge the split partials of rows with more than one split: grid (rows, nq), block D threads
+// Merge the split partials of rows with more than one split: grid (grid rows, nq), block D threads
 // (thread = output dim). Split maxima and sums go through LDS; the weighted sum runs in split
 // order, so the result does not depend on which split finished first.
 template <class T, int D>
-__global__ __launch_bounds__(128) void k_attn_combine(int nq, const int* __restrict__ seq_lens, int split_tokens,
+__global__ __launch_bounds__(128) void k_attn_combine(int nq, const int* __restrict__ row_ids,
+                                                      const int* __restrict__ seq_lens, int split_tokens,
                                                       int max_splits, const float* __restrict__ partials,
                                                       void* __restrict__ out) {
   extern __shared__ float sm_comb[];      // [2 * max_splits]
-  const int row = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int prow = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int row = row_ids ? row_ids[prow] : prow;
+  if (row < 0) return;
   const int L = seq_lens[row];
   const int ns = (L + split_tokens - 1) / split_tokens;
   if (L <= 0 || ns <= 1) return;
-  const float* part = partials + (static_cast<size_t>(row) * nq + h) * max_splits * (D + 2);
+  const float* part = partials + (static_cast<size_t>(prow) * nq + h) * max_splits * (D + 2);
   float* mx = sm_comb;
   float* sl = sm_comb + max_splits;
   for (int s = t; s < ns; s += blockDim.x) {

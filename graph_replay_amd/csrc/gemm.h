@@ -2,14 +2,15 @@
 //
 // The stacked matrices follow "Removing overhead: fusion, graphs and async scheduling", section
 // "Fewer, larger matmuls": one matmul over [W_Q | W_K | W_V] and one over [W_gate | W_up]. Three
-// kernels cover the row counts of a step:
+// kernel families cover the row counts of a step:
 //   k_gemv       VALU, <= 8 token rows: every weight element is read once with 16-byte loads and
 //                used for all rows; optional prologue computing x = RMSNorm(r + sum of deltas) * g
 //                (the fused residual-add + RMSNorm), optional SiLU(gate) * up epilogue.
 //   k_gemv_mfma  16 or 32 token rows (bf16/fp16): v_mfma_f32_16x16x32 with both operands loaded
 //                straight from memory in the MFMA lane layout; the four waves split K.
-//   k_gemm       >= 33 token rows (bf16/fp16): LDS-tiled MFMA GEMM, optional split-K into fp32
-//                partial outputs that the consumer sums in fixed order.
+//   k_gemm_tn    >= 33 token rows (bf16/fp16, K a multiple of 64): XCD-ordered LDS-tiled MFMA GEMM
+//   k_gemm       >= 33 token rows otherwise: LDS-tiled MFMA GEMM
+//   Both split K on request into fp32 partial outputs that the consumer sums in fixed order.
 #pragma once
 #include "common.h"
 
@@ -366,6 +367,199 @@ __device__ inline uint32_t pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
   } else {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, f16x2_t));
+  }
+}
+
+// MFMA GEMM for many token rows: out[m][n] = sum_k x[m][k] W[n][k] with both operands K-contiguous.
+// Block tile BN weight rows x BM tokens, BK-deep k-steps double-buffered in LDS (rows padded by 8
+// elements, so the 16 lanes of a fragment read hit distinct banks); NWN x NWM waves, each owning a
+// WN x WM sub-tile of 16x16 MFMA tiles. The next k-step is fetched into registers while the current
+// one is multiplied, then stored to the other LDS buffer: one barrier per k-step.
+// Block order is XCD-aware: block b runs on XCD b % 8 (round-robin dispatch), and the blocks of one
+// XCD take all m tiles of an n tile before the next, so a weight tile is read into one L2.
+// EPI_SILU: within each wave the first WN/2 rows are gate rows and the last WN/2 the matching up
+// rows, so SiLU(gate) * up is formed in registers. gridDim.z splits K (EPI_F32 partial outputs).
+template <class T, int BN, int BM, int BK, int NWN, int NWM>
+__global__ __launch_bounds__(64 * NWN * NWM) void k_gemm_tn(GemmArgs a, int epi, int n_tiles, int m_tiles) {
+  using S = typename T::S;
+  constexpr int NT = 64 * NWN * NWM;
+  constexpr int LDK = BK + 8;
+  constexpr int WN = BN / NWN, WM = BM / NWM;
+  constexpr int TN = WN / 16, TM = WM / 16;
+  constexpr int KS = BK / 32;
+  constexpr int VR = BK / 8;                         // 16-byte vectors per tile row per k-step
+  constexpr int WV = BN * VR / NT, XV = BM * VR / NT;
+  static_assert(WN % 32 == 0 && WM % 16 == 0 && BK % 32 == 0, "tile shape");
+  static_assert(WV * NT == BN * VR && XV * NT == BM * VR, "tile must split evenly over the threads");
+  __shared__ __align__(16) S sw[2][BN * LDK];
+  __shared__ __align__(16) S sx[2][BM * LDK];
+
+  const int b = blockIdx.x;
+  const int slot = b >> 3;
+  const int tn = (b & 7) + 8 * (slot / m_tiles), tm = slot % m_tiles;
+  if (tn >= n_tiles) return;                         // grid is rounded up to whole XCD rounds
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid % NWN, wm = wid / NWN;
+  const int K = a.K;
+  const bool silu_epi = (epi == EPI_SILU);
+  const int m0 = tm * BM;
+  const S* W = static_cast<const S*>(a.W);
+  const S* X = static_cast<const S*>(a.x);
+
+  auto wrow_of = [&](int R) -> int {                 // tile row -> weight row (or -1: none)
+    if (silu_epi) {
+      const int w = R / WN, r = R % WN;
+      const int j = tn * (BN / 2) + w * (WN / 2) + (r % (WN / 2));
+      if (j >= a.N) return -1;
+      return (r < WN / 2) ? j : a.N + j;
+    }
+    const int n = tn * BN + R;
+    return n < a.N ? n : -1;
+  };
+  const int ksteps = K / BK;
+  const int per = (ksteps + gridDim.z - 1) / gridDim.z;
+  const int ks0 = blockIdx.z * per, ks1 = min(ksteps, ks0 + per);
+
+  // per-thread source rows of the staged vectors (fixed over k-steps)
+  const S* wsrc[WV];
+  bool wok[WV];
+#pragma unroll
+  for (int i = 0; i < WV; ++i) {
+    const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
+    const int wr = wrow_of(R);
+    wok[i] = wr >= 0;
+    wsrc[i] = W + static_cast<size_t>(wr >= 0 ? wr : 0) * K + c;
+  }
+  const S* xsrc[XV];
+  bool xok[XV];
+#pragma unroll
+  for (int i = 0; i < XV; ++i) {
+    const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
+    const int m = m0 + R;
+    xok[i] = m < a.M;
+    xsrc[i] = X + static_cast<size_t>(m < a.M ? m : a.M - 1) * K + c;
+  }
+  uint4 wreg[WV], xreg[XV];
+  auto fetch = [&](int ks) {
+    const int k0 = ks * BK;
+#pragma unroll
+    for (int i = 0; i < WV; ++i) wreg[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0);
+#pragma unroll
+    for (int i = 0; i < XV; ++i) xreg[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+      const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
+      *reinterpret_cast<uint4*>(&sw[buf][R * LDK + c]) = wok[i] ? wreg[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
+      *reinterpret_cast<uint4*>(&sx[buf][R * LDK + c]) = xok[i] ? xreg[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (ks0 < ks1) {
+    fetch(ks0);
+    stash(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  const int frow = lane & 15, koff = 8 * (lane >> 4);
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const bool more = ks + 1 < ks1;
+    if (more) fetch(ks + 1);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      uint4 af[TN], bf[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(&sw[buf][(wn * WN + i * 16 + frow) * LDK + kk * 32 + koff]);
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        bf[j] = *reinterpret_cast<const uint4*>(&sx[buf][(wm * WM + j * 16 + frow) * LDK + kk * 32 + koff]);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bf[j], acc[i][j]);
+    }
+    if (more) {
+      stash(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // lane holds rows rbase .. rbase+3 of column `col` of every 16x16 tile
+  const int col = lane & 15, rbase = 4 * (lane >> 4);
+  if (silu_epi) {
+    S* out = static_cast<S*>(a.out);
+#pragma unroll
+    for (int i = 0; i < TN / 2; ++i) {
+      const int j0 = tn * (BN / 2) + wn * (WN / 2) + i * 16 + rbase;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = m0 + wm * WM + j * 16 + col;
+        if (m >= a.M) continue;
+        S v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = T::from_f(silu(acc[i][j][e]) * acc[i + TN / 2][j][e]);
+        S* dst = out + static_cast<size_t>(m) * a.ldo + j0;
+        if (j0 + 3 < a.N) {
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < a.N) dst[e] = v[e];
+        }
+      }
+    }
+  } else {
+    const S* bias = (blockIdx.z == 0) ? static_cast<const S*>(a.bias) : nullptr;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int n0 = tn * BN + wn * WN + i * 16 + rbase;
+      float bb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bb[e] = (bias && n0 + e < a.N) ? T::to_f(bias[n0 + e]) : 0.f;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = m0 + wm * WM + j * 16 + col;
+        if (m >= a.M) continue;
+        if (epi == EPI_STORE_T) {
+          S v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = T::from_f(acc[i][j][e] + bb[e]);
+          S* dst = static_cast<S*>(a.out) + static_cast<size_t>(m) * a.ldo + n0;
+          if (n0 + 3 < a.N) {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(v);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n0 + e < a.N) dst[e] = v[e];
+          }
+        } else {
+          float* dst = static_cast<float*>(a.out) + blockIdx.z * a.out_split_stride + static_cast<size_t>(m) * a.ldo + n0;
+          const float4 v = make_float4(acc[i][j][0] + bb[0], acc[i][j][1] + bb[1], acc[i][j][2] + bb[2],
+                                       acc[i][j][3] + bb[3]);
+          if (n0 + 3 < a.N) {
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n0 + e < a.N) dst[e] = vv[e];
+          }
+        }
+      }
+    }
   }
 }
 

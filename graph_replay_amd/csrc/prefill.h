@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
   if (h >= a.nq) return;       // waves never synchronise with each other
   const int tile = blockIdx.x;
   const int req = a.tile_req[tile], q0 = a.tile_q0[tile];
+  if (req < 0) return;         // padding tile (the tile list is padded to a fixed length)
   const int cnt = min(16, a.qsl[req + 1] - q0);
   const int g = h / (a.nq / a.nkv);
   const int col = lane & 15, grp = lane >> 4;

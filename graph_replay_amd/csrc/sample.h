@@ -44,6 +44,7 @@ struct SampleArgs {
   int* part_idx;
   unsigned* row_cnt;                  // [rows], zero between launches (reset by the row's last block)
   unsigned* done_cnt;                 // [1], zero between launches (reset by the last row)
+  const int* n_rows;                  // device row count (nullptr: gridDim.x); rows past it are idle
   int* tokens_out;                    // [rows]
   // decode advance (advance != 0)
   int advance;
@@ -86,6 +87,14 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   __shared__ int si[4];
   __shared__ int last_flag;
   const int row = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+  if (a.n_rows && row >= *a.n_rows) {
+    // idle row: still counted in by one block, so the step counter and its reset stay exact
+    if (ch == 0 && threadIdx.x == 0 && a.rng && arrive_last(a.done_cnt, gridDim.x)) {
+      uint64_t* r = const_cast<uint64_t*>(a.rng);
+      r[1] = r[1] + 1;
+    }
+    return;
+  }
   const float T = a.temperature ? a.temperature[row] : 0.f;
   const uint64_t seed = a.rng ? a.rng[0] : a.seed;
   const uint64_t step = a.rng ? a.rng[1] : a.step;

@@ -62,6 +62,10 @@ struct step_ctx {
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
   std::vector<int> kernels_per_bucket;
+  std::vector<hipGraph_t> mgraphs;              // per mixed token-count bucket
+  std::vector<hipGraphExec_t> mexecs;
+  std::vector<int> kernels_per_mbucket;
+  int last_mixed_bucket = 0;                    // bucket of the last mixed step (0: exact-size plan)
   int last_bucket = 0;
   int launches = 0;                   // kernels enqueued by the current plan run
   uint64_t step_count = 0;            // Philox step counter the next host-fed step starts from
@@ -180,10 +184,10 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.dmeta_bytes = 16 + sizeof(int) * (5 * static_cast<size_t>(MB) + static_cast<size_t>(MB) * W);
   L.dmeta = take(L.dmeta_bytes);
   // mixed: rng[2] | tok | pos | slot | row_req | row_len [TM] | qsl [RM+1] | req_len [RM] | bt [RM*W]
-  //        | logit_idx [LM] | temp [LM] | tile_req, tile_q0 [TM/16 + RM]
+  //        | logit_idx [LM] | temp [LM] | tile_req, tile_q0 [TM/16 + RM + 1] | dec_rows [RM] | n_logits
   const size_t tiles = TM / 16 + RM + 1;
   L.mmeta_bytes = 16 + sizeof(int) * (5 * static_cast<size_t>(TM) + (RM + 1) + RM + static_cast<size_t>(RM) * W +
-                                      2 * static_cast<size_t>(LM) + 2 * tiles);
+                                      2 * static_cast<size_t>(LM) + 2 * tiles + RM + 1);
   L.mmeta = take(L.mmeta_bytes);
   L.rope_cos = take(sizeof(float) * static_cast<size_t>(c.max_position) * (d / 2));
   L.rope_sin = take(sizeof(float) * static_cast<size_t>(c.max_position) * (d / 2));
@@ -249,6 +253,15 @@ int validate_config(step_ctx* ctx, const step_config* c) {
   if (c->buckets[c->num_buckets - 1] != c->max_batch) return fail(ctx, STEP_EINVAL, "last bucket must equal max_batch");
   if (c->max_tokens > 0 && (c->max_reqs <= 0 || c->max_logit_rows <= 0))
     return fail(ctx, STEP_EINVAL, "mixed steps need max_reqs and max_logit_rows");
+  if (c->num_mixed_buckets < 0 || c->num_mixed_buckets > STEP_MAX_BUCKETS)
+    return fail(ctx, STEP_EINVAL, "num_mixed_buckets out of range");
+  if (c->num_mixed_buckets > 0 && c->max_tokens <= 0)
+    return fail(ctx, STEP_EINVAL, "mixed buckets need mixed-step buffers (max_tokens > 0)");
+  for (int i = 0; i < c->num_mixed_buckets; ++i) {
+    if (c->mixed_buckets[i] <= 0 || c->mixed_buckets[i] > c->max_tokens ||
+        (i && c->mixed_buckets[i] <= c->mixed_buckets[i - 1]))
+      return fail(ctx, STEP_EINVAL, "mixed buckets must be ascending and in [1, max_tokens]");
+  }
   return STEP_OK;
 }
 
@@ -362,6 +375,25 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       else if (rt == 2) launch((k_gemv_mfma<T, 2, 4, 2>), grid, dim3(256), 0, s, a, l.epi);
       else launch((k_gemv_mfma<T, 2, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
       e = hipGetLastError();
+    } else if (l.K % 64 == 0 && l.ldo % 4 == 0) {
+      // tiled GEMM: gate|up on 128x128 tiles with 4 waves along the weight rows; other projections
+      // on 128 x (64 | 128) tiles of 2 x 2 waves with K split until ~200 blocks are in flight
+      const bool silu_epi = l.epi == EPI_SILU;
+      const bool wide_m = silu_epi || l.K >= 4096;
+      const int BN = 128, BM = wide_m ? 128 : 64;
+      const int n_tiles = silu_epi ? (l.N + BN / 2 - 1) / (BN / 2) : (l.N + BN - 1) / BN;
+      const int m_tiles = (l.M + BM - 1) / BM;
+      int ks = 1;
+      if (l.ksplit_ok && l.epi == EPI_F32) {
+        while (ks < kMaxKsplit && n_tiles * m_tiles * ks < 200 && (l.K / 64) / (ks * 2) >= 8) ks *= 2;
+      }
+      a.ksplit = ks;
+      if (l.ksplit_used) *l.ksplit_used = ks;
+      dim3 grid(8 * ((n_tiles + 7) / 8) * m_tiles, 1, ks);
+      if (silu_epi) launch((k_gemm_tn<T, 128, 128, 64, 4, 1>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
+      else if (wide_m) launch((k_gemm_tn<T, 128, 128, 64, 2, 2>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
+      else launch((k_gemm_tn<T, 128, 64, 64, 2, 2>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
+      e = hipGetLastError();
     } else {
       const bool big = l.M > 64;
       const int BN = big ? 128 : 64, BM = big ? 128 : 64;
@@ -422,7 +454,7 @@ hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream
 template <class T, int D>
 hipError_t launch_combine(step_ctx* ctx, int rows, const AttnRowsArgs& a) {
   launch((k_attn_combine<T, D>), dim3(rows, a.nq), dim3(D), sizeof(float) * 2 * a.max_splits, ctx->stream,
-                     a.nq, a.seq_lens, a.split_tokens, a.max_splits, a.partials, a.out);
+                     a.nq, a.row_ids, a.seq_lens, a.split_tokens, a.max_splits, a.partials, a.out);
   return hipGetLastError();
 }
 
@@ -431,7 +463,8 @@ hipError_t launch_combine(step_ctx* ctx, int rows, const AttnRowsArgs& a) {
 // the n_qkv fp32 partial outputs of the QKV projection.
 template <class T>
 int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv, const int* pos, const int* slot,
-                  const int* bt, int bt_stride, const int* row_req, const int* seq_lens, int max_len, void* out) {
+                  const int* bt, int bt_stride, const int* row_req, const int* seq_lens, int max_len, void* out,
+                  const int* row_ids = nullptr) {
   const step_config& c = ctx->cfg;
   const Layout& Ly = ctx->lay;
   AttnRowsArgs a{};
@@ -446,7 +479,7 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.k_norm = c.qk_norm ? ctx->k_norm[layer] : nullptr;
   a.eps = c.rms_eps;
   a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
-  a.block_table = bt; a.bt_stride = bt_stride; a.row_req = row_req; a.seq_lens = seq_lens;
+  a.block_table = bt; a.bt_stride = bt_stride; a.row_ids = row_ids; a.row_req = row_req; a.seq_lens = seq_lens;
   a.split_tokens = split_tokens_for(rows, max_len);
   a.max_splits = std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
   a.num_blocks = c.num_blocks;
@@ -485,7 +518,8 @@ int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_st
 
 int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, const float* temp, const float* uniforms,
                const uint64_t* rng, uint64_t seed, uint64_t stepc, int* tokens_out, int advance, int* ids, int* pos,
-               int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld) {
+               int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld,
+               const int* n_rows = nullptr) {
   SampleArgs a{};
   a.logits = logits; a.ld = ld; a.vocab = vocab;
   int chunk = 1024;
@@ -499,6 +533,7 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.tokens_out = tokens_out;
   a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
+  a.n_rows = n_rows;
   const int nch = (vocab + chunk - 1) / chunk;
   pre_launch(ctx, KK_SAMPLE);
   launch(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
@@ -625,12 +660,14 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
 namespace {
 
 // Mixed-step metadata: rng[2] | tok | pos | slot | row_req | row_len [TM] | qsl [RM+1] | req_len [RM]
-// | bt [RM*W] | logit_idx [LM] | temp [LM] | tile_req [tiles] | tile_q0 [tiles]
+// | bt [RM*W] | logit_idx [LM] | temp [LM] | tile_req [tiles] | tile_q0 [tiles] | dec_rows [RM] | n_logits
 struct MixedMeta {
   uint64_t* rng;
   int *tok, *pos, *slot, *row_req, *row_len, *qsl, *req_len, *bt, *lidx;
   float* temp;
   int *tile_req, *tile_q0;
+  int* dec_rows;   // packed rows of the decode requests, -1 past them (bucketed plan)
+  int* n_logits;   // sampled rows (bucketed plan)
 };
 MixedMeta mixed_meta(char* base, const Layout& L, int W) {
   MixedMeta m;
@@ -649,6 +686,8 @@ MixedMeta mixed_meta(char* base, const Layout& L, int W) {
   m.temp = reinterpret_cast<float*>(m.lidx + LM);
   m.tile_req = reinterpret_cast<int*>(m.temp + LM);
   m.tile_q0 = m.tile_req + tiles;
+  m.dec_rows = m.tile_q0 + tiles;
+  m.n_logits = m.dec_rows + RM;
   return m;
 }
 
@@ -679,7 +718,22 @@ int run_decode_any(step_ctx* ctx, int B) {
 
 struct MixedPlan {
   int T, n_pre_tok, n_pre_req, n_dec, n_logits, max_len, mode, n_tiles;
+  bool fixed = false;   // bucketed plan: every launch shape depends on T (the bucket) only
 };
+
+// The launch plan of a mixed step padded to token-count bucket TB: TB token rows, a tile list of
+// TB/16 + max_reqs entries, decode-row attention over min(max_reqs, TM) listed rows with splits
+// sized for max_position, and max_logit_rows logits rows; the real counts live in the metadata.
+MixedPlan fixed_plan(const step_ctx* ctx, int TB) {
+  MixedPlan p{};
+  p.T = TB;
+  p.n_logits = ctx->lay.LM;
+  p.max_len = ctx->cfg.max_position;
+  p.mode = 0;
+  p.n_tiles = TB / 16 + ctx->lay.RM;
+  p.fixed = true;
+  return p;
+}
 
 template <class T>
 int run_attn_prefill(step_ctx* ctx, int layer, const MixedPlan& p, const MixedMeta& m, const float* q, void* out) {
@@ -711,6 +765,16 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
   void* attn_o = ctx->ws + L.attn_o;
   const size_t row_elems = static_cast<size_t>(c.q_heads) * c.head_dim;
   auto attn = [&](int l, int) -> int {
+    if (p.fixed) {
+      if constexpr (std::is_same<T, F32>::value) {
+        return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
+      } else {
+        // listed tiles on the packed kernel, listed decode rows on the row kernel (disjoint outputs)
+        TRY(run_attn_prefill<T>(ctx, l, p, m, q, attn_o));
+        return run_attn_rows<T>(ctx, l, std::min(L.RM, L.TM), q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len,
+                                p.max_len, attn_o, m.dec_rows);
+      }
+    }
     if (p.mode == 1 || p.n_pre_tok == 0 || std::is_same<T, F32>::value) {
       // one query row per token: prefill rows see keys [0, pos], decode rows their request's keys
       return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
@@ -728,7 +792,23 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
   };
   TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, false, attn));
   return run_sample(ctx, ctx->logits, p.n_logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
-                    nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0);
+                    nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0, p.fixed ? m.n_logits : nullptr);
+}
+
+// Metadata of a mixed step padded to TB tokens with no real rows (capture and warm-up state).
+void fill_mixed_padding(const step_ctx* ctx, char* base, int TB) {
+  const Layout& L = ctx->lay;
+  const int W = ctx->cfg.max_blocks_per_seq;
+  MixedMeta m = mixed_meta(base, L, W);
+  m.rng[0] = 0;
+  m.rng[1] = 0;
+  for (int i = 0; i < TB; ++i) { m.tok[i] = 0; m.pos[i] = 0; m.slot[i] = -1; m.row_req[i] = 0; m.row_len[i] = 0; }
+  for (int j = 0; j <= L.RM; ++j) m.qsl[j] = 0;
+  for (int j = 0; j < L.RM; ++j) { m.req_len[j] = 0; m.dec_rows[j] = -1; }
+  std::memset(m.bt, 0, sizeof(int) * static_cast<size_t>(L.RM) * W);
+  for (int i = 0; i < L.LM; ++i) { m.lidx[i] = 0; m.temp[i] = 0.f; }
+  for (int t = 0; t < TB / 16 + L.RM; ++t) { m.tile_req[t] = -1; m.tile_q0[t] = 0; }
+  *m.n_logits = 0;
 }
 
 int run_mixed_any(step_ctx* ctx, const MixedPlan& p) {
@@ -917,6 +997,50 @@ extern "C" int step_init(const step_config* cfg, const step_weights* w, const st
     ctx->graphs[bi] = g;
     ctx->execs[bi] = x;
   }
+  // mixed-step buckets: all-padding metadata, two warm-ups, then capture (largest first)
+  ctx->mgraphs.assign(c.num_mixed_buckets, nullptr);
+  ctx->mexecs.assign(c.num_mixed_buckets, nullptr);
+  ctx->kernels_per_mbucket.assign(c.num_mixed_buckets, 0);
+  for (int bi = c.num_mixed_buckets - 1; bi >= 0; --bi) {
+    const int TB = c.mixed_buckets[bi];
+    fill_mixed_padding(ctx, ctx->h_stage[0], TB);
+    if ((e = hipMemcpyAsync(ctx->ws + ctx->lay.mmeta, ctx->h_stage[0], ctx->lay.mmeta_bytes, hipMemcpyHostToDevice, s)) !=
+        hipSuccess) {
+      ctx->stream = user;
+      return hip_fail(e, "hipMemcpyAsync(mixed meta)");
+    }
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) { ctx->stream = user; return hip_fail(e, "hipStreamSynchronize"); }
+    const MixedPlan mp = fixed_plan(ctx, TB);
+    for (int wup = 0; wup < 2; ++wup) {
+      ctx->launches = 0;
+      rc = run_mixed_any(ctx, mp);
+      if (rc != STEP_OK) { ctx->stream = user; return bail(rc); }
+    }
+    ctx->kernels_per_mbucket[bi] = ctx->launches;
+    if (!c.use_graphs) continue;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) { ctx->stream = user; return hip_fail(e, "hipStreamSynchronize"); }
+    if ((e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+      ctx->stream = user;
+      return bail(fail(ctx, STEP_ECAPTURE, "hipStreamBeginCapture: %s", hipGetErrorString(e)));
+    }
+    ctx->launches = 0;
+    rc = run_mixed_any(ctx, mp);
+    hipGraph_t g = nullptr;
+    hipError_t ee = hipStreamEndCapture(s, &g);
+    if (rc != STEP_OK || ee != hipSuccess || !g) {
+      ctx->stream = user;
+      if (g) (void)hipGraphDestroy(g);
+      return bail(rc != STEP_OK ? rc : fail(ctx, STEP_ECAPTURE, "hipStreamEndCapture: %s", hipGetErrorString(ee)));
+    }
+    hipGraphExec_t x = nullptr;
+    if ((e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0)) != hipSuccess) {
+      ctx->stream = user;
+      (void)hipGraphDestroy(g);
+      return bail(fail(ctx, STEP_ECAPTURE, "hipGraphInstantiate: %s", hipGetErrorString(e)));
+    }
+    ctx->mgraphs[bi] = g;
+    ctx->mexecs[bi] = x;
+  }
   ctx->stream = user;
   // warm-ups moved the Philox step counter: put the padding state back
   fill_decode_padding(c, ctx->h_stage[0]);
@@ -1046,10 +1170,16 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
       if (hp->h_positions[i] != hp->h_seq_lens[j] - n + (i - qsl[j]))
         return fail(ctx, STEP_EINVAL, "request %d: chunk positions must be seq_len - %d .. seq_len - 1", j, n);
   }
+  // bucketed plan: the smallest mixed bucket that holds the step (packed prefill attention only)
+  int mbi = -1;
+  if (hp->prefill_attention == 0)
+    for (int i = 0; i < c.num_mixed_buckets; ++i)
+      if (c.mixed_buckets[i] >= T) { mbi = i; break; }
   int slot_i;
   char* st = stage_slot(ctx, &slot_i);
   if (!st) return fail(ctx, STEP_EHIP, "waiting for the staging buffer failed");
   MixedMeta m = mixed_meta(st, ctx->lay, W);
+  if (mbi >= 0) fill_mixed_padding(ctx, st, c.mixed_buckets[mbi]);
   m.rng[0] = hp->seed;
   m.rng[1] = ctx->step_count;
   for (int j = 0; j < R; ++j) {
@@ -1076,15 +1206,32 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
     m.lidx[i] = hp->h_logits_indices[i];
     m.temp[i] = hp->h_temperature ? hp->h_temperature[i] : 0.f;
   }
+  for (int j = Rp; j < R; ++j) m.dec_rows[j - Rp] = qsl[j];
+  *m.n_logits = NL;
   HIPCHK(ctx, hipMemcpyAsync(ctx->ws + ctx->lay.mmeta, st, ctx->lay.mmeta_bytes, hipMemcpyHostToDevice, ctx->stream));
   HIPCHK(ctx, hipEventRecord(ctx->stage_ev[slot_i], ctx->stream));
-  MixedPlan p{T, qsl[Rp], Rp, Rd, NL, max_len, hp->prefill_attention, n_tiles};
   ctx->launches = 0;
-  int rc = run_mixed_any(ctx, p);
+  int rc;
+  if (mbi >= 0) {
+    ctx->last_mixed_bucket = c.mixed_buckets[mbi];
+    if (ctx->mexecs[mbi]) {
+      HIPCHK(ctx, hipGraphLaunch(ctx->mexecs[mbi], ctx->stream));
+      ctx->launches = ctx->kernels_per_mbucket[mbi];
+      rc = STEP_OK;
+    } else {
+      rc = run_mixed_any(ctx, fixed_plan(ctx, c.mixed_buckets[mbi]));
+    }
+  } else {
+    ctx->last_mixed_bucket = 0;
+    MixedPlan p{T, qsl[Rp], Rp, Rd, NL, max_len, hp->prefill_attention, n_tiles};
+    rc = run_mixed_any(ctx, p);
+  }
   if (rc != STEP_OK) return rc;
   ctx->step_count++;
   return STEP_OK;
 }
+
+extern "C" int step_last_mixed_bucket(const step_ctx* ctx) { return ctx ? ctx->last_mixed_bucket : STEP_ESTATE; }
 
 extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, int32_t ld, int32_t vocab,
                            const float* h_temperature, const float* d_uniforms, uint64_t seed, uint64_t counter,
@@ -1163,6 +1310,10 @@ extern "C" void step_destroy(step_ctx* ctx) {
   for (auto& x : ctx->execs)
     if (x) (void)hipGraphExecDestroy(x);
   for (auto& g : ctx->graphs)
+    if (g) (void)hipGraphDestroy(g);
+  for (auto& x : ctx->mexecs)
+    if (x) (void)hipGraphExecDestroy(x);
+  for (auto& g : ctx->mgraphs)
     if (g) (void)hipGraphDestroy(g);
   for (int i = 0; i < 2; ++i) {
     if (ctx->stage_ev[i]) (void)hipEventDestroy(ctx->stage_ev[i]);

@@ -74,6 +74,17 @@ typedef struct {
   int32_t num_buckets;           /* ascending decode batch sizes; the last must equal max_batch */
   int32_t buckets[STEP_MAX_BUCKETS];
   int32_t use_graphs;            /* 1: capture one hipGraph per bucket at init; 0: launch eagerly */
+  /* Token-count buckets of mixed steps (ascending, each in [1, max_tokens]). With at least one, a
+   * mixed step whose packed token count fits a bucket (and prefill_attention == 0) is padded to the
+   * smallest such bucket and runs a launch plan that depends on the bucket only: padding tokens
+   * (token 0, position 0, slot -1, no keys), a prefill tile list padded to bucket/16 + max_reqs,
+   * decode-row attention over a device row list of max_reqs entries with splits sized for
+   * max_position, and max_logit_rows logits rows of which the first num_logits are sampled. That
+   * plan is captured as one hipGraph per bucket at init when use_graphs is 1 and launched eagerly
+   * otherwise, with the same results. Larger steps, and steps with prefill_attention == 1, run the
+   * exact-size eager plan. 0 buckets: every mixed step runs the exact-size eager plan. */
+  int32_t num_mixed_buckets;
+  int32_t mixed_buckets[STEP_MAX_BUCKETS];
 } step_config;
 
 typedef struct {
@@ -170,6 +181,9 @@ const char *step_kernel_kind_name(int32_t kind);
 /* Rows of the bucket the last decode step ran at, and kernels launched per decode step. */
 int step_last_bucket(const step_ctx *ctx);
 int step_kernels_per_decode(const step_ctx *ctx, int32_t bucket);
+/* Token-count bucket the last mixed step was padded to (see step_config.mixed_buckets), or 0 when
+ * it ran the exact-size eager plan. */
+int step_last_mixed_bucket(const step_ctx *ctx);
 
 const char *step_last_error(const step_ctx *ctx);
 void step_destroy(step_ctx *ctx);
