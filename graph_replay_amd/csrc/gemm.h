@@ -8,7 +8,8 @@
 //                (the fused residual-add + RMSNorm), optional SiLU(gate) * up epilogue.
 //   k_gemv_mfma  16 or 32 token rows (bf16/fp16): v_mfma_f32_16x16x32 with both operands loaded
 //                straight from memory in the MFMA lane layout; the four waves split K.
-//   k_gemm_tn    >= 33 token rows (bf16/fp16, K a multiple of 64): XCD-ordered LDS-tiled MFMA GEMM
+//   k_gemm_ring  >= 33 token rows (bf16/fp16, K a multiple of 64): MFMA GEMM over an LDS ring filled
+//                by direct-to-LDS loads, XCD-ordered blocks
 //   k_gemm       >= 33 token rows otherwise: LDS-tiled MFMA GEMM
 //   Both split K on request into fp32 partial outputs that the consumer sums in fixed order.
 #pragma once
@@ -370,35 +371,57 @@ __device__ inline uint32_t pack2(float x, float y) {
   }
 }
 
-// MFMA GEMM for many token rows: out[m][n] = sum_k x[m][k] W[n][k] with both operands K-contiguous.
-// Block tile BN weight rows x BM tokens, BK-deep k-steps double-buffered in LDS (rows padded by 8
-// elements, so the 16 lanes of a fragment read hit distinct banks); NWN x NWM waves, each owning a
-// WN x WM sub-tile of 16x16 MFMA tiles. The next k-step is fetched into registers while the current
-// one is multiplied, then stored to the other LDS buffer: one barrier per k-step.
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left at "no wait"), gfx9 encoding
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l writes the 16 bytes at
+// `g` to LDS address lds + 16 l. It is issued as inline assembly so that the compiler, which cannot
+// tell ring slots apart, does not put a wait for every outstanding LDS load in front of each LDS
+// read; the caller waits with wait_vmcnt and a barrier before reading the slot. (The compiler does
+// not count these loads, and no other vector-memory load is in flight around them.)
+__device__ inline void lds_load16(const void* g, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(g) : "memory");
+}
+
+// MFMA GEMM for many token rows: out[m][n] = sum_k x[m][k] W[n][k], both operands K-contiguous.
+// Block tile BN weight rows x BM tokens, NWN x NWM waves each owning a WN x WM sub-tile of 16x16
+// MFMA tiles (v_mfma_f32_16x16x32). K goes in steps of BK = 64 (a tile row is 128 bytes = 8 vectors)
+// through a ring of NS LDS stages filled by direct-to-LDS loads, so NS - 1 steps are in flight
+// without staging registers; with NS = 2 two blocks fit per CU. The 16-byte vector c of tile row r
+// sits in slot c ^ ((r >> 1) & 7) of the row (each load instruction covers 8 rows and takes its
+// lanes' sources in that order): the 16 lanes that read one MFMA fragment column then hit 16
+// distinct bank groups. One wait + barrier per k-step: after it, step s is in LDS for every wave
+// and nobody reads step s - 1, whose slot takes step s + NS - 1.
 // Block order is XCD-aware: block b runs on XCD b % 8 (round-robin dispatch), and the blocks of one
 // XCD take all m tiles of an n tile before the next, so a weight tile is read into one L2.
 // EPI_SILU: within each wave the first WN/2 rows are gate rows and the last WN/2 the matching up
 // rows, so SiLU(gate) * up is formed in registers. gridDim.z splits K (EPI_F32 partial outputs).
-template <class T, int BN, int BM, int BK, int NWN, int NWM>
-__global__ __launch_bounds__(64 * NWN * NWM) void k_gemm_tn(GemmArgs a, int epi, int n_tiles, int m_tiles) {
+template <class T, int BN, int BM, int NWN, int NWM, int NS>
+__global__ __launch_bounds__(64 * NWN * NWM) void k_gemm_ring(GemmArgs a, int epi, int n_tiles, int m_tiles) {
   using S = typename T::S;
-  constexpr int NT = 64 * NWN * NWM;
-  constexpr int LDK = BK + 8;
+  constexpr int BK = 64, NW = NWN * NWM;
   constexpr int WN = BN / NWN, WM = BM / NWM;
   constexpr int TN = WN / 16, TM = WM / 16;
-  constexpr int KS = BK / 32;
-  constexpr int VR = BK / 8;                         // 16-byte vectors per tile row per k-step
-  constexpr int WV = BN * VR / NT, XV = BM * VR / NT;
-  static_assert(WN % 32 == 0 && WM % 16 == 0 && BK % 32 == 0, "tile shape");
-  static_assert(WV * NT == BN * VR && XV * NT == BM * VR, "tile must split evenly over the threads");
-  __shared__ __align__(16) S sw[2][BN * LDK];
-  __shared__ __align__(16) S sx[2][BM * LDK];
+  constexpr int WI = BN / 8 / NW, XI = BM / 8 / NW;   // load instructions per wave per k-step
+  constexpr int LPS = WI + XI;
+  constexpr int STAGE = (BN + BM) * 128;                // bytes per stage
+  static_assert(WN % 32 == 0 && WM % 16 == 0, "tile shape");
+  static_assert(WI * NW * 8 == BN && XI * NW * 8 == BM, "rows must split evenly over the waves");
+  static_assert(LPS * (NS - 2) < 64 && NS >= 2, "vmcnt range");
+  __shared__ __align__(16) unsigned char ring[NS * STAGE];
 
   const int b = blockIdx.x;
   const int slot = b >> 3;
   const int tn = (b & 7) + 8 * (slot / m_tiles), tm = slot % m_tiles;
-  if (tn >= n_tiles) return;                         // grid is rounded up to whole XCD rounds
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (tn >= n_tiles) return;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wid % NWN, wm = wid / NWN;
   const int K = a.K;
   const bool silu_epi = (epi == EPI_SILU);
@@ -406,58 +429,42 @@ __global__ __launch_bounds__(64 * NWN * NWM) void k_gemm_tn(GemmArgs a, int epi,
   const S* W = static_cast<const S*>(a.W);
   const S* X = static_cast<const S*>(a.x);
 
-  auto wrow_of = [&](int R) -> int {                 // tile row -> weight row (or -1: none)
+  auto wrow_of = [&](int R) -> int {                    // tile row -> weight row (clamped)
     if (silu_epi) {
       const int w = R / WN, r = R % WN;
-      const int j = tn * (BN / 2) + w * (WN / 2) + (r % (WN / 2));
-      if (j >= a.N) return -1;
+      const int j = min(tn * (BN / 2) + w * (WN / 2) + (r % (WN / 2)), a.N - 1);
       return (r < WN / 2) ? j : a.N + j;
     }
-    const int n = tn * BN + R;
-    return n < a.N ? n : -1;
+    return min(tn * BN + R, a.N - 1);
   };
   const int ksteps = K / BK;
   const int per = (ksteps + gridDim.z - 1) / gridDim.z;
   const int ks0 = blockIdx.z * per, ks1 = min(ksteps, ks0 + per);
+  const int n = max(0, ks1 - ks0);
 
-  // per-thread source rows of the staged vectors (fixed over k-steps)
-  const S* wsrc[WV];
-  bool wok[WV];
+  // this lane's source for each of its load instructions (row r = 8 q + lane / 8, slot lane % 8);
+  // rows past N or M read a clamped valid row, and their outputs are never stored
+  const S* wsrc[WI];
+  const S* xsrc[XI];
 #pragma unroll
-  for (int i = 0; i < WV; ++i) {
-    const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
-    const int wr = wrow_of(R);
-    wok[i] = wr >= 0;
-    wsrc[i] = W + static_cast<size_t>(wr >= 0 ? wr : 0) * K + c;
+  for (int i = 0; i < WI; ++i) {
+    const int q = wid + NW * i, r = 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    wsrc[i] = W + static_cast<size_t>(wrow_of(r)) * K + c * 8;
   }
-  const S* xsrc[XV];
-  bool xok[XV];
 #pragma unroll
-  for (int i = 0; i < XV; ++i) {
-    const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
-    const int m = m0 + R;
-    xok[i] = m < a.M;
-    xsrc[i] = X + static_cast<size_t>(m < a.M ? m : a.M - 1) * K + c;
+  for (int i = 0; i < XI; ++i) {
+    const int q = wid + NW * i, r = 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    xsrc[i] = X + static_cast<size_t>(min(m0 + r, a.M - 1)) * K + c * 8;
   }
-  uint4 wreg[WV], xreg[XV];
-  auto fetch = [&](int ks) {
-    const int k0 = ks * BK;
+  auto issue = [&](int s) {                             // k-step ks0 + s into ring slot s % NS
+    unsigned char* st = ring + (s % NS) * STAGE;
+    const int k0 = (ks0 + s) * BK;
 #pragma unroll
-    for (int i = 0; i < WV; ++i) wreg[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0);
+    for (int i = 0; i < WI; ++i) lds_load16(wsrc[i] + k0, st + (wid + NW * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < XV; ++i) xreg[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < WV; ++i) {
-      const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
-      *reinterpret_cast<uint4*>(&sw[buf][R * LDK + c]) = wok[i] ? wreg[i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      const int idx = threadIdx.x + NT * i, R = idx / VR, c = (idx % VR) * 8;
-      *reinterpret_cast<uint4*>(&sx[buf][R * LDK + c]) = xok[i] ? xreg[i] : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < XI; ++i) lds_load16(xsrc[i] + k0, st + BN * 128 + (wid + NW * i) * 1024);
   };
 
   f32x4_t acc[TN][TM];
@@ -466,38 +473,39 @@ __global__ __launch_bounds__(64 * NWN * NWM) void k_gemm_tn(GemmArgs a, int epi,
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (ks0 < ks1) {
-    fetch(ks0);
-    stash(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  const int frow = lane & 15, koff = 8 * (lane >> 4);
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const bool more = ks + 1 < ks1;
-    if (more) fetch(ks + 1);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < n) issue(s);
+  const int frow = lane & 15, kq = lane >> 4;
+  for (int s = 0; s < n; ++s) {
+    // this wave's loads of step s are done once at most NS - 2 later steps are outstanding
+    if (s + NS - 2 < n) wait_vmcnt<LPS * (NS - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (s + NS - 1 < n) issue(s + NS - 1);
+    const unsigned char* st = ring + (s % NS) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + kq;                        // k vector of this lane's fragment slots
       uint4 af[TN], bf[TM];
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(&sw[buf][(wn * WN + i * 16 + frow) * LDK + kk * 32 + koff]);
+      for (int i = 0; i < TN; ++i) {
+        const int r = wn * WN + i * 16 + frow;
+        af[i] = *reinterpret_cast<const uint4*>(st + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+      }
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
-        bf[j] = *reinterpret_cast<const uint4*>(&sx[buf][(wm * WM + j * 16 + frow) * LDK + kk * 32 + koff]);
+      for (int j = 0; j < TM; ++j) {
+        const int r = wm * WM + j * 16 + frow;
+        bf[j] = *reinterpret_cast<const uint4*>(st + BN * 128 + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+      }
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bf[j], acc[i][j]);
     }
-    if (more) {
-      stash(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
   }
+  // (the last step waited for vmcnt 0: no load is in flight past this point)
 
-  // lane holds rows rbase .. rbase+3 of column `col` of every 16x16 tile
   const int col = lane & 15, rbase = 4 * (lane >> 4);
   if (silu_epi) {
     S* out = static_cast<S*>(a.out);

@@ -376,23 +376,21 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       else launch((k_gemv_mfma<T, 2, 4, 1>), grid, dim3(256), 0, s, a, l.epi);
       e = hipGetLastError();
     } else if (l.K % 64 == 0 && l.ldo % 4 == 0) {
-      // tiled GEMM: gate|up on 128x128 tiles with 4 waves along the weight rows; other projections
-      // on 128 x (64 | 128) tiles of 2 x 2 waves with K split until ~200 blocks are in flight
+      // ring GEMM: gate|up on 128x128 tiles, other projections on 64x128 tiles with K split (fp32
+      // partials) while the grid has fewer than 256 blocks and each split keeps >= 8 k-steps
       const bool silu_epi = l.epi == EPI_SILU;
-      const bool wide_m = silu_epi || l.K >= 4096;
-      const int BN = 128, BM = wide_m ? 128 : 64;
+      const int BN = silu_epi ? 128 : 64, BM = 128;
       const int n_tiles = silu_epi ? (l.N + BN / 2 - 1) / (BN / 2) : (l.N + BN - 1) / BN;
       const int m_tiles = (l.M + BM - 1) / BM;
       int ks = 1;
       if (l.ksplit_ok && l.epi == EPI_F32) {
-        while (ks < kMaxKsplit && n_tiles * m_tiles * ks < 200 && (l.K / 64) / (ks * 2) >= 8) ks *= 2;
+        while (ks < kMaxKsplit && n_tiles * m_tiles * ks < 256 && (l.K / 64) / (ks * 2) >= 8) ks *= 2;
       }
       a.ksplit = ks;
       if (l.ksplit_used) *l.ksplit_used = ks;
       dim3 grid(8 * ((n_tiles + 7) / 8) * m_tiles, 1, ks);
-      if (silu_epi) launch((k_gemm_tn<T, 128, 128, 64, 4, 1>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
-      else if (wide_m) launch((k_gemm_tn<T, 128, 128, 64, 2, 2>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
-      else launch((k_gemm_tn<T, 128, 64, 64, 2, 2>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
+      if (silu_epi) launch((k_gemm_ring<T, 128, 128, 2, 2, 2>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
+      else launch((k_gemm_ring<T, 64, 128, 2, 2, 2>), grid, dim3(256), 0, s, a, l.epi, n_tiles, m_tiles);
       e = hipGetLastError();
     } else {
       const bool big = l.M > 64;
