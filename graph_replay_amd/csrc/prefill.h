@@ -68,22 +68,40 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
   for (int t = 0; t < DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
   const int nkb = maxpos / 16 + 1;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int pb0 = (kb < a.bt_stride) ? bt[kb] : -1;
-    const int pb = pb0 >= 0 ? pb0 : a.num_blocks - 1;
-    const size_t tileoff = (static_cast<size_t>(pb) * a.nkv + g) * 16 * D;   // K and V tiles alike
-    const S* kp = static_cast<const S*>(a.k_pool) + tileoff;
-    const S* vp = static_cast<const S*>(a.v_pool) + tileoff;
-    uint4 kf[KS];
+  // table entries of the first 64 key blocks (lane j holds block j), fetched before the loop
+  const int bt_pre = (lane < a.bt_stride) ? bt[lane] : -1;
+  auto pool_block = [&](int kb) -> int {   // kb is wave-uniform
+    int pb0;
+    if (kb < 64) pb0 = __builtin_amdgcn_readlane(bt_pre, kb);
+    else pb0 = (kb < a.bt_stride) ? bt[kb] : -1;
+    return pb0 >= 0 ? pb0 : a.num_blocks - 1;
+  };
+  uint4 kf[KS];   // K fragment: key col, dims ks*32 + 8*grp .. + 8
+  uint2 vf[DT];   // V^T fragment: dim t*16 + col, keys 4*grp .. + 4 (from the dim-major V tile)
+  auto load_k = [&](int pb) {
+    const S* kp = static_cast<const S*>(a.k_pool) + (static_cast<size_t>(pb) * a.nkv + g) * 16 * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const uint4*>(kp + col * D + ks * 32 + 8 * grp);
-    // V^T fragments straight from the dim-major V tile: dim t*16 + col, keys 4*grp .. + 4
-    uint2 vf[DT];
+  };
+  auto load_v = [&](int pb) {
+    const S* vp = static_cast<const S*>(a.v_pool) + (static_cast<size_t>(pb) * a.nkv + g) * 16 * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t) vf[t] = *reinterpret_cast<const uint2*>(vp + (t * 16 + col) * 16 + 4 * grp);
+  };
+  {
+    const int pb = pool_block(0);
+    load_k(pb);
+    load_v(pb);
+  }
+  // software-pipelined: block kb + 1's K is requested once block kb's score product has issued,
+  // its V once the value product has
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    const int next = pool_block(more ? kb + 1 : kb);
     f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(kf[ks], qf[ks], s);
+    if (more) load_k(next);
     // causal mask; this lane holds keys kb*16 + 4*grp + i of query `col`
     float bm = -INFINITY;
 #pragma unroll
@@ -122,6 +140,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < DT; ++t) acc[t] = mfma16x16x16<T>(vf[t], pt, acc[t]);
+    if (more) load_v(next);
   }
   if (col < cnt) {
     S* o = static_cast<S*>(a.out) + (static_cast<size_t>(q0 + col) * a.nq + h) * D;
