@@ -24,9 +24,9 @@ form single-token layer, zero-layer closed form).
 """
 from .model import (RequestCache, attend, final_logits, forward_request, linear, rmsnorm, rope,
                     rope_angles, silu_mul)
-from .sampling import argmax_lowest, gumbel_scores, philox4x32_10, philox_uniforms, sample
+from .sampling import argmax_lowest, gumbel_scores, philox4x32_10, philox_uniforms, sample, topk_topp_keep
 from .paging import bucket_for, pad_rows, slot_of
 
-__all__ = ["RequestCache", "attend", "final_logits", "forward_request", "linear", "rmsnorm", "rope",
+__all__ = ["RequestCache", "attend", "final_logits", "forward_request", "linear", "rmsnorm", "rope", "topk_topp_keep",
            "rope_angles", "silu_mul", "argmax_lowest", "gumbel_scores", "philox4x32_10", "philox_uniforms",
            "sample", "bucket_for", "pad_rows", "slot_of"]

@@ -8,6 +8,17 @@ Gumbel-max equation).
 
 Reading: ties in the argmax go to the lowest index.
 
+Top-k and top-p filtering follow the same section (the passage after the sampler listing): the
+filters run before the argmax and set the filtered logits to -inf; top-k uses a fixed k, and top-p is
+a sort and a mask. Readings of this build, where the passage does not fix the details:
+  * both filters act only when T > 0, on z = logit / T computed in fp32 (the device's value), so
+    every comparison that decides the kept set is the same fp32 comparison on both sides;
+  * top-k keeps every z >= the k-th largest z (ties at the threshold are kept); k <= 0 or k >= V
+    disables it;
+  * top-p acts after top-k, on the softmax of the kept z: in the order (z descending, index
+    ascending), a token is kept iff the mass strictly before it is < p (the shortest prefix whose
+    mass reaches p); p >= 1 disables it.
+
 The uniforms, where they are not passed in, come from Philox-4x32-10 as
 defined by Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
 1, 2, 3" (SC'11): ten rounds of two 32x32->64-bit multiplies with the
@@ -38,11 +49,39 @@ def gumbel_scores(z: np.ndarray, temperature: float, u: np.ndarray) -> np.ndarra
     return (z.astype(F32) / F32(temperature) + g).astype(F32)
 
 
-def sample(z: np.ndarray, temperature: float, u: np.ndarray = None) -> np.ndarray:
-    """Token ids [rows] from logits [rows, V]: greedy at T == 0, Gumbel-max otherwise."""
+def sample(z: np.ndarray, temperature: float, u: np.ndarray = None, top_k: int = 0,
+           top_p: float = 1.0) -> np.ndarray:
+    """Token ids [rows] from logits [rows, V]: greedy at T == 0, Gumbel-max otherwise, over the
+    tokens that top-k / top-p keep (filtered scores are -inf)."""
     if temperature == 0:
         return argmax_lowest(z)
-    return argmax_lowest(gumbel_scores(z, temperature, u))
+    sc = gumbel_scores(z, temperature, u)
+    if (0 < top_k < z.shape[-1]) or top_p < 1.0:
+        zs = np.atleast_2d(z.astype(F32) / F32(temperature))
+        keep = np.stack([topk_topp_keep(r, top_k, top_p) for r in zs]).reshape(sc.shape)
+        sc = np.where(keep, sc, F32(-np.inf)).astype(F32)
+    return argmax_lowest(sc)
+
+
+def topk_topp_keep(z32: np.ndarray, top_k: int, top_p: float) -> np.ndarray:
+    """Kept-token mask [V] of one row of fp32 z = logit / T (see the module docstring)."""
+    z32 = np.asarray(z32, dtype=F32)
+    V = z32.shape[0]
+    keep = np.ones(V, dtype=bool)
+    if 0 < top_k < V:
+        kth = np.sort(z32)[::-1][top_k - 1]
+        keep = z32 >= kth
+    if top_p < 1.0:
+        z = z32.astype(np.float64)
+        w = np.where(keep, np.exp(z - z[keep].max()), 0.0)
+        mass = w / w.sum()
+        order = np.lexsort((np.arange(V), -z))          # z descending, then index ascending
+        order = order[keep[order]]
+        before = np.cumsum(mass[order]) - mass[order]
+        kept = np.zeros(V, dtype=bool)
+        kept[order] = before < top_p
+        keep = kept
+    return keep
 
 
 def _mulhilo(a: np.ndarray, b: int):

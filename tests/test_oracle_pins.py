@@ -176,6 +176,96 @@ def test_gumbel_limits():
     assert stats.chisquare(counts).pvalue > 1e-3                                  # huge T: uniform
 
 
+# ---------------------------------------------------------------- top-k / top-p filters
+
+def _keep_brute(z32, k, p):
+    """Independent statement of the kept set: sort the (value, index) pairs, cut top-k by count with
+    ties at the k-th value kept, then grow a prefix one token at a time until its mass reaches p."""
+    V = len(z32)
+    pairs = sorted(((-float(z32[i]), i) for i in range(V)))
+    cand = [i for _, i in pairs]
+    if 0 < k < V:
+        kth = float(z32[cand[k - 1]])
+        cand = [i for i in cand if float(z32[i]) >= kth]
+    if p < 1.0:
+        zmax = max(float(z32[i]) for i in cand)
+        w = {i: math.exp(float(z32[i]) - zmax) for i in cand}
+        tot = sum(w.values())
+        chosen, acc = [], 0.0
+        for i in cand:
+            chosen.append(i)
+            acc += w[i] / tot
+            if acc >= p:
+                break
+        cand = chosen
+    out = np.zeros(V, dtype=bool)
+    out[cand] = True
+    return out
+
+
+def test_filters_off_keep_everything():
+    z = np.random.default_rng(5).normal(size=50).astype(F32)
+    for k, p in [(0, 1.0), (50, 1.0), (80, 1.0), (-3, 1.0), (0, 1.5)]:
+        assert oracle.topk_topp_keep(z, k, p).all()
+
+
+def test_top1_keeps_the_argmax_and_its_ties():
+    z = np.array([0.5, 2.0, -1.0, 2.0, 1.0], dtype=F32)
+    assert oracle.topk_topp_keep(z, 1, 1.0).tolist() == [False, True, False, True, False]
+    assert oracle.topk_topp_keep(z, 3, 1.0).tolist() == [False, True, False, True, True]
+
+
+def test_top_p_hand_computed_masses():
+    # probabilities 0.4, 0.3, 0.2, 0.1 placed at shuffled indices
+    z = np.log(np.array([0.2, 0.4, 0.1, 0.3])).astype(F32)
+    keep = lambda k, p: np.nonzero(oracle.topk_topp_keep(z, k, p))[0].tolist()
+    assert keep(0, 0.39) == [1]            # the second token starts at mass 0.4 >= 0.39
+    assert keep(0, 0.41) == [1, 3]
+    assert keep(0, 0.5) == [1, 3]
+    assert keep(0, 0.75) == [0, 1, 3]
+    assert keep(0, 0.95) == [0, 1, 2, 3]
+    # top-k first: {0.4, 0.3} renormalised to 4/7, 3/7
+    assert keep(2, 0.5) == [1]
+    assert keep(2, 0.6) == [1, 3]
+    assert keep(3, 0.85) == [0, 1, 3]      # 4/9 + 3/9 = 7/9 < 0.85: the third one is needed
+
+
+def test_top_p_uniform_logits_keep_lowest_indices():
+    z = np.zeros(10, dtype=F32)
+    assert np.nonzero(oracle.topk_topp_keep(z, 0, 0.35))[0].tolist() == [0, 1, 2, 3]
+    assert np.nonzero(oracle.topk_topp_keep(z, 0, 0.05))[0].tolist() == [0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_filters_match_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    V = 12
+    z = np.round(rng.normal(size=V) * 2, 1).astype(F32)      # rounded: some exact ties
+    for k in [0, 1, 2, 5, 11, 12]:
+        for p in [1.0, 0.97, 0.8, 0.5, 0.2, 0.01]:
+            got = oracle.topk_topp_keep(z, k, p)
+            assert np.array_equal(got, _keep_brute(z, k, p)), (k, p)
+
+
+def test_filtered_gumbel_max_frequencies_match_filtered_softmax():
+    """The pages' milestone check, with filters: 20,000 Gumbel-max draws with Philox uniforms land
+    on the kept tokens with frequencies softmax(z / T) renormalised over the kept set."""
+    rng = np.random.default_rng(11)
+    V, T, k, p, n = 16, 0.8, 10, 0.9, 20000
+    logits = rng.normal(size=V).astype(F32) * F32(1.5)
+    u = oracle.philox_uniforms(seed=4321, step=0, rows=n, cols=V)
+    draws = oracle.sample(np.repeat(logits[None, :], n, 0), T, u, top_k=k, top_p=p)
+    keep = oracle.topk_topp_keep(logits / F32(T), k, p)
+    assert keep[draws].all()
+    zz = logits.astype(np.float64) / T
+    w = np.where(keep, np.exp(zz - zz.max()), 0.0)
+    expected = w / w.sum() * n
+    counts = np.bincount(draws, minlength=V)
+    idx = np.nonzero(keep)[0]
+    chi2 = float(((counts[idx] - expected[idx]) ** 2 / expected[idx]).sum())
+    assert chi2 < stats.chi2.ppf(0.999, len(idx) - 1), chi2
+
+
 # ---------------------------------------------------------------- paging and buckets
 
 def test_bucket_choice_matches_page_example(golden_dir):
