@@ -86,9 +86,12 @@ def step_mixed(ctx, packed: StepPacked) -> None:
 
 
 def step_sample(ctx, d_logits: int, rows: int, ld: int, vocab: int, h_temperature: Optional[np.ndarray],
-                d_uniforms: Optional[int], seed: int, counter: int, d_tokens: int) -> None:
+                h_top_k: Optional[np.ndarray], h_top_p: Optional[np.ndarray], d_uniforms: Optional[int], seed: int,
+                counter: int, d_tokens: int) -> None:
     t = _f32(h_temperature) if h_temperature is not None else None
-    rc = _lib.load().step_sample(ctx, C.cast(C.c_void_p(d_logits), _lib.F32P), rows, ld, vocab, _fp(t),
+    k = _i32(h_top_k) if h_top_k is not None else None
+    p = _f32(h_top_p) if h_top_p is not None else None
+    rc = _lib.load().step_sample(ctx, C.cast(C.c_void_p(d_logits), _lib.F32P), rows, ld, vocab, _fp(t), _ip(k), _fp(p),
                                  C.cast(C.c_void_p(d_uniforms), _lib.F32P) if d_uniforms else None,
                                  C.c_uint64(seed), C.c_uint64(counter), C.cast(C.c_void_p(d_tokens), _lib.I32P))
     _raise(rc, ctx)
@@ -115,7 +118,8 @@ class Decoder:
     def __init__(self, shape, weights: dict, *, num_blocks: int, max_blocks_per_seq: int, max_position: int,
                  max_batch: int = 1, buckets: Optional[Sequence[int]] = None, max_tokens: int = 0,
                  max_reqs: int = 0, max_logit_rows: int = 0, use_graphs: bool = True, history: bool = False,
-                 mixed_buckets: Optional[Sequence[int]] = None, device: str = "cuda:0"):
+                 mixed_buckets: Optional[Sequence[int]] = None, sampling_filters: bool = False,
+                 device: str = "cuda:0"):
         import torch
         lib = _lib.load()
         self.torch = torch
@@ -196,6 +200,7 @@ class Decoder:
         cfg.num_mixed_buckets = len(mixed_buckets)
         for i, b in enumerate(mixed_buckets):
             cfg.mixed_buckets[i] = int(b)
+        cfg.sampling_filters = int(sampling_filters)
         self.cfg = cfg
         self.buckets = buckets
         nbytes = step_workspace_bytes(cfg)
@@ -218,22 +223,26 @@ class Decoder:
         self.ctx = step_init(cfg, w, b, self.stream.cuda_stream)
 
     # -- steps
-    def decode(self, tokens, positions, seq_lens, slots, block_table, temperature=None, seed: int = 0) -> None:
+    def decode(self, tokens, positions, seq_lens, slots, block_table, temperature=None, seed: int = 0,
+               top_k=None, top_p=None) -> None:
         t, p, s, sl = _i32(tokens), _i32(positions), _i32(seq_lens), _i32(slots)
         bt = _i32(block_table)
         if bt.ndim != 2 or bt.shape[0] != t.shape[0]:
             raise ValueError("block_table must be [rows, width]")
         temp = _f32(temperature) if temperature is not None else None
+        tk = _i32(top_k) if top_k is not None else None
+        tp = _f32(top_p) if top_p is not None else None
         hb = StepBatch(num_rows=t.shape[0], bt_width=bt.shape[1], h_tokens=_ip(t), h_positions=_ip(p),
                        h_seq_lens=_ip(s), h_slot_mapping=_ip(sl), h_block_table=_ip(bt), h_temperature=_fp(temp),
-                       seed=seed)
+                       seed=seed, h_top_k=_ip(tk), h_top_p=_fp(tp))
         step_decode(self.ctx, hb)
 
     def decode_continue(self) -> None:
         step_decode(self.ctx, None)
 
     def mixed(self, query_start_loc, seq_lens, tokens, positions, slots, block_table, logits_indices,
-              num_prefill_reqs: int, temperature=None, seed: int = 0, prefill_attention: int = 0) -> None:
+              num_prefill_reqs: int, temperature=None, seed: int = 0, prefill_attention: int = 0, top_k=None,
+              top_p=None) -> None:
         qsl, sl_, t, p, s = _i32(query_start_loc), _i32(seq_lens), _i32(tokens), _i32(positions), _i32(slots)
         bt, li = _i32(block_table), _i32(logits_indices)
         temp = _f32(temperature) if temperature is not None else None
@@ -243,13 +252,17 @@ class Decoder:
                         h_query_start_loc=_ip(qsl), h_seq_lens=_ip(sl_), h_tokens=_ip(t), h_positions=_ip(p),
                         h_slot_mapping=_ip(s), h_block_table=_ip(bt), h_logits_indices=_ip(li),
                         h_temperature=_fp(temp), seed=seed, prefill_attention=prefill_attention)
+        tk = _i32(top_k) if top_k is not None else None
+        tp = _f32(top_p) if top_p is not None else None
+        hp.h_top_k, hp.h_top_p = _ip(tk), _fp(tp)
         step_mixed(self.ctx, hp)
 
-    def sample(self, logits, temperature=None, uniforms=None, seed: int = 0, counter: int = 0):
+    def sample(self, logits, temperature=None, uniforms=None, seed: int = 0, counter: int = 0, top_k=None,
+               top_p=None):
         torch = self.torch
         rows, ld = logits.shape
         out = torch.empty(rows, dtype=torch.int32, device=self.device)
-        step_sample(self.ctx, logits.data_ptr(), rows, ld, ld, temperature,
+        step_sample(self.ctx, logits.data_ptr(), rows, ld, ld, temperature, top_k, top_p,
                     uniforms.data_ptr() if uniforms is not None else None, seed, counter, out.data_ptr())
         return out
 

@@ -22,7 +22,8 @@ class StepConfig(C.Structure):
         (n, C.c_int32) for n in ("block_size", "num_blocks", "max_blocks_per_seq", "max_position", "max_batch",
                                  "max_tokens", "max_reqs", "max_logit_rows", "num_buckets")] + [
         ("buckets", C.c_int32 * MAX_BUCKETS), ("use_graphs", C.c_int32),
-        ("num_mixed_buckets", C.c_int32), ("mixed_buckets", C.c_int32 * MAX_BUCKETS)]
+        ("num_mixed_buckets", C.c_int32), ("mixed_buckets", C.c_int32 * MAX_BUCKETS),
+        ("sampling_filters", C.c_int32)]
 
 
 class StepWeights(C.Structure):
@@ -39,7 +40,7 @@ class StepBuffers(C.Structure):
 class StepBatch(C.Structure):
     _fields_ = [("num_rows", C.c_int32), ("bt_width", C.c_int32), ("h_tokens", I32P), ("h_positions", I32P),
                 ("h_seq_lens", I32P), ("h_slot_mapping", I32P), ("h_block_table", I32P), ("h_temperature", F32P),
-                ("seed", C.c_uint64)]
+                ("seed", C.c_uint64), ("h_top_k", I32P), ("h_top_p", F32P)]
 
 
 class StepPacked(C.Structure):
@@ -47,7 +48,8 @@ class StepPacked(C.Structure):
                                          "bt_width")] + [
         (n, I32P) for n in ("h_query_start_loc", "h_seq_lens", "h_tokens", "h_positions", "h_slot_mapping",
                             "h_block_table", "h_logits_indices")] + [
-        ("h_temperature", F32P), ("seed", C.c_uint64), ("prefill_attention", C.c_int32)]
+        ("h_temperature", F32P), ("seed", C.c_uint64), ("prefill_attention", C.c_int32),
+        ("h_top_k", I32P), ("h_top_p", F32P)]
 
 
 EXPORTS = {
@@ -56,7 +58,8 @@ EXPORTS = {
                             C.POINTER(P)]),
     "step_decode": (C.c_int, [P, C.POINTER(StepBatch)]),
     "step_mixed": (C.c_int, [P, C.POINTER(StepPacked)]),
-    "step_sample": (C.c_int, [P, F32P, C.c_int32, C.c_int32, C.c_int32, F32P, F32P, C.c_uint64, C.c_uint64, I32P]),
+    "step_sample": (C.c_int, [P, F32P, C.c_int32, C.c_int32, C.c_int32, F32P, I32P, F32P, F32P, C.c_uint64,
+                              C.c_uint64, I32P]),
     "step_profile_decode": (C.c_int, [P, C.c_int32, F32P, I32P]),
     "step_kernel_kind_name": (C.c_char_p, [C.c_int32]),
     "step_last_bucket": (C.c_int, [P]),

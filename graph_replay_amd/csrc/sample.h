@@ -33,6 +33,279 @@ __device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Top-k / top-p filters before the Gumbel-max argmax (same page and section: the filters run before
+// the argmax and set filtered logits to -inf; a fixed k keeps shapes static, and top-p is a sort and
+// a mask). Readings: both act only at T > 0, on z = logit / T in fp32; top-k keeps every z >= the
+// k-th largest (k <= 0 or k >= V: off); top-p acts on the softmax of the top-k-kept z, in the order
+// (z descending, index ascending), and keeps a token while the mass before it is < p (p >= 1: off).
+//
+// k_sample_filter writes per row a pair (x, y): token i is kept iff key_i > x or (key_i == x and
+// i < y), key being an order-preserving 32-bit key of z. One block of 1024 threads per row:
+//   * a key range known to hold the cut is split into 2048 bins (counts for top-k, masses for
+//     top-p), the bin holding the cut is found by a scan from the top bin down, and the range
+//     shrinks to that bin, until the bin holds at most 2048 tokens or a single key value;
+//   * the bin's tokens are gathered into LDS and sorted by (key desc, index asc), which gives the
+//     cut exactly; a single key value with more tokens than that (a run of exact ties) is cut by
+//     a scan in index order.
+// Masses are exp(z - zmax) in fixed point (units of 2^-31, truncated) summed as 64-bit integers, so
+// every sum is exact and independent of thread order: the filter is deterministic. Top-p looks at
+// tokens within 30 of zmax (their mass is all but < 2e-8 of the total): when p asks for more than
+// that window holds, the whole top-k set is kept.
+__device__ inline uint32_t fkey(float z) {
+  const uint32_t u = (z == 0.f) ? 0u : __float_as_uint(z);   // -0 and +0 share a key
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float fkey_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ inline unsigned long long qmass(float z, float zmax) {
+  return static_cast<unsigned long long>(static_cast<uint32_t>(__expf(z - zmax) * 2147483648.0f));
+}
+
+struct FilterArgs {
+  const float* logits;
+  int ld, vocab;
+  const float* temperature;           // [rows] or nullptr (greedy: nothing filtered)
+  const int* top_k;                   // [rows] or nullptr
+  const float* top_p;                 // [rows] or nullptr
+  const int* n_rows;                  // device row count (nullptr: gridDim.x); rows past it are idle
+  uint2* filt;                        // [rows] out: (x, y)
+};
+
+constexpr int kFilterThreads = 1024;
+
+__device__ inline unsigned long long shfl_up_u64(unsigned long long v, int d) {
+  const unsigned lo = __shfl_up(static_cast<unsigned>(v), d, 64);
+  const unsigned hi = __shfl_up(static_cast<unsigned>(v >> 32), d, 64);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// exclusive scan over the block in thread order (all threads call it); wtot: 16 entries of LDS
+__device__ inline unsigned long long block_excl_scan(unsigned long long v, unsigned long long* wtot,
+                                                     unsigned long long* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  unsigned long long inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned long long o = shfl_up_u64(inc, d);
+    if (lane >= d) inc += o;
+  }
+  __syncthreads();
+  if (lane == 63) wtot[wid] = inc;
+  __syncthreads();
+  unsigned long long base = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wid) base += wtot[w];
+    all += wtot[w];
+  }
+  *total = all;
+  return base + inc - v;
+}
+
+__global__ __launch_bounds__(kFilterThreads) void k_sample_filter(FilterArgs a) {
+  constexpr int NB = 2048, CAP = 2048, NT = kFilterThreads;
+  __shared__ unsigned hcnt[NB];
+  __shared__ unsigned long long hmass[NB];
+  __shared__ uint32_t ckey[CAP];
+  __shared__ int cidx[CAP];
+  __shared__ unsigned long long wtot[NT / 64];
+  __shared__ float wred[NT / 64];
+  __shared__ int s_bin, s_n, s_idx;
+  __shared__ unsigned long long s_above;
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  if (a.n_rows && row >= *a.n_rows) return;
+  const int V = a.vocab;
+  const float T = a.temperature ? a.temperature[row] : 0.f;
+  const int k = a.top_k ? a.top_k[row] : 0;
+  const float p = a.top_p ? a.top_p[row] : 1.f;
+  const bool use_k = T > 0.f && k > 0 && k < V;
+  const bool use_p = T > 0.f && p < 1.f;
+  if (!use_k && !use_p) {
+    if (t == 0) a.filt[row] = make_uint2(0u, 0x7fffffffu);
+    return;
+  }
+  const float* lg = a.logits + static_cast<size_t>(row) * a.ld;
+
+  // zmax and zmin (block reductions in a fixed order)
+  float zmx = -INFINITY, zmn = INFINITY;
+  for (int i = t; i < V; i += NT) {
+    const float z = lg[i] / T;
+    zmx = fmaxf(zmx, z);
+    zmn = fminf(zmn, z);
+  }
+  zmx = wave_max(zmx);
+  zmn = -wave_max(-zmn);
+  if (lane == 0) wred[wid] = zmx;
+  __syncthreads();
+  float zmax = -INFINITY;
+  for (int w = 0; w < NT / 64; ++w) zmax = fmaxf(zmax, wred[w]);
+  __syncthreads();
+  if (lane == 0) wred[wid] = zmn;
+  __syncthreads();
+  float zmin = INFINITY;
+  for (int w = 0; w < NT / 64; ++w) zmin = fminf(zmin, wred[w]);
+  __syncthreads();
+
+  // Find the cut in [lo, hi] (keys >= kmin only): by count (target = k, above = count of kept keys
+  // above hi) or by mass (target = p * Z). Returns (x, y) for the kept set, or found = false when
+  // the range holds too little (mass phase: the cut is below the window).
+  auto select = [&](bool by_mass, uint32_t lo, uint32_t hi, uint32_t kmin, double target,
+                    unsigned long long above, uint2* out) -> bool {
+    for (;;) {
+      for (int i = t; i < NB; i += NT) { hcnt[i] = 0u; hmass[i] = 0ull; }
+      __syncthreads();
+      const unsigned long long W = static_cast<unsigned long long>(hi) - lo + 1ull;
+      for (int i = t; i < V; i += NT) {
+        const float z = lg[i] / T;
+        const uint32_t key = fkey(z);
+        if (key < lo || key > hi || key < kmin) continue;
+        const int bin = static_cast<int>((static_cast<unsigned long long>(key - lo) * NB) / W);
+        atomicAdd(&hcnt[bin], 1u);
+        if (by_mass) atomicAdd(&hmass[bin], qmass(z, zmax));
+      }
+      if (t == 0) s_bin = -1;
+      __syncthreads();
+      // descending bins: thread t holds bins NB-1-2t and NB-2-2t
+      const int b0 = NB - 1 - 2 * t, b1 = b0 - 1;
+      const unsigned long long v0 = by_mass ? hmass[b0] : hcnt[b0], v1 = by_mass ? hmass[b1] : hcnt[b1];
+      unsigned long long tot;
+      const unsigned long long ex = block_excl_scan(v0 + v1, wtot, &tot) + above;
+      if (static_cast<double>(ex) < target && target <= static_cast<double>(ex + v0)) {
+        s_bin = b0;
+        s_above = ex;
+      } else if (static_cast<double>(ex + v0) < target && target <= static_cast<double>(ex + v0 + v1)) {
+        s_bin = b1;
+        s_above = ex + v0;
+      }
+      __syncthreads();
+      const int b = s_bin;
+      if (b < 0) return false;
+      above = s_above;
+      const unsigned n = hcnt[b];
+      const uint32_t nlo = lo + static_cast<uint32_t>((static_cast<unsigned long long>(b) * W + NB - 1) / NB);
+      const uint32_t nhi = lo + static_cast<uint32_t>(((static_cast<unsigned long long>(b) + 1) * W + NB - 1) / NB) - 1u;
+      __syncthreads();
+      lo = nlo;
+      hi = nhi;
+      if (n <= CAP) {
+        // gather the bin, sort by (key desc, index asc), cut exactly
+        if (t == 0) s_n = 0;
+        for (int i = t; i < CAP; i += NT) { ckey[i] = 0u; cidx[i] = 0x7fffffff; }
+        __syncthreads();
+        for (int i = t; i < V; i += NT) {
+          const uint32_t key = fkey(lg[i] / T);
+          if (key < lo || key > hi || key < kmin) continue;
+          const int pos = atomicAdd(&s_n, 1);
+          ckey[pos] = key;
+          cidx[pos] = i;
+        }
+        __syncthreads();
+        for (int size = 2; size <= CAP; size <<= 1) {
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int e = t; e < CAP / 2; e += NT) {
+              const int i = 2 * e - (e & (stride - 1));
+              const int j = i + stride;
+              const bool desc = ((i & size) == 0);   // first half of each run: (key desc, idx asc)
+              const uint32_t ki = ckey[i], kj = ckey[j];
+              const int ii = cidx[i], ij = cidx[j];
+              const bool i_first = ki > kj || (ki == kj && ii < ij);
+              if (i_first != desc) {
+                ckey[i] = kj; ckey[j] = ki;
+                cidx[i] = ij; cidx[j] = ii;
+              }
+            }
+            __syncthreads();
+          }
+        }
+        if (!by_mass) {
+          if (t == 0) *out = make_uint2(ckey[static_cast<int>(target - static_cast<double>(above)) - 1], 0x7fffffffu);
+        } else {
+          // two sorted entries per thread, in order
+          unsigned long long m0 = 2 * t < static_cast<int>(n) ? qmass(fkey_value(ckey[2 * t]), zmax) : 0ull;
+          unsigned long long m1 = 2 * t + 1 < static_cast<int>(n) ? qmass(fkey_value(ckey[2 * t + 1]), zmax) : 0ull;
+          if (t == 0) s_idx = -1;
+          __syncthreads();
+          unsigned long long tt;
+          const unsigned long long e0 = block_excl_scan(m0 + m1, wtot, &tt) + above;
+          int jsel = -1;
+          if (2 * t < static_cast<int>(n) && target <= static_cast<double>(e0 + m0) && static_cast<double>(e0) < target) jsel = 2 * t;
+          else if (2 * t + 1 < static_cast<int>(n) && target <= static_cast<double>(e0 + m0 + m1) &&
+                   static_cast<double>(e0 + m0) < target) jsel = 2 * t + 1;
+          if (jsel >= 0) s_idx = jsel;
+          __syncthreads();
+          const int j = s_idx;
+          // rounding can leave the cut just past the last entry: keep the whole bin then
+          if (t == 0) *out = (j >= 0) ? make_uint2(ckey[j], static_cast<uint32_t>(cidx[j]) + 1u)
+                                      : make_uint2(ckey[n - 1], static_cast<uint32_t>(cidx[n - 1]) + 1u);
+        }
+        __syncthreads();
+        return true;
+      }
+      if (lo == hi) {
+        // one key value held by more than CAP tokens: exact ties
+        if (!by_mass) {
+          if (t == 0) *out = make_uint2(lo, 0x7fffffffu);
+          __syncthreads();
+          return true;
+        }
+        const unsigned long long q = qmass(fkey_value(lo), zmax);
+        const double need = (target - static_cast<double>(above)) / static_cast<double>(q > 0 ? q : 1ull);
+        const long long c = static_cast<long long>(fmax(1.0, ceil(need)));   // ties to keep
+        if (c >= static_cast<long long>(n)) {
+          if (t == 0) *out = make_uint2(lo, 0x7fffffffu);
+          __syncthreads();
+          return true;
+        }
+        // the c-th tie in index order: contiguous chunks per thread, exclusive scan of the counts
+        const int ch = (V + NT - 1) / NT, c0 = t * ch, c1 = min(V, c0 + ch);
+        unsigned own = 0;
+        for (int i = c0; i < c1; ++i) own += (fkey(lg[i] / T) == lo) ? 1u : 0u;
+        unsigned long long tt;
+        const unsigned long long ex = block_excl_scan(own, wtot, &tt);
+        if (static_cast<long long>(ex) < c && c <= static_cast<long long>(ex + own)) {
+          long long r = c - static_cast<long long>(ex);
+          for (int i = c0; i < c1; ++i)
+            if (fkey(lg[i] / T) == lo && --r == 0) {
+              s_idx = i;
+              break;
+            }
+        }
+        __syncthreads();
+        if (t == 0) *out = make_uint2(lo, static_cast<uint32_t>(s_idx) + 1u);
+        __syncthreads();
+        return true;
+      }
+    }
+  };
+
+  __shared__ uint2 s_out;
+  uint32_t kthr = 0u;
+  if (use_k) {
+    select(false, fkey(zmin), fkey(zmax), 0u, static_cast<double>(k), 0ull, &s_out);
+    __syncthreads();
+    kthr = s_out.x;
+  }
+  if (!use_p) {
+    if (t == 0) a.filt[row] = make_uint2(kthr, 0x7fffffffu);
+    return;
+  }
+  // top-p over the top-k set: Z = total mass of keys >= kthr (window bins + the tail below it)
+  const uint32_t wlo = max(kthr, fkey(zmax - 30.f));
+  unsigned long long zt = 0;
+  for (int i = t; i < V; i += NT) {
+    const float z = lg[i] / T;
+    if (fkey(z) >= kthr) zt += qmass(z, zmax);
+  }
+  unsigned long long Z;
+  (void)block_excl_scan(zt, wtot, &Z);
+  __syncthreads();
+  const double target = static_cast<double>(p) * static_cast<double>(Z);
+  const bool found = select(true, wlo, fkey(zmax), kthr, target, 0ull, &s_out);
+  __syncthreads();
+  if (t == 0) a.filt[row] = found ? s_out : make_uint2(kthr, 0x7fffffffu);
+}
+
 struct SampleArgs {
   const float* logits;
   int ld, vocab, chunk;               // chunk: columns per block (multiple of 1024)
@@ -45,6 +318,7 @@ struct SampleArgs {
   unsigned* row_cnt;                  // [rows], zero between launches (reset by the row's last block)
   unsigned* done_cnt;                 // [1], zero between launches (reset by the last row)
   const int* n_rows;                  // device row count (nullptr: gridDim.x); rows past it are idle
+  const uint2* filt;                  // [rows] top-k / top-p cut from k_sample_filter, or nullptr
   int* tokens_out;                    // [rows]
   // decode advance (advance != 0)
   int advance;
@@ -100,6 +374,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   const uint64_t step = a.rng ? a.rng[1] : a.step;
   const float* z = a.logits + static_cast<size_t>(row) * a.ld;
   const int c0 = ch * a.chunk, c1 = min(a.vocab, c0 + a.chunk);
+  const uint2 cut = a.filt ? a.filt[row] : make_uint2(0u, 0x7fffffffu);   // keep all when absent
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   for (int c = c0 + 4 * threadIdx.x; c < c1; c += 4 * blockDim.x) {
@@ -124,7 +399,10 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       float sc = zz[j];
       if (T > 0.f) {
         const float uu = fminf(fmaxf(u[j], 1e-10f), 1.0f);
-        sc = sc / T - logf(-logf(uu));
+        const float zd = sc / T;
+        const uint32_t key = fkey(zd);
+        const bool kept = key > cut.x || (key == cut.x && c + j < static_cast<int>(cut.y));
+        sc = kept ? zd - logf(-logf(uu)) : -INFINITY;
       }
       best_merge(bv, bi, sc, c + j);
     }

@@ -37,6 +37,7 @@ struct Layout {  // byte offsets into the workspace
   size_t rope_cos, rope_sin;
   size_t resid[2], h, qkv, q, attn_o, d_o, d_d, act;
   size_t attn_part, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
+  size_t samp_topk, samp_topp, samp_filt;
   size_t total;
   int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
   int max_splits_alloc;               // splits per row the partial buffer holds (at 64 keys/split)
@@ -111,11 +112,11 @@ int elem_bytes(int dtype) { return dtype == STEP_F32 ? 4 : 2; }
 
 enum KernelKind {
   KK_QKV = 0, KK_QKV_POST, KK_ATTN, KK_O, KK_GATE_UP, KK_DOWN, KK_LM_HEAD, KK_NORM, KK_SAMPLE, KK_PREFILL_ATTN,
-  KK_ATTN_COMBINE, KK_COUNT
+  KK_ATTN_COMBINE, KK_SAMPLE_FILTER, KK_COUNT
 };
 const char* const kKindNames[KK_COUNT] = {"qkv_proj", "qknorm_rope_kvwrite", "attn_decode", "o_proj", "gate_up_silu",
                                           "down_proj", "lm_head", "add_rmsnorm", "sample", "attn_prefill",
-                                          "attn_combine"};
+                                          "attn_combine", "sample_filter"};
 
 // Called before every kernel launch: counts it and, while profiling, marks its start.
 // Profile events for the next launch: set by pre_launch during a profile step, taken by launch().
@@ -181,13 +182,15 @@ bool compute_layout(const step_config& c, Layout& L) {
     off = align_up(off + bytes);
     return o;
   };
-  L.dmeta_bytes = 16 + sizeof(int) * (5 * static_cast<size_t>(MB) + static_cast<size_t>(MB) * W);
+  // decode: rng[2] | ids | pos | slot | len | temp [MB] | bt [MB*W] | top_k | top_p [MB]
+  L.dmeta_bytes = 16 + sizeof(int) * (7 * static_cast<size_t>(MB) + static_cast<size_t>(MB) * W);
   L.dmeta = take(L.dmeta_bytes);
   // mixed: rng[2] | tok | pos | slot | row_req | row_len [TM] | qsl [RM+1] | req_len [RM] | bt [RM*W]
   //        | logit_idx [LM] | temp [LM] | tile_req, tile_q0 [TM/16 + RM + 1] | dec_rows [RM] | n_logits
+  //        | top_k [LM] | top_p [LM]
   const size_t tiles = TM / 16 + RM + 1;
   L.mmeta_bytes = 16 + sizeof(int) * (5 * static_cast<size_t>(TM) + (RM + 1) + RM + static_cast<size_t>(RM) * W +
-                                      2 * static_cast<size_t>(LM) + 2 * tiles + RM + 1);
+                                      2 * static_cast<size_t>(LM) + 2 * tiles + RM + 1 + 2 * static_cast<size_t>(LM));
   L.mmeta = take(L.mmeta_bytes);
   L.rope_cos = take(sizeof(float) * static_cast<size_t>(c.max_position) * (d / 2));
   L.rope_sin = take(sizeof(float) * static_cast<size_t>(c.max_position) * (d / 2));
@@ -215,7 +218,11 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.samp_idx = take(sizeof(int) * static_cast<size_t>(LM) * nch_max);
   L.samp_cnt = take(sizeof(unsigned) * static_cast<size_t>(LM));
   L.samp_done = take(sizeof(unsigned) * 4);
-  L.samp_temp = take(sizeof(float) * static_cast<size_t>(LM));
+  // standalone sampler inputs: temperature | top_k | top_p [LM] each, one contiguous copy
+  L.samp_temp = take(3 * sizeof(float) * static_cast<size_t>(LM));
+  L.samp_topk = L.samp_temp + sizeof(float) * static_cast<size_t>(LM);
+  L.samp_topp = L.samp_topk + sizeof(int) * static_cast<size_t>(LM);
+  L.samp_filt = take(sizeof(uint2) * static_cast<size_t>(std::max(LM, MB)));
   L.samp_rng = take(16);
   L.total = off;
   (void)RM;
@@ -517,7 +524,19 @@ int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_st
 int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, const float* temp, const float* uniforms,
                const uint64_t* rng, uint64_t seed, uint64_t stepc, int* tokens_out, int advance, int* ids, int* pos,
                int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld,
-               const int* n_rows = nullptr) {
+               const int* n_rows = nullptr, const int* topk = nullptr, const float* topp = nullptr) {
+  uint2* filt = nullptr;
+  if (temp && (topk || topp)) {
+    // per-row top-k / top-p cut first (one block of 1024 threads per row)
+    FilterArgs f{};
+    f.logits = logits; f.ld = ld; f.vocab = vocab; f.temperature = temp; f.top_k = topk; f.top_p = topp;
+    f.n_rows = n_rows;
+    f.filt = filt = reinterpret_cast<uint2*>(ctx->ws + ctx->lay.samp_filt);
+    pre_launch(ctx, KK_SAMPLE_FILTER);
+    launch(k_sample_filter, dim3(rows), dim3(kFilterThreads), 0, ctx->stream, f);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample filter launch failed: %s", hipGetErrorString(e));
+  }
   SampleArgs a{};
   a.logits = logits; a.ld = ld; a.vocab = vocab;
   int chunk = 1024;
@@ -532,6 +551,7 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
   a.n_rows = n_rows;
+  a.filt = filt;
   const int nch = (vocab + chunk - 1) / chunk;
   pre_launch(ctx, KK_SAMPLE);
   launch(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
@@ -552,6 +572,8 @@ struct DecodeMeta {
   int *ids, *pos, *slot, *len;
   float* temp;
   int* bt;
+  int* topk;
+  float* topp;
 };
 DecodeMeta decode_meta(char* base, int MB, int W) {
   DecodeMeta m;
@@ -562,7 +584,8 @@ DecodeMeta decode_meta(char* base, int MB, int W) {
   m.len = m.slot + MB;
   m.temp = reinterpret_cast<float*>(m.len + MB);
   m.bt = reinterpret_cast<int*>(m.temp + MB);
-  (void)W;
+  m.topk = m.bt + static_cast<size_t>(MB) * W;
+  m.topp = reinterpret_cast<float*>(m.topk + MB);
   return m;
 }
 
@@ -666,6 +689,8 @@ struct MixedMeta {
   int *tile_req, *tile_q0;
   int* dec_rows;   // packed rows of the decode requests, -1 past them (bucketed plan)
   int* n_logits;   // sampled rows (bucketed plan)
+  int* topk;       // [LM] per sampled row
+  float* topp;
 };
 MixedMeta mixed_meta(char* base, const Layout& L, int W) {
   MixedMeta m;
@@ -686,6 +711,8 @@ MixedMeta mixed_meta(char* base, const Layout& L, int W) {
   m.tile_q0 = m.tile_req + tiles;
   m.dec_rows = m.tile_q0 + tiles;
   m.n_logits = m.dec_rows + RM;
+  m.topk = m.n_logits + 1;
+  m.topp = reinterpret_cast<float*>(m.topk + LM);
   return m;
 }
 
@@ -703,7 +730,8 @@ int run_decode(step_ctx* ctx, int B) {
   };
   TRY(run_layers<T>(ctx, B, m.ids, m.pos, m.slot, 0, nullptr, true, attn));
   return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
-                    m.len, m.slot, m.bt, W, ctx->history, c.max_position);
+                    m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr,
+                    c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
 }
 
 int run_decode_any(step_ctx* ctx, int B) {
@@ -790,7 +818,8 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
   };
   TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, false, attn));
   return run_sample(ctx, ctx->logits, p.n_logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
-                    nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0, p.fixed ? m.n_logits : nullptr);
+                    nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0, p.fixed ? m.n_logits : nullptr,
+                    c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
 }
 
 // Metadata of a mixed step padded to TB tokens with no real rows (capture and warm-up state).
@@ -804,7 +833,7 @@ void fill_mixed_padding(const step_ctx* ctx, char* base, int TB) {
   for (int j = 0; j <= L.RM; ++j) m.qsl[j] = 0;
   for (int j = 0; j < L.RM; ++j) { m.req_len[j] = 0; m.dec_rows[j] = -1; }
   std::memset(m.bt, 0, sizeof(int) * static_cast<size_t>(L.RM) * W);
-  for (int i = 0; i < L.LM; ++i) { m.lidx[i] = 0; m.temp[i] = 0.f; }
+  for (int i = 0; i < L.LM; ++i) { m.lidx[i] = 0; m.temp[i] = 0.f; m.topk[i] = 0; m.topp[i] = 1.f; }
   for (int t = 0; t < TB / 16 + L.RM; ++t) { m.tile_req[t] = -1; m.tile_q0[t] = 0; }
   *m.n_logits = 0;
 }
@@ -831,7 +860,9 @@ void fill_decode_padding(const step_config& c, char* base) {
   DecodeMeta m = decode_meta(base, c.max_batch, c.max_blocks_per_seq);
   m.rng[0] = 0;
   m.rng[1] = 0;
-  for (int i = 0; i < c.max_batch; ++i) { m.ids[i] = 0; m.pos[i] = 0; m.slot[i] = -1; m.len[i] = 0; m.temp[i] = 0.f; }
+  for (int i = 0; i < c.max_batch; ++i) {
+    m.ids[i] = 0; m.pos[i] = 0; m.slot[i] = -1; m.len[i] = 0; m.temp[i] = 0.f; m.topk[i] = 0; m.topp[i] = 1.f;
+  }
   std::memset(m.bt, 0, sizeof(int) * static_cast<size_t>(c.max_batch) * c.max_blocks_per_seq);
 }
 
@@ -919,7 +950,7 @@ extern "C" int step_init(const step_config* cfg, const step_weights* w, const st
   hipError_t e;
   if ((e = hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking)) != hipSuccess) return hip_fail(e, "hipStreamCreate");
   ctx->stage_bytes = std::max(ctx->lay.dmeta_bytes, ctx->lay.mmeta_bytes);
-  ctx->stage_bytes = std::max(ctx->stage_bytes, sizeof(float) * static_cast<size_t>(ctx->lay.LM));
+  ctx->stage_bytes = std::max(ctx->stage_bytes, 3 * sizeof(float) * static_cast<size_t>(ctx->lay.LM));
   for (int i = 0; i < 2; ++i) {
     if ((e = hipHostMalloc(reinterpret_cast<void**>(&ctx->h_stage[i]), ctx->stage_bytes, hipHostMallocDefault)) != hipSuccess)
       return hip_fail(e, "hipHostMalloc");
@@ -1060,6 +1091,8 @@ extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) {
       return fail(ctx, STEP_EINVAL, "bt_width %d above max_blocks_per_seq %d", hb->bt_width, c.max_blocks_per_seq);
     if (!hb->h_tokens || !hb->h_positions || !hb->h_seq_lens || !hb->h_slot_mapping || (hb->bt_width && !hb->h_block_table))
       return fail(ctx, STEP_EINVAL, "NULL batch array");
+    if ((hb->h_top_k || hb->h_top_p) && !c.sampling_filters)
+      return fail(ctx, STEP_EINVAL, "top-k / top-p given to a context built without sampling_filters");
     B = bucket_of(c, r);
     if (B < 0) return fail(ctx, STEP_EINVAL, "no bucket holds %d rows", r);
     const int W = c.max_blocks_per_seq;
@@ -1096,6 +1129,8 @@ extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) {
       m.slot[i] = hb->h_slot_mapping[i];
       m.len[i] = hb->h_seq_lens[i];
       m.temp[i] = hb->h_temperature ? hb->h_temperature[i] : 0.f;
+      m.topk[i] = hb->h_top_k ? hb->h_top_k[i] : 0;
+      m.topp[i] = hb->h_top_p ? hb->h_top_p[i] : 1.f;
       int* row = m.bt + static_cast<size_t>(i) * W;
       for (int j = 0; j < W; ++j) row[j] = j < hb->bt_width ? hb->h_block_table[static_cast<size_t>(i) * hb->bt_width + j] : -1;
     }
@@ -1135,6 +1170,8 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
     return fail(ctx, STEP_EINVAL, "NULL batch array");
   if (hp->prefill_attention != 0 && hp->prefill_attention != 1)
     return fail(ctx, STEP_EINVAL, "prefill_attention must be 0 or 1");
+  if ((hp->h_top_k || hp->h_top_p) && !c.sampling_filters)
+    return fail(ctx, STEP_EINVAL, "top-k / top-p given to a context built without sampling_filters");
   const int* qsl = hp->h_query_start_loc;
   if (qsl[0] != 0 || qsl[R] != T) return fail(ctx, STEP_EINVAL, "query_start_loc must run from 0 to num_tokens");
   for (int j = 0; j < R; ++j) {
@@ -1203,6 +1240,8 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
   for (int i = 0; i < NL; ++i) {
     m.lidx[i] = hp->h_logits_indices[i];
     m.temp[i] = hp->h_temperature ? hp->h_temperature[i] : 0.f;
+    m.topk[i] = hp->h_top_k ? hp->h_top_k[i] : 0;
+    m.topp[i] = hp->h_top_p ? hp->h_top_p[i] : 1.f;
   }
   for (int j = Rp; j < R; ++j) m.dec_rows[j - Rp] = qsl[j];
   *m.n_logits = NL;
@@ -1232,24 +1271,38 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
 extern "C" int step_last_mixed_bucket(const step_ctx* ctx) { return ctx ? ctx->last_mixed_bucket : STEP_ESTATE; }
 
 extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, int32_t ld, int32_t vocab,
-                           const float* h_temperature, const float* d_uniforms, uint64_t seed, uint64_t counter,
-                           int32_t* d_tokens_out) {
+                           const float* h_temperature, const int32_t* h_top_k, const float* h_top_p,
+                           const float* d_uniforms, uint64_t seed, uint64_t counter, int32_t* d_tokens_out) {
   if (!ctx || ctx->dead) return STEP_ESTATE;
   if (!d_logits || !d_tokens_out) return fail(ctx, STEP_EINVAL, "NULL logits or tokens");
   if (rows < 1 || rows > ctx->lay.LM) return fail(ctx, STEP_EINVAL, "rows %d outside [1, %d]", rows, ctx->lay.LM);
   if (vocab < 1 || vocab > ctx->cfg.vocab || ld < vocab) return fail(ctx, STEP_EINVAL, "bad vocab %d / ld %d", vocab, ld);
   float* temp = nullptr;
+  int* topk = nullptr;
+  float* topp = nullptr;
   if (h_temperature) {
+    // temperature | top_k | top_p staged together, one copy
+    const size_t LM = static_cast<size_t>(ctx->lay.LM);
     int slot_i;
     char* st = stage_slot(ctx, &slot_i);
     if (!st) return fail(ctx, STEP_EHIP, "waiting for the staging buffer failed");
-    std::memcpy(st, h_temperature, sizeof(float) * rows);
-    temp = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_temp);
-    HIPCHK(ctx, hipMemcpyAsync(temp, st, sizeof(float) * rows, hipMemcpyHostToDevice, ctx->stream));
+    float* s_temp = reinterpret_cast<float*>(st);
+    int* s_topk = reinterpret_cast<int*>(st + sizeof(float) * LM);
+    float* s_topp = reinterpret_cast<float*>(st + 2 * sizeof(float) * LM);
+    for (int i = 0; i < rows; ++i) {
+      s_temp[i] = h_temperature[i];
+      s_topk[i] = h_top_k ? h_top_k[i] : 0;
+      s_topp[i] = h_top_p ? h_top_p[i] : 1.f;
+    }
+    char* dst = ctx->ws + ctx->lay.samp_temp;
+    HIPCHK(ctx, hipMemcpyAsync(dst, st, 3 * sizeof(float) * LM, hipMemcpyHostToDevice, ctx->stream));
     HIPCHK(ctx, hipEventRecord(ctx->stage_ev[slot_i], ctx->stream));
+    temp = reinterpret_cast<float*>(dst);
+    if (h_top_k) topk = reinterpret_cast<int*>(ctx->ws + ctx->lay.samp_topk);
+    if (h_top_p) topp = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_topp);
   }
   return run_sample(ctx, d_logits, rows, ld, vocab, temp, d_uniforms, nullptr, seed, counter, d_tokens_out, 0, nullptr,
-                    nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0);
+                    nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, topk, topp);
 }
 
 extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_ms, int32_t* h_kind) {

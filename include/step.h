@@ -85,6 +85,16 @@ typedef struct {
    * exact-size eager plan. 0 buckets: every mixed step runs the exact-size eager plan. */
   int32_t num_mixed_buckets;
   int32_t mixed_buckets[STEP_MAX_BUCKETS];
+  /* 1: decode and mixed steps apply per-row top-k / top-p filters before the Gumbel-max argmax (one
+   * more kernel per step, captured in the graphs); 0: no filters, and the batches' h_top_k / h_top_p
+   * must be NULL. "Fast decode: syncs, CUDA graphs and compilation", section "Sampling without the
+   * CPU": filtered logits are set to -inf before the argmax; top-k with a fixed k, top-p as a sort
+   * and a mask. Semantics (rows with T > 0 only, on z = logit / T in fp32): top-k keeps every z >=
+   * the k-th largest z (k <= 0 or k >= vocab: off); top-p then keeps, in the order (z desc, index
+   * asc), each token while the softmax mass (over the top-k set) before it is < p (p >= 1: off).
+   * Top-p only looks at tokens within 30 of the largest z; a p that needs more keeps the whole
+   * top-k set (the mass left out is below 2e-8). */
+  int32_t sampling_filters;
 } step_config;
 
 typedef struct {
@@ -120,6 +130,8 @@ typedef struct {
   const int32_t *h_tokens, *h_positions, *h_seq_lens, *h_slot_mapping, *h_block_table;
   const float *h_temperature;    /* [num_rows]; NULL => all greedy; 0 => greedy row */
   uint64_t seed;                 /* Philox key for the Gumbel noise of this and later continued steps */
+  const int32_t *h_top_k;        /* [num_rows] or NULL (off); needs sampling_filters; kept by continued steps */
+  const float *h_top_p;          /* [num_rows] or NULL (off); needs sampling_filters; kept by continued steps */
 } step_batch;
 
 /* One packed mixed step: prefill requests first (their chunk tokens contiguous), decode requests
@@ -134,6 +146,8 @@ typedef struct {
   const float *h_temperature;        /* [num_logits] or NULL (greedy) */
   uint64_t seed;
   int32_t prefill_attention;         /* 0: packed MFMA kernel (16-bit dtypes); 1: one query row per token */
+  const int32_t *h_top_k;            /* [num_logits] or NULL (off); needs sampling_filters */
+  const float *h_top_p;              /* [num_logits] or NULL (off); needs sampling_filters */
 } step_packed;
 
 /* Device bytes the workspace must hold for this configuration (0 if the configuration is invalid). */
@@ -162,11 +176,12 @@ int step_decode(step_ctx *ctx, const step_batch *h_batch);
 int step_mixed(step_ctx *ctx, const step_packed *h_batch);
 
 /* Standalone sampler over d_logits [rows][ld] fp32: temperature h_temperature[row] (NULL: greedy);
- * d_uniforms [rows][ld] fp32 supplies the uniforms (NULL: Philox-4x32-10 keyed by seed with step
- * counter `counter`). Writes d_tokens_out[rows]. */
+ * optional per-row top-k h_top_k and top-p h_top_p (NULL: off; semantics as for sampling_filters,
+ * which this call does not need); d_uniforms [rows][ld] fp32 supplies the uniforms (NULL:
+ * Philox-4x32-10 keyed by seed with step counter `counter`). Writes d_tokens_out[rows]. */
 int step_sample(step_ctx *ctx, const float *d_logits, int32_t rows, int32_t ld, int32_t vocab,
-                const float *h_temperature, const float *d_uniforms, uint64_t seed, uint64_t counter,
-                int32_t *d_tokens_out);
+                const float *h_temperature, const int32_t *h_top_k, const float *h_top_p,
+                const float *d_uniforms, uint64_t seed, uint64_t counter, int32_t *d_tokens_out);
 
 /* Profiling (a debug aid, not part of the graphed path): runs one decode step at the bucket of the last
  * batch EAGERLY over the current static state, behind a short bounded device-side wait so the kernels
