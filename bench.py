@@ -34,19 +34,22 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kind_bytes(shape, rows: int, seq_lens_sum: int) -> dict:
-    """Algorithmic HBM bytes of ONE launch of each kernel kind in a decode step of `rows` rows."""
+def kind_bytes(shape, rows: int, seq_lens_sum: int, weight_prefetch: bool = False) -> dict:
+    """Algorithmic HBM bytes of ONE launch of each kernel kind in a decode step of `rows` rows. With the
+    weight prefetch (at most 8 rows), the attention launch also reads the layer's O, gate|up and down
+    weights from HBM into L2 (the GEMVs then find them there), so they count for that launch."""
     eb = shape.elem_bytes
     H, I, V, d = shape.hidden, shape.intermediate, shape.vocab, shape.head_dim
     nq, nkv = shape.q_heads, shape.kv_heads
     qkv = shape.qkv_out
+    staged = (H * nq * d + 2 * I * H + H * I) * eb if (weight_prefetch and rows <= 8) else 0
     return {
         "qkv_proj": qkv * H * eb + rows * qkv * 4,
         "o_proj": H * nq * d * eb + rows * H * 4,
         "gate_up_silu": 2 * I * H * eb + rows * I * eb,
         "down_proj": H * I * eb + rows * H * 4,
         "lm_head": V * H * eb + rows * V * 4,
-        "attn_decode": seq_lens_sum * 2 * nkv * d * eb + rows * nq * d * (4 + eb),
+        "attn_decode": seq_lens_sum * 2 * nkv * d * eb + rows * nq * d * (4 + eb) + staged,
         "qknorm_rope_kvwrite": rows * (qkv * 4 + nq * d * 4 + 2 * nkv * d * eb),
         "sample": rows * V * 4,
         "add_rmsnorm": rows * H * (4 + 4 + 4 + eb),
@@ -87,7 +90,7 @@ def measured_traffic(workload: str, kind: str):
     return int(k.get("fetch_bytes", 0) + k.get("write_bytes", 0))
 
 
-def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int) -> dict:
+def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int, weight_prefetch: bool = False) -> dict:
     prof = dec.profile_decode()
     per = {}
     for name, ms in prof:
@@ -96,7 +99,7 @@ def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int) -> dict:
         t[1] += 1
     dom = max(per, key=lambda k: per[k][0])
     avg_ms = per[dom][0] / per[dom][1]
-    nbytes = kind_bytes(shape, rows, seq_lens_sum)[dom]
+    nbytes = kind_bytes(shape, rows, seq_lens_sum, weight_prefetch)[dom]
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
     table = {k: {"launches": v[1], "total_us": round(v[0] * 1e3, 1), "avg_us": round(v[0] * 1e3 / v[1], 2)}
              for k, v in sorted(per.items(), key=lambda kv: -kv[1][0])}
@@ -106,14 +109,14 @@ def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int) -> dict:
             "profile_sum_us": round(sum(ms for _, ms in prof) * 1e3, 1), "kernels": table}
 
 
-def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024):
+def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefetch: bool = True):
     import graph_replay_amd as g
     torch = __import__("torch")
     total = ctx_len + 1 + warmup + steps + 2            # positions used, profile step included
     table = synth.block_tables([total], -(-total // 16) + 2, 1002, shuffled=False)[0]
     nb = len(table) + 2
     dec = g.Decoder(shape, W, num_blocks=nb, max_blocks_per_seq=len(table), max_position=total + 16, max_batch=1,
-                    buckets=[1], max_tokens=ctx_len, max_reqs=1, max_logit_rows=1)
+                    buckets=[1], max_tokens=ctx_len, max_reqs=1, max_logit_rows=1, weight_prefetch=weight_prefetch)
     bt = np.asarray([table], np.int32)
     prompt = synth.tokens(ctx_len, shape.vocab, 1002)
     pos = np.arange(ctx_len, dtype=np.int32)
@@ -133,7 +136,7 @@ def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024):
     seq_sum_mean = start_len + (steps - 1) / 2.0
     nbytes = step_bytes(shape, seq_sum_mean)
     ms_step = ms / steps
-    roof = roofline_from_profile(shape, dec, 1, start_len + steps)
+    roof = roofline_from_profile(shape, dec, 1, start_len + steps, weight_prefetch)
     roof["traffic"] = measured_traffic("qwen3-0.6b_bs1", roof["kernel"])
     out = {
         "tok_s": steps / (ms * 1e-3), "ms_per_step": ms_step, "bytes_per_step": int(nbytes),
@@ -312,6 +315,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy a 1 GiB device buffer 4 times (calibrates the HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-weight-prefetch", action="store_true",
+                    help="batch-1 step without the L2 weight prefetch in the attention launches")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -344,7 +349,7 @@ def main():
     if args.workload == "mixed":
         print(json.dumps({"metric": METRIC, **run_mixed()}), flush=True)
         return
-    r1 = run_bs1(shape, W, args.steps, warmup)
+    r1 = run_bs1(shape, W, args.steps, warmup, weight_prefetch=not args.no_weight_prefetch)
     r32 = None if (args.no_bs32 or args.workload == "bs1") else run_bs32(shape, W, args.steps, warmup)
     rmix = None if (args.no_mixed or args.workload == "bs1") else run_mixed()
     cpu = None if args.no_cpu else cpu_baseline(shape, W)
@@ -354,7 +359,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "qwen3-0.6b-bf16-decode-bs1-ctx1024", "batch": 1, "context": 1024,
                    "decode_steps": args.steps, "graph": "one hipGraph replay per step",
-                   "kernels_per_step": r1["kernels_per_step"]},
+                   "kernels_per_step": r1["kernels_per_step"], "weight_prefetch": not args.no_weight_prefetch},
         "step_hbm": {"bytes_per_step": r1["bytes_per_step"], "achieved": round(r1["step_hbm_GBps"], 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r1["step_hbm_frac"], 4)},
         "roofline": r1["roofline"],

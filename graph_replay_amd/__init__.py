@@ -119,6 +119,7 @@ class Decoder:
                  max_batch: int = 1, buckets: Optional[Sequence[int]] = None, max_tokens: int = 0,
                  max_reqs: int = 0, max_logit_rows: int = 0, use_graphs: bool = True, history: bool = False,
                  mixed_buckets: Optional[Sequence[int]] = None, sampling_filters: bool = False,
+                 weight_prefetch: bool = True,
                  device: str = "cuda:0"):
         import torch
         lib = _lib.load()
@@ -201,6 +202,7 @@ class Decoder:
         for i, b in enumerate(mixed_buckets):
             cfg.mixed_buckets[i] = int(b)
         cfg.sampling_filters = int(sampling_filters)
+        cfg.weight_prefetch = int(weight_prefetch)
         self.cfg = cfg
         self.buckets = buckets
         nbytes = step_workspace_bytes(cfg)

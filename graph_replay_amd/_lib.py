@@ -23,7 +23,8 @@ class StepConfig(C.Structure):
                                  "max_tokens", "max_reqs", "max_logit_rows", "num_buckets")] + [
         ("buckets", C.c_int32 * MAX_BUCKETS), ("use_graphs", C.c_int32),
         ("num_mixed_buckets", C.c_int32), ("mixed_buckets", C.c_int32 * MAX_BUCKETS),
-        ("sampling_filters", C.c_int32)]
+        ("sampling_filters", C.c_int32),
+        ("weight_prefetch", C.c_int32)]
 
 
 class StepWeights(C.Structure):

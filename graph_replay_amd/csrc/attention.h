@@ -111,12 +111,24 @@ struct AttnRowsArgs {
   const int* row_req;        // row -> block-table row (nullptr: identity)
   const int* seq_lens;       // [rows] keys visible to the row, its own token included
   int split_tokens;          // P: keys per split (multiple of 64)
-  int max_splits;            // gridDim.z
+  int max_splits;            // splits per row (gridDim.z, past which come prefetch blocks)
   int num_blocks;            // pool blocks; a negative table entry reads the scratch block
   void* out;                 // [rows][nq * D] in the model dtype
   float* partials;           // [rows][nq][max_splits][D + 2]: (max, sum, unnormalised output)
+  unsigned* split_cnt;       // [grid rows][nkv] arrival counters, zero between launches: the last
+                             // split of a (row, KV head) to finish merges the partials
   float scale;
+  L2Prefetch pf;             // blocks with blockIdx.z >= max_splits only prefetch weights (pf.n > 0)
 };
+
+// Blocks past the split grid prefetch the weights of the GEMVs that follow (see l2_prefetch).
+__device__ inline bool attn_prefetch_block(const AttnRowsArgs& a) {
+  if (static_cast<int>(blockIdx.z) < a.max_splits) return false;
+  const int plane = gridDim.x * gridDim.y;
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y + plane * blockIdx.z;
+  l2_prefetch(a.pf, lin, plane * a.max_splits, plane * (gridDim.z - a.max_splits));
+  return true;
+}
 
 constexpr int kMaxSplits = 128;   // splits per row one launch may use (the host sizes P for it)
 
@@ -219,9 +231,69 @@ __device__ inline void attn_finish(const AttnRowsArgs& a, int row, int prow, int
       out[(g * G + j) * D + dd] = T::from_f(O / Ls);
     } else {
       float* pp = part + (static_cast<size_t>(j) * a.max_splits + sp) * (D + 2);
-      pp[2 + dd] = O;
-      if (dd == 0) { pp[0] = M; pp[1] = Ls; }
+      st_dev(pp + 2 + dd, O);
+      if (dd == 0) { st_dev(pp, M); st_dev(pp + 1, Ls); }
     }
+  }
+  if (nsplit == 1) return;
+  // The last split to arrive merges all splits in split order, so the result does not depend on
+  // which split finished first. The partials go through device-scope stores and loads and one
+  // device-scope counter per (row, KV head), reset by the merging block for the next launch.
+  __shared__ int s_last;
+  __shared__ float s_m[G][kMaxSplits], s_l[G][kMaxSplits];
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive_last(a.split_cnt + static_cast<size_t>(prow) * a.nkv + g, nsplit);
+  __syncthreads();
+  if (!s_last) return;
+  // One round of loads: each split's (max, sum) as one 8-byte load, and the first kOB splits of each
+  // thread's output dim, all in flight together; then the sums in split order. Block = 256 threads.
+  constexpr int kOB = 32;
+  const int nml = G * nsplit;
+  auto ml_ptr = [&](int m) { return part + (static_cast<size_t>(m / nsplit) * a.max_splits + m % nsplit) * (D + 2); };
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < G * D; i0 += blockDim.x) {
+    const int i = i0 + tid;
+    const bool act = i < G * D;
+    const int j = act ? i / D : 0, dd = i % D;
+    const float* pj = part + static_cast<size_t>(j) * a.max_splits * (D + 2) + 2 + dd;
+    float ov[kOB];
+#pragma unroll
+    for (int k = 0; k < kOB; ++k) ov[k] = (act && k < nsplit) ? ld_dev(pj + static_cast<size_t>(k) * (D + 2)) : 0.f;
+    if (i0 == 0) {
+      // (unrolled: a loop here would make the compiler drain the O loads before entering it)
+      float2 v[(G * kMaxSplits + 255) / 256];
+#pragma unroll
+      for (int r = 0; r < (G * kMaxSplits + 255) / 256; ++r) {
+        const int m = tid + 256 * r;
+        if (m < nml) v[r] = ld_dev2(ml_ptr(m));
+      }
+#pragma unroll
+      for (int r = 0; r < (G * kMaxSplits + 255) / 256; ++r) {
+        const int m = tid + 256 * r;
+        if (m < nml) { s_m[m / nsplit][m % nsplit] = v[r].x; s_l[m / nsplit][m % nsplit] = v[r].y; }
+      }
+      __syncthreads();
+    }
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, s_m[j][s2]);
+    float Ls = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kOB) {
+      if (s0) {
+#pragma unroll
+        for (int k = 0; k < kOB; ++k)
+          ov[k] = (act && s0 + k < nsplit) ? ld_dev(pj + static_cast<size_t>(s0 + k) * (D + 2)) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kOB; ++k) {
+        if (s0 + k < nsplit) {
+          const float f = __expf(s_m[j][s0 + k] - M);
+          Ls += s_l[j][s0 + k] * f;
+          O += ov[k] * f;
+        }
+      }
+    }
+    if (act) out[(g * G + j) * D + dd] = T::from_f(O / Ls);
   }
 }
 
@@ -230,10 +302,11 @@ __device__ inline void attn_finish(const AttnRowsArgs& a, int row, int prow, int
 // "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers keys
 // [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends on
 // the bucket only and replays as captured. A row with one split writes its output; otherwise each
-// split writes (max, sum, unnormalised output) and k_attn_combine merges them in split order.
-// Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv query
-// heads sharing the KV head are processed together. Two kernels share this contract:
-// k_attn_rows_mfma (16-bit types, matrix cores) and k_attn_rows (any type, fp32 FMA; fp32 models).
+// split writes (max, sum, unnormalised output) and the last split to finish merges them in split
+// order. Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv
+// query heads sharing the KV head are processed together. Blocks past the split grid (z >=
+// max_splits) only prefetch weights into L2. Two kernels share this contract: k_attn_rows_mfma
+// (16-bit types, matrix cores) and k_attn_rows (any type, fp32 FMA; fp32 models).
 
 // fp32 FMA version: 8 lanes per key in the score phase, a lane owns 8 dims in the value phase.
 template <class T, int D, int G>
@@ -245,6 +318,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wo[4][G][D];
   __shared__ float qs[G][D];
+  if (attn_prefetch_block(a)) return;
   const int prow = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int row = a.row_ids ? a.row_ids[prow] : prow;
   if (row < 0) return;
@@ -410,6 +484,7 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
   __shared__ __align__(16) float qs[G][D];
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wo[4][G][D];
+  if (attn_prefetch_block(a)) return;
   const int prow = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int row = a.row_ids ? a.row_ids[prow] : prow;
   if (row < 0) return;
@@ -581,41 +656,6 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
   }
   __syncthreads();
   attn_finish<T, D, G>(a, row, prow, g, sp, nsplit, wm, wl, wo);
-}
-
-// Merge the split partials of rows with more than one split: grid (grid rows, nq), block D threads
-// (thread = output dim). Split maxima and sums go through LDS; the weighted sum runs in split
-// order, so the result does not depend on which split finished first.
-template <class T, int D>
-__global__ __launch_bounds__(128) void k_attn_combine(int nq, const int* __restrict__ row_ids,
-                                                      const int* __restrict__ seq_lens, int split_tokens,
-                                                      int max_splits, const float* __restrict__ partials,
-                                                      void* __restrict__ out) {
-  extern __shared__ float sm_comb[];      // [2 * max_splits]
-  const int prow = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int row = row_ids ? row_ids[prow] : prow;
-  if (row < 0) return;
-  const int L = seq_lens[row];
-  const int ns = (L + split_tokens - 1) / split_tokens;
-  if (L <= 0 || ns <= 1) return;
-  const float* part = partials + (static_cast<size_t>(prow) * nq + h) * max_splits * (D + 2);
-  float* mx = sm_comb;
-  float* sl = sm_comb + max_splits;
-  for (int s = t; s < ns; s += blockDim.x) {
-    mx[s] = part[static_cast<size_t>(s) * (D + 2)];
-    sl[s] = part[static_cast<size_t>(s) * (D + 2) + 1];
-  }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, mx[s]);
-  float Ls = 0.f, O = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
-    const float f = __expf(mx[s] - M);
-    Ls += sl[s] * f;
-    O += part[static_cast<size_t>(s) * (D + 2) + 2 + t] * f;
-  }
-  static_cast<typename T::S*>(out)[(static_cast<size_t>(row) * nq + h) * D + t] = T::from_f(O / Ls);
 }
 
 }  // namespace gr

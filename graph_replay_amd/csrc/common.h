@@ -90,6 +90,12 @@ __device__ inline float ld_dev(const float* p) {
   return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ inline int ld_dev(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// two consecutive floats (8-byte aligned) in one load
+__device__ inline float2 ld_dev2(const float* p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
 // all of this thread's stores have completed (are visible at device scope for device-scope stores)
 __device__ inline void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
 // counts this block in; true for exactly one block: the last of `expected` to arrive (the counter
@@ -99,6 +105,72 @@ __device__ inline bool arrive_last(unsigned* counter, unsigned expected) {
   const bool last = (prev == expected - 1);
   if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return last;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Weight prefetch into the L2 of the XCD that will read it. A batch-1 decode layer reads 30 MB of
+// weights in GEMV kernels that each last only a few microseconds, so each is bound by the HBM
+// latency of its first loads rather than by bandwidth, while the attention between them leaves HBM
+// mostly idle. Blocks appended to a latency-bound kernel touch (one dword per 128-byte line) the
+// rows that later GEMV blocks will read, on the XCD where those blocks will run: workgroups of a
+// launch go round-robin over the 8 XCDs, so block b of any kernel runs on XCD b mod 8 and shares
+// that XCD's 4 MB L2 with block b' of another kernel iff b = b' mod 8.
+// Target t: a 1-D GEMV grid of nblk blocks; block g reads rows [g*pb, g*pb + pb) below n_rows and,
+// when up_off > 0, the rows up_off + [g*pb, g*pb + pb) too (a stacked gate|up matrix); a row is
+// row_bytes long. Touches are hints: no result depends on them.
+constexpr int kPrefetchTargets = 3;
+struct L2Prefetch {
+  const char* base[kPrefetchTargets];
+  int row_bytes[kPrefetchTargets];
+  int pb[kPrefetchTargets];        // rows per GEMV block (per half for a gate|up matrix)
+  int n_rows[kPrefetchTargets];    // rows in the GEMV's output range (gate rows for gate|up)
+  int up_off[kPrefetchTargets];    // row offset of the up half, 0 if none
+  int nblk[kPrefetchTargets];      // GEMV grid size
+  int n;                           // targets in use (0: no prefetch blocks)
+};
+
+// Called by prefetch block `q` of `nq` (the launch's blocks [first, first + nq)); `lin` is the
+// block's linear id in its launch, which fixes its XCD.
+__device__ inline void l2_prefetch(const L2Prefetch& p, int lin, int first, int nq) {
+  const int xcd = lin & 7;
+  const int q = (lin - first) >> 3;         // index among this XCD's prefetch blocks
+  const int nq_x = nq >> 3;                 // prefetch blocks per XCD (a partial last group idles)
+  if (q >= nq_x) return;
+  constexpr int kLine = 128, kBatch = 16;
+  int items[kPrefetchTargets], lpr[kPrefetchTargets], total = 0;
+  for (int t = 0; t < kPrefetchTargets; ++t) {
+    if (t >= p.n) { items[t] = 0; lpr[t] = 1; continue; }
+    lpr[t] = (p.row_bytes[t] + kLine - 1) / kLine;
+    const int gblocks = (p.nblk[t] > xcd) ? (p.nblk[t] - 1 - xcd) / 8 + 1 : 0;   // blocks g = xcd mod 8
+    items[t] = gblocks * p.pb[t] * (p.up_off[t] ? 2 : 1) * lpr[t];
+    total += items[t];
+  }
+  const int stride = nq_x * static_cast<int>(blockDim.x);
+  uint32_t acc = 0;
+  for (int i0 = q * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x); i0 < total; i0 += kBatch * stride) {
+    uint32_t v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      int i = i0 + k * stride;
+      v[k] = 0;
+      if (i >= total) continue;
+      int t = 0;
+      while (t + 1 < kPrefetchTargets && i >= items[t]) { i -= items[t]; ++t; }
+      const int per_g = p.pb[t] * (p.up_off[t] ? 2 : 1) * lpr[t];
+      const int g = xcd + 8 * (i / per_g);
+      const int w = i % per_g;
+      const int r = w / lpr[t], line = w % lpr[t];
+      const int half = r / p.pb[t];
+      const int row = g * p.pb[t] + (r % p.pb[t]);
+      if (row >= p.n_rows[t]) continue;
+      const size_t off = static_cast<size_t>(row + half * p.up_off[t]) * p.row_bytes[t] +
+                         min(line * kLine, p.row_bytes[t] - 4);
+      v[k] = *reinterpret_cast<const uint32_t*>(p.base[t] + off);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) acc ^= v[k];
+  }
+  asm volatile("" ::"v"(acc));   // keeps the loads; nothing is stored
 }
 
 }  // namespace gr

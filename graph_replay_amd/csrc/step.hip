@@ -36,7 +36,7 @@ struct Layout {  // byte offsets into the workspace
   size_t mmeta, mmeta_bytes;          // mixed step inputs
   size_t rope_cos, rope_sin;
   size_t resid[2], h, qkv, q, attn_o, d_o, d_d, act;
-  size_t attn_part, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
+  size_t attn_part, attn_cnt, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
   size_t samp_topk, samp_topp, samp_filt;
   size_t total;
   int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
@@ -68,6 +68,7 @@ struct step_ctx {
   std::vector<int> kernels_per_mbucket;
   int last_mixed_bucket = 0;                    // bucket of the last mixed step (0: exact-size plan)
   int last_bucket = 0;
+  gr::L2Prefetch pf{};                // weights the next attention launch prefetches (pf.n == 0: none)
   int launches = 0;                   // kernels enqueued by the current plan run
   uint64_t step_count = 0;            // Philox step counter the next host-fed step starts from
   bool have_batch = false;
@@ -112,11 +113,11 @@ int elem_bytes(int dtype) { return dtype == STEP_F32 ? 4 : 2; }
 
 enum KernelKind {
   KK_QKV = 0, KK_QKV_POST, KK_ATTN, KK_O, KK_GATE_UP, KK_DOWN, KK_LM_HEAD, KK_NORM, KK_SAMPLE, KK_PREFILL_ATTN,
-  KK_ATTN_COMBINE, KK_SAMPLE_FILTER, KK_COUNT
+  KK_SAMPLE_FILTER, KK_COUNT
 };
 const char* const kKindNames[KK_COUNT] = {"qkv_proj", "qknorm_rope_kvwrite", "attn_decode", "o_proj", "gate_up_silu",
                                           "down_proj", "lm_head", "add_rmsnorm", "sample", "attn_prefill",
-                                          "attn_combine", "sample_filter"};
+                                          "sample_filter"};
 
 // Called before every kernel launch: counts it and, while profiling, marks its start.
 // Profile events for the next launch: set by pre_launch during a profile step, taken by launch().
@@ -165,6 +166,8 @@ int split_tokens_for(int rows, int max_len) {
 
 // copies of split-K partial outputs the workspace holds
 constexpr int kMaxKsplit = 8;
+// weight-prefetch blocks appended to an attention launch (about one per CU)
+constexpr int kPrefetchBlocks = 256;
 
 bool compute_layout(const step_config& c, Layout& L) {
   const int H = c.hidden, d = c.head_dim, nq = c.q_heads, nkv = c.kv_heads, I = c.intermediate;
@@ -213,6 +216,7 @@ bool compute_layout(const step_config& c, Layout& L) {
   }
   L.max_splits_alloc = 0;
   L.attn_part = take(sizeof(float) * part_rows_splits * nq * (d + 2));
+  L.attn_cnt = take(sizeof(unsigned) * static_cast<size_t>(TM) * nkv);
   const int nch_max = (c.vocab + 1023) / 1024;
   L.samp_val = take(sizeof(float) * static_cast<size_t>(LM) * nch_max);
   L.samp_idx = take(sizeof(int) * static_cast<size_t>(LM) * nch_max);
@@ -328,6 +332,29 @@ int gemv_kc(int MT, int eb) {
   return (32768 / (MT * eb)) / (64 * epv) * (64 * epv);
 }
 
+// Launch geometry of k_gemv: MT token rows per block row, rows_pw weight rows per wave (the largest
+// that still gives >= 512 blocks), per_block weight rows per block (EPI_SILU: gate rows, each with
+// its up row), u vectors per lane in flight; grid (nblk, ygrid), block x reading the weight rows
+// [x * per_block, (x + 1) * per_block) (and the matching up rows).
+struct GemvGeom { int MT, rows_pw, per_block, u, nblk, ygrid; };
+GemvGeom gemv_geom(int M, int N, int K, int epi, int eb) {
+  GemvGeom g{};
+  g.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  g.ygrid = (M + g.MT - 1) / g.MT;
+  g.rows_pw = (g.MT >= 8) ? 4 : 8;   // 8 x 8 accumulators would spill
+  const int min_rows = (epi == EPI_SILU) ? 2 : 1;
+  const int nvl = (std::min(K, gemv_kc(g.MT, eb)) / (16 / eb) + 63) / 64;   // vectors per lane per row
+  auto per_block = [&](int rpw) { return 4 * ((epi == EPI_SILU) ? rpw / 2 : rpw); };
+  while (g.rows_pw > min_rows) {
+    if (static_cast<long>((N + per_block(g.rows_pw) - 1) / per_block(g.rows_pw)) * g.ygrid >= 512) break;
+    g.rows_pw /= 2;
+  }
+  g.per_block = per_block(g.rows_pw);
+  g.u = g.rows_pw == 1 ? (nvl > 4 ? 8 : 4) : g.rows_pw == 2 ? (nvl > 2 ? 4 : 2) : 2;
+  g.nblk = (N + g.per_block - 1) / g.per_block;
+  return g;
+}
+
 template <class T>
 int run_linear(step_ctx* ctx, const Lin& l) {
   GemmArgs a{};
@@ -341,28 +368,16 @@ int run_linear(step_ctx* ctx, const Lin& l) {
   const bool is_f32 = std::is_same<T, F32>::value;
   pre_launch(ctx, l.kind);
   if (l.M <= 8 || is_f32 || l.norm) {
-    const int MT = l.M <= 1 ? 1 : l.M <= 2 ? 2 : l.M <= 4 ? 4 : 8;
-    const int units = l.N;  // output columns (EPI_SILU: gate/up pairs)
-    const int ygrid = (l.M + MT - 1) / MT;
-    int rows_pw = (MT >= 8) ? 4 : 8;   // 8 x 8 accumulators would spill
-    const int min_rows = (l.epi == EPI_SILU) ? 2 : 1;
     const int eb = static_cast<int>(sizeof(typename T::S));
-    const int nvl = (std::min(l.K, gemv_kc(MT, eb)) / (16 / eb) + 63) / 64;   // vectors per lane per row
-    // largest rows-per-wave that still gives >= 512 blocks
-    while (rows_pw > min_rows) {
-      const int per_block = 4 * ((l.epi == EPI_SILU) ? rows_pw / 2 : rows_pw);
-      if (static_cast<long>((units + per_block - 1) / per_block) * ygrid >= 512) break;
-      rows_pw /= 2;
-    }
-    const int per_block = 4 * ((l.epi == EPI_SILU) ? rows_pw / 2 : rows_pw);
-    const int u = rows_pw == 1 ? (nvl > 4 ? 8 : 4) : rows_pw == 2 ? (nvl > 2 ? 4 : 2) : 2;
+    const GemvGeom g = gemv_geom(l.M, l.N, l.K, l.epi, eb);
+    const int MT = g.MT;
     if (l.norm && (l.K > 2048 || l.K > gemv_kc(MT, eb))) e = hipErrorInvalidValue;   // one-chunk prologue only
-    dim3 grid((units + per_block - 1) / per_block, ygrid);
+    dim3 grid(g.nblk, g.ygrid);
     if (!(l.norm && (l.K > 2048 || l.K > gemv_kc(MT, eb)))) switch (MT) {
-      case 1: e = launch_gemv_mt<T, 1>(a, l.epi, rows_pw, u, grid, s); break;
-      case 2: e = launch_gemv_mt<T, 2>(a, l.epi, rows_pw, u, grid, s); break;
-      case 4: e = launch_gemv_mt<T, 4>(a, l.epi, rows_pw, u, grid, s); break;
-      default: e = launch_gemv_mt<T, 8>(a, l.epi, rows_pw, u, grid, s); break;
+      case 1: e = launch_gemv_mt<T, 1>(a, l.epi, g.rows_pw, g.u, grid, s); break;
+      case 2: e = launch_gemv_mt<T, 2>(a, l.epi, g.rows_pw, g.u, grid, s); break;
+      case 4: e = launch_gemv_mt<T, 4>(a, l.epi, g.rows_pw, g.u, grid, s); break;
+      default: e = launch_gemv_mt<T, 8>(a, l.epi, g.rows_pw, g.u, grid, s); break;
     }
   } else if constexpr (!std::is_same<T, F32>::value) {
     if (l.M <= 32) {
@@ -456,13 +471,6 @@ hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream
   return hipGetLastError();
 }
 
-template <class T, int D>
-hipError_t launch_combine(step_ctx* ctx, int rows, const AttnRowsArgs& a) {
-  launch((k_attn_combine<T, D>), dim3(rows, a.nq), dim3(D), sizeof(float) * 2 * a.max_splits, ctx->stream,
-                     a.nq, a.row_ids, a.seq_lens, a.split_tokens, a.max_splits, a.partials, a.out);
-  return hipGetLastError();
-}
-
 // Row attention over `rows` query rows; max_len bounds the keys of any row (sets the split grid).
 // q == nullptr: decode rows, whose QK-norm + RoPE + KV write run inside the attention kernel from
 // the n_qkv fp32 partial outputs of the QKV projection.
@@ -490,18 +498,20 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.num_blocks = c.num_blocks;
   a.out = out;
   a.partials = reinterpret_cast<float*>(ctx->ws + Ly.attn_part);
+  a.split_cnt = reinterpret_cast<unsigned*>(ctx->ws + Ly.attn_cnt);
   a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
   const int G = c.q_heads / c.kv_heads;
+  if (rows > Ly.TM) return fail(ctx, STEP_EINVAL, "attention over %d rows exceeds the workspace's %d", rows, Ly.TM);
   dim3 grid(rows, c.kv_heads, a.max_splits);
+  if (ctx->pf.n > 0) {
+    a.pf = ctx->pf;
+    const int plane = rows * c.kv_heads;
+    grid.z += (kPrefetchBlocks + plane - 1) / plane;
+  }
   pre_launch(ctx, KK_ATTN);
   hipError_t e = (c.head_dim == 64) ? launch_attn_rows_d<T, 64>(a, G, grid, ctx->stream)
                                     : launch_attn_rows_d<T, 128>(a, G, grid, ctx->stream);
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (a.max_splits > 1) {
-    pre_launch(ctx, KK_ATTN_COMBINE);
-    e = (c.head_dim == 64) ? launch_combine<T, 64>(ctx, rows, a) : launch_combine<T, 128>(ctx, rows, a);
-    if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention combine launch failed: %s", hipGetErrorString(e));
-  }
   return STEP_OK;
 }
 
@@ -593,6 +603,29 @@ DecodeMeta decode_meta(char* base, int MB, int W) {
 // attn(layer) enqueues the attention of one layer (rows or packed prefill + rows).
 // fused_rope: the attention kernel does QK-norm + RoPE + KV write itself (decode rows, one token per
 // request); otherwise k_qkv_post runs first so every chunk token's K and V are in the pool.
+// Prefetch targets of layer l's attention launch: the gate|up, down and O GEMVs that follow it, as
+// k_gemv lays them out for M rows (one block row: M <= 8).
+template <class T>
+void set_prefetch(step_ctx* ctx, int l, int M) {
+  const step_config& c = ctx->cfg;
+  const int eb = static_cast<int>(sizeof(typename T::S));
+  const int H = c.hidden, I = c.intermediate, QD = c.q_heads * c.head_dim;
+  struct Tg { const void* w; int N, K, epi; } tg[gr::kPrefetchTargets] = {
+      {ctx->gate_up_w[l], I, H, EPI_SILU}, {ctx->down_w[l], H, I, EPI_F32}, {ctx->o_w[l], H, QD, EPI_F32}};
+  gr::L2Prefetch& p = ctx->pf;
+  p = gr::L2Prefetch{};
+  for (int t = 0; t < gr::kPrefetchTargets; ++t) {
+    const GemvGeom g = gemv_geom(M, tg[t].N, tg[t].K, tg[t].epi, eb);
+    p.base[t] = static_cast<const char*>(tg[t].w);
+    p.row_bytes[t] = tg[t].K * eb;
+    p.pb[t] = g.per_block;
+    p.n_rows[t] = tg[t].N;
+    p.up_off[t] = (tg[t].epi == EPI_SILU) ? tg[t].N : 0;
+    p.nblk[t] = g.nblk;
+  }
+  p.n = gr::kPrefetchTargets;
+}
+
 template <class T, class AttnFn>
 int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* slot, int n_logits, const int* logit_rows,
                bool fused_rope, AttnFn attn) {
@@ -634,7 +667,11 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
     }
     TRY(run_linear<T>(ctx, lin));
     if (!fused_rope) TRY(run_qkv_post<T>(ctx, l, M, n_qkv, qkv_stride, pos, slot));
-    TRY(attn(l, n_qkv));
+    // decode rows: the attention launch also pulls this layer's remaining weights into L2
+    if (fused_rope && c.weight_prefetch && M <= 8) set_prefetch<T>(ctx, l, M);
+    const int ar = attn(l, n_qkv);
+    ctx->pf.n = 0;
+    TRY(ar);
     // ---- O projection
     int n_o = 1;
     Lin lo{};

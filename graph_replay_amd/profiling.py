@@ -78,8 +78,6 @@ def _copy_factor(d: str) -> float:
 def _kind_bs1(name: str, grid: int) -> str:
     if "k_attn_rows" in name:
         return "attn_decode"
-    if "k_attn_combine" in name:
-        return "attn_combine"
     if "k_sample" in name:
         return "sample"
     if "k_gemv<gr::BF16, 1, 8, 2>" in name:

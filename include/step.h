@@ -95,6 +95,11 @@ typedef struct {
    * Top-p only looks at tokens within 30 of the largest z; a p that needs more keeps the whole
    * top-k set (the mass left out is below 2e-8). */
   int32_t sampling_filters;
+  /* 1: decode steps of at most 8 rows append blocks to each layer's attention launch that load the
+   * weights of the layer's O, gate|up and down projections into the L2 of the XCD whose GEMV blocks
+   * will read them (HBM is otherwise idle during attention). A performance hint only: results are
+   * the same bits either way. 0: off. */
+  int32_t weight_prefetch;
 } step_config;
 
 typedef struct {
