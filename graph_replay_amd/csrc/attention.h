@@ -246,35 +246,42 @@ __device__ inline void attn_finish(const AttnRowsArgs& a, int row, int prow, int
   if (threadIdx.x == 0) s_last = arrive_last(a.split_cnt + static_cast<size_t>(prow) * a.nkv + g, nsplit);
   __syncthreads();
   if (!s_last) return;
-  // One round of loads: each split's (max, sum) as one 8-byte load, and the first kOB splits of each
-  // thread's output dim, all in flight together; then the sums in split order. Block = 256 threads.
-  constexpr int kOB = 32;
+  // One round of loads: the first kOB splits of each of the thread's NO output dims, and each
+  // split's (max, sum) as one 8-byte load, all in flight together; then the sums in split order.
+  // Block = 256 threads. (Fixed trip counts throughout: around a loop the compiler would drain the
+  // outstanding loads first.)
+  constexpr int NO = (G * D + 255) / 256;
+  constexpr int kOB = NO == 1 ? 32 : (NO == 2 ? 16 : 8);
+  constexpr int NML = (G * kMaxSplits + 255) / 256;
   const int nml = G * nsplit;
-  auto ml_ptr = [&](int m) { return part + (static_cast<size_t>(m / nsplit) * a.max_splits + m % nsplit) * (D + 2); };
   const int tid = threadIdx.x;
-  for (int i0 = 0; i0 < G * D; i0 += blockDim.x) {
-    const int i = i0 + tid;
+  float ov[NO][kOB];
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    const int i = tid + 256 * o;
+    const bool act = i < G * D;
+    const float* pj = part + static_cast<size_t>(act ? i / D : 0) * a.max_splits * (D + 2) + 2 + i % D;
+#pragma unroll
+    for (int k = 0; k < kOB; ++k) ov[o][k] = (act && k < nsplit) ? ld_dev(pj + static_cast<size_t>(k) * (D + 2)) : 0.f;
+  }
+  float2 mlv[NML];
+#pragma unroll
+  for (int r = 0; r < NML; ++r) {
+    const int m = tid + 256 * r;
+    if (m < nml) mlv[r] = ld_dev2(part + (static_cast<size_t>(m / nsplit) * a.max_splits + m % nsplit) * (D + 2));
+  }
+#pragma unroll
+  for (int r = 0; r < NML; ++r) {
+    const int m = tid + 256 * r;
+    if (m < nml) { s_m[m / nsplit][m % nsplit] = mlv[r].x; s_l[m / nsplit][m % nsplit] = mlv[r].y; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    const int i = tid + 256 * o;
     const bool act = i < G * D;
     const int j = act ? i / D : 0, dd = i % D;
     const float* pj = part + static_cast<size_t>(j) * a.max_splits * (D + 2) + 2 + dd;
-    float ov[kOB];
-#pragma unroll
-    for (int k = 0; k < kOB; ++k) ov[k] = (act && k < nsplit) ? ld_dev(pj + static_cast<size_t>(k) * (D + 2)) : 0.f;
-    if (i0 == 0) {
-      // (unrolled: a loop here would make the compiler drain the O loads before entering it)
-      float2 v[(G * kMaxSplits + 255) / 256];
-#pragma unroll
-      for (int r = 0; r < (G * kMaxSplits + 255) / 256; ++r) {
-        const int m = tid + 256 * r;
-        if (m < nml) v[r] = ld_dev2(ml_ptr(m));
-      }
-#pragma unroll
-      for (int r = 0; r < (G * kMaxSplits + 255) / 256; ++r) {
-        const int m = tid + 256 * r;
-        if (m < nml) { s_m[m / nsplit][m % nsplit] = v[r].x; s_l[m / nsplit][m % nsplit] = v[r].y; }
-      }
-      __syncthreads();
-    }
     float M = -INFINITY;
     for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, s_m[j][s2]);
     float Ls = 0.f, O = 0.f;
@@ -282,14 +289,14 @@ __device__ inline void attn_finish(const AttnRowsArgs& a, int row, int prow, int
       if (s0) {
 #pragma unroll
         for (int k = 0; k < kOB; ++k)
-          ov[k] = (act && s0 + k < nsplit) ? ld_dev(pj + static_cast<size_t>(s0 + k) * (D + 2)) : 0.f;
+          ov[o][k] = (act && s0 + k < nsplit) ? ld_dev(pj + static_cast<size_t>(s0 + k) * (D + 2)) : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < kOB; ++k) {
         if (s0 + k < nsplit) {
           const float f = __expf(s_m[j][s0 + k] - M);
           Ls += s_l[j][s0 + k] * f;
-          O += ov[k] * f;
+          O += ov[o][k] * f;
         }
       }
     }
