@@ -2,10 +2,12 @@
 
 One "step" is one whole decode step (every layer, LM head, sampling, device-side advance), replayed
 as the bucket's hipGraph. The primary line is batch 1 with a 1,024-token context built by a real
-prefill; the same JSON line carries the batch-32 workload (contexts uniform in [128, 2048], shuffled
-paged KV, Gumbel-max at T = 1) under "bs32". Inputs are resident in HBM before the timed region.
+prefill, run as one persistent kernel plus the sampler (--no-persistent: the multi-kernel graph);
+the same JSON line carries the batch-32 workload (contexts uniform in [128, 2048], shuffled paged
+KV, Gumbel-max at T = 1) under "bs32". Inputs are resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-bs32] [--no-mixed] [--no-cpu]
+                    [--no-persistent]
 
 The line also carries the Qwen2.5-1.5B-shape mixed step (prefill chunks + decode rows, 544 packed
 tokens) under "mixed": the bucketed plan replayed as a hipGraph against the exact-size eager plan.
@@ -53,6 +55,8 @@ def kind_bytes(shape, rows: int, seq_lens_sum: int, weight_prefetch: bool = Fals
         "qknorm_rope_kvwrite": rows * (qkv * 4 + nq * d * 4 + 2 * nkv * d * eb),
         "sample": rows * V * 4,
         "add_rmsnorm": rows * H * (4 + 4 + 4 + eb),
+        # the whole single-row step in one kernel: every weight, the KV read, the logits written
+        "decode_step_persistent": step_bytes(shape, seq_lens_sum) + rows * V * 4,
     }
 
 
@@ -109,14 +113,35 @@ def roofline_from_profile(shape, dec, rows: int, seq_lens_sum: int, weight_prefe
             "profile_sum_us": round(sum(ms for _, ms in prof) * 1e3, 1), "kernels": table}
 
 
-def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefetch: bool = True):
+def phase_breakdown(st, layers: int) -> dict:
+    """Mean microseconds per layer between the phase stamps of a profiled persistent step (block 0's
+    view): each interval ends when that phase's input has arrived (or, for attention, when block 0's
+    attention item is done)."""
+    names = ["to_qkv_in", "to_attn_done", "to_merge_done", "to_o_in", "to_mlp_in", "to_down_in"]
+    acc = {n: 0.0 for n in names}
+    for l in range(layers):
+        prev = st[0] if l == 0 else st[8 * (l - 1) + 6]
+        for k, n in enumerate(names):
+            cur = st[8 * l + k + 1]
+            acc[n] += cur - prev
+            prev = cur
+    out = {n: round(v / layers, 2) for n, v in acc.items()}
+    out["final_norm_in"] = round(st[8 * layers + 1] - st[8 * (layers - 1) + 6], 2)
+    out["lm_head"] = round(st[8 * layers + 2] - st[8 * layers + 1], 2)
+    out["total"] = round(st[8 * layers + 2], 2)
+    return out
+
+
+def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefetch: bool = True,
+            persistent: bool = False):
     import graph_replay_amd as g
     torch = __import__("torch")
     total = ctx_len + 1 + warmup + steps + 2            # positions used, profile step included
     table = synth.block_tables([total], -(-total // 16) + 2, 1002, shuffled=False)[0]
     nb = len(table) + 2
     dec = g.Decoder(shape, W, num_blocks=nb, max_blocks_per_seq=len(table), max_position=total + 16, max_batch=1,
-                    buckets=[1], max_tokens=ctx_len, max_reqs=1, max_logit_rows=1, weight_prefetch=weight_prefetch)
+                    buckets=[1], max_tokens=ctx_len, max_reqs=1, max_logit_rows=1, weight_prefetch=weight_prefetch,
+                    persistent_decode=persistent)
     bt = np.asarray([table], np.int32)
     prompt = synth.tokens(ctx_len, shape.vocab, 1002)
     pos = np.arange(ctx_len, dtype=np.int32)
@@ -138,6 +163,11 @@ def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefe
     ms_step = ms / steps
     roof = roofline_from_profile(shape, dec, 1, start_len + steps, weight_prefetch)
     roof["traffic"] = measured_traffic("qwen3-0.6b_bs1", roof["kernel"])
+    if persistent:
+        st = dec.phase_stamps()
+        if st is not None:
+            roof["phases_us"] = phase_breakdown(st, shape.layers)
+    dec.device_status()
     out = {
         "tok_s": steps / (ms * 1e-3), "ms_per_step": ms_step, "bytes_per_step": int(nbytes),
         "step_hbm_GBps": nbytes / (ms_step * 1e-3) / 1e9, "kernels_per_step": dec.kernels_per_decode(1),
@@ -317,6 +347,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-weight-prefetch", action="store_true",
                     help="batch-1 step without the L2 weight prefetch in the attention launches")
+    ap.add_argument("--no-persistent", action="store_true",
+                    help="batch-1 step as the multi-kernel graph instead of one persistent kernel (plus the sampler)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -349,7 +381,8 @@ def main():
     if args.workload == "mixed":
         print(json.dumps({"metric": METRIC, **run_mixed()}), flush=True)
         return
-    r1 = run_bs1(shape, W, args.steps, warmup, weight_prefetch=not args.no_weight_prefetch)
+    r1 = run_bs1(shape, W, args.steps, warmup, weight_prefetch=not args.no_weight_prefetch,
+                 persistent=not args.no_persistent)
     r32 = None if (args.no_bs32 or args.workload == "bs1") else run_bs32(shape, W, args.steps, warmup)
     rmix = None if (args.no_mixed or args.workload == "bs1") else run_mixed()
     cpu = None if args.no_cpu else cpu_baseline(shape, W)
@@ -358,8 +391,11 @@ def main():
         "warmup": warmup, "ms_per_step": round(r1["ms_per_step"], 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "qwen3-0.6b-bf16-decode-bs1-ctx1024", "batch": 1, "context": 1024,
-                   "decode_steps": args.steps, "graph": "one hipGraph replay per step",
-                   "kernels_per_step": r1["kernels_per_step"], "weight_prefetch": not args.no_weight_prefetch},
+                   "decode_steps": args.steps,
+                   "graph": "one hipGraph replay per step" + ("" if args.no_persistent else
+                                                               " (one persistent kernel + the sampler)"),
+                   "kernels_per_step": r1["kernels_per_step"], "weight_prefetch": not args.no_weight_prefetch,
+                   "persistent_decode": not args.no_persistent},
         "step_hbm": {"bytes_per_step": r1["bytes_per_step"], "achieved": round(r1["step_hbm_GBps"], 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r1["step_hbm_frac"], 4)},
         "roofline": r1["roofline"],

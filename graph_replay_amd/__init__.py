@@ -97,6 +97,10 @@ def step_sample(ctx, d_logits: int, rows: int, ld: int, vocab: int, h_temperatur
     _raise(rc, ctx)
 
 
+def step_device_status(ctx) -> None:
+    _raise(_lib.load().step_device_status(ctx), ctx)
+
+
 def step_destroy(ctx) -> None:
     if ctx:
         _lib.load().step_destroy(ctx)
@@ -119,7 +123,7 @@ class Decoder:
                  max_batch: int = 1, buckets: Optional[Sequence[int]] = None, max_tokens: int = 0,
                  max_reqs: int = 0, max_logit_rows: int = 0, use_graphs: bool = True, history: bool = False,
                  mixed_buckets: Optional[Sequence[int]] = None, sampling_filters: bool = False,
-                 weight_prefetch: bool = True,
+                 weight_prefetch: bool = True, persistent_decode: bool = False,
                  device: str = "cuda:0"):
         import torch
         lib = _lib.load()
@@ -203,6 +207,7 @@ class Decoder:
             cfg.mixed_buckets[i] = int(b)
         cfg.sampling_filters = int(sampling_filters)
         cfg.weight_prefetch = int(weight_prefetch)
+        cfg.persistent_decode = int(persistent_decode)
         self.cfg = cfg
         self.buckets = buckets
         nbytes = step_workspace_bytes(cfg)
@@ -278,6 +283,19 @@ class Decoder:
             _raise(n, self.ctx)
         n = min(n, max_kernels)
         return [(lib.step_kernel_kind_name(int(kind[i])).decode(), float(ms[i])) for i in range(n)]
+
+    def device_status(self) -> None:
+        """Raise StepError if a wait inside a persistent decode step gave up (waits for the stream)."""
+        step_device_status(self.ctx)
+
+    def phase_stamps(self):
+        """Phase timestamps (us) of the last profiled persistent step, or None."""
+        lib = _lib.load()
+        buf = (C.c_double * 512)()
+        n = lib.step_phase_stamps(self.ctx, 512, buf)
+        if n < 0:
+            _raise(n, self.ctx)
+        return [buf[i] for i in range(min(n, 512))] if n > 0 else None
 
     def last_bucket(self) -> int:
         return int(_lib.load().step_last_bucket(self.ctx))

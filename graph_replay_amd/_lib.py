@@ -24,7 +24,8 @@ class StepConfig(C.Structure):
         ("buckets", C.c_int32 * MAX_BUCKETS), ("use_graphs", C.c_int32),
         ("num_mixed_buckets", C.c_int32), ("mixed_buckets", C.c_int32 * MAX_BUCKETS),
         ("sampling_filters", C.c_int32),
-        ("weight_prefetch", C.c_int32)]
+        ("weight_prefetch", C.c_int32),
+        ("persistent_decode", C.c_int32)]
 
 
 class StepWeights(C.Structure):
@@ -67,6 +68,8 @@ EXPORTS = {
     "step_kernels_per_decode": (C.c_int, [P, C.c_int32]),
     "step_last_mixed_bucket": (C.c_int, [P]),
     "step_last_error": (C.c_char_p, [P]),
+    "step_device_status": (C.c_int, [P]),
+    "step_phase_stamps": (C.c_int, [P, C.c_int32, C.POINTER(C.c_double)]),
     "step_destroy": (None, [P]),
 }
 

@@ -20,6 +20,7 @@
 #include "attention.h"
 #include "common.h"
 #include "gemm.h"
+#include "persistent.h"
 #include "prefill.h"
 #include "sample.h"
 #include "../../include/step.h"
@@ -38,6 +39,9 @@ struct Layout {  // byte offsets into the workspace
   size_t resid[2], h, qkv, q, attn_o, d_o, d_d, act;
   size_t attn_part, attn_cnt, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
   size_t samp_topk, samp_topp, samp_filt;
+  // persistent decode step: per-layer pointers, tagged hand-off words, control words, stamps
+  size_t p_lw, p_qkv, p_part, p_attn, p_o, p_act, p_down, p_ctl, p_stamps;
+  int p_splits;                       // attention splits per KV head the partial words hold
   size_t total;
   int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
   int max_splits_alloc;               // splits per row the partial buffer holds (at 64 keys/split)
@@ -81,6 +85,11 @@ struct step_ctx {
   bool prof_on = false;
   std::vector<hipEvent_t> prof_ev, prof_ev_end;
   std::vector<int> prof_kind;
+  // persistent single-row decode step (persistent_decode): blocks per launch (0: not in use),
+  // whether the next launch records phase stamps, and the stamps of the last profiled step
+  int p_nb = 0;
+  bool p_stamp_next = false;
+  std::vector<unsigned long long> p_stamps;
   std::string err;
   bool dead = false;
 };
@@ -113,11 +122,11 @@ int elem_bytes(int dtype) { return dtype == STEP_F32 ? 4 : 2; }
 
 enum KernelKind {
   KK_QKV = 0, KK_QKV_POST, KK_ATTN, KK_O, KK_GATE_UP, KK_DOWN, KK_LM_HEAD, KK_NORM, KK_SAMPLE, KK_PREFILL_ATTN,
-  KK_SAMPLE_FILTER, KK_COUNT
+  KK_SAMPLE_FILTER, KK_PERSIST, KK_COUNT
 };
 const char* const kKindNames[KK_COUNT] = {"qkv_proj", "qknorm_rope_kvwrite", "attn_decode", "o_proj", "gate_up_silu",
                                           "down_proj", "lm_head", "add_rmsnorm", "sample", "attn_prefill",
-                                          "sample_filter"};
+                                          "sample_filter", "decode_step_persistent"};
 
 // Called before every kernel launch: counts it and, while profiling, marks its start.
 // Profile events for the next launch: set by pre_launch during a profile step, taken by launch().
@@ -228,6 +237,18 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.samp_topp = L.samp_topk + sizeof(int) * static_cast<size_t>(LM);
   L.samp_filt = take(sizeof(uint2) * static_cast<size_t>(std::max(LM, MB)));
   L.samp_rng = take(16);
+  if (c.persistent_decode) {
+    L.p_splits = (c.max_position + gr::kPSplit - 1) / gr::kPSplit;
+    L.p_lw = take(sizeof(gr::PLayer) * static_cast<size_t>(c.layers));
+    L.p_qkv = take(sizeof(uint64_t) * static_cast<size_t>(QKV));
+    L.p_part = take(sizeof(uint64_t) * static_cast<size_t>(nq) * L.p_splits * (d + 2));
+    L.p_attn = take(sizeof(uint64_t) * static_cast<size_t>(nq) * d);
+    L.p_o = take(sizeof(uint64_t) * static_cast<size_t>(H));
+    L.p_act = take(sizeof(uint64_t) * static_cast<size_t>(I));
+    L.p_down = take(sizeof(uint64_t) * static_cast<size_t>(H));
+    L.p_ctl = take(4 * sizeof(unsigned));          // epoch | done | err | spare
+    L.p_stamps = take(sizeof(unsigned long long) * gr::kPStamps);
+  }
   L.total = off;
   (void)RM;
   return true;
@@ -272,6 +293,20 @@ int validate_config(step_ctx* ctx, const step_config* c) {
     if (c->mixed_buckets[i] <= 0 || c->mixed_buckets[i] > c->max_tokens ||
         (i && c->mixed_buckets[i] <= c->mixed_buckets[i - 1]))
       return fail(ctx, STEP_EINVAL, "mixed buckets must be ascending and in [1, max_tokens]");
+  }
+  if (c->persistent_decode != 0 && c->persistent_decode != 1) return fail(ctx, STEP_EINVAL, "persistent_decode must be 0 or 1");
+  if (c->persistent_decode) {
+    if (c->dtype == STEP_F32 || c->head_dim != 128 || c->hidden != 1024 || c->q_heads * c->head_dim != 2048 ||
+        c->intermediate != 3072 || G != 2)
+      return fail(ctx, STEP_EUNSUPPORTED,
+                  "persistent_decode is built for 16-bit dtypes at hidden 1024, 16 x 128 query dims, intermediate "
+                  "3072 and 2 query heads per KV head");
+    if (c->layers > gr::kPMaxLayers)
+      return fail(ctx, STEP_EUNSUPPORTED, "persistent_decode holds at most %d layers", gr::kPMaxLayers);
+    const int max_keys = std::min(gr::kPSplit * gr::kPMaxSplits, gr::kPSplit * gr::kPBlocks / c->kv_heads);
+    if (c->max_position > max_keys)
+      return fail(ctx, STEP_EUNSUPPORTED, "persistent_decode needs max_position <= %d", max_keys);
+    if (c->buckets[0] != 1) return fail(ctx, STEP_EINVAL, "persistent_decode serves bucket 1, which the buckets must hold");
   }
   return STEP_OK;
 }
@@ -753,12 +788,56 @@ MixedMeta mixed_meta(char* base, const Layout& L, int W) {
   return m;
 }
 
+// The single-row decode step as one persistent kernel (see persistent.h), instantiated for the
+// widths validate_config admits: hidden 1024 (2 vectors per lane), 2048 query dims (4),
+// intermediate 3072 (6), 2 query heads per KV head.
+template <class T>
+int run_persist(step_ctx* ctx, const DecodeMeta& m) {
+  if constexpr (std::is_same<T, F32>::value) {
+    return fail(ctx, STEP_EUNSUPPORTED, "persistent decode has no fp32 kernel");
+  } else {
+    const step_config& c = ctx->cfg;
+    const Layout& L = ctx->lay;
+    char* ws = ctx->ws;
+    PersistArgs a{};
+    a.layers = c.layers; a.nq = c.q_heads; a.nkv = c.kv_heads; a.vocab = c.vocab; a.max_position = c.max_position;
+    a.eps = c.rms_eps; a.scale = 1.0f / std::sqrt(static_cast<float>(c.head_dim));
+    a.lw = reinterpret_cast<const PLayer*>(ws + L.p_lw);
+    a.embed = c_embed_of(ctx); a.lm_head = c_lm_head_of(ctx); a.final_norm = c_final_norm_of(ctx);
+    a.ids = m.ids; a.pos = m.pos; a.slot = m.slot; a.len = m.len; a.bt = m.bt;
+    a.bt_stride = c.max_blocks_per_seq; a.num_blocks = c.num_blocks; a.splits_alloc = L.p_splits;
+    a.rope_cos = reinterpret_cast<const float*>(ws + L.rope_cos);
+    a.rope_sin = reinterpret_cast<const float*>(ws + L.rope_sin);
+    a.x_qkv = reinterpret_cast<uint64_t*>(ws + L.p_qkv);
+    a.x_part = reinterpret_cast<uint64_t*>(ws + L.p_part);
+    a.x_attn = reinterpret_cast<uint64_t*>(ws + L.p_attn);
+    a.x_o = reinterpret_cast<uint64_t*>(ws + L.p_o);
+    a.x_act = reinterpret_cast<uint64_t*>(ws + L.p_act);
+    a.x_down = reinterpret_cast<uint64_t*>(ws + L.p_down);
+    unsigned* ctl = reinterpret_cast<unsigned*>(ws + L.p_ctl);
+    a.epoch = ctl; a.done = ctl + 1; a.err = reinterpret_cast<int*>(ctl + 2);
+    a.stamps = ctx->p_stamp_next ? reinterpret_cast<unsigned long long*>(ws + L.p_stamps) : nullptr;
+    a.logits = ctx->logits;
+    pre_launch(ctx, KK_PERSIST);
+    launch((k_persist_decode<T, 2, 4, 6, 2>), dim3(ctx->p_nb), dim3(gr::kPThreads), 0, ctx->stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ctx, STEP_EHIP, "persistent decode launch failed: %s", hipGetErrorString(e));
+    return STEP_OK;
+  }
+}
+
 template <class T>
 int run_decode(step_ctx* ctx, int B) {
   const step_config& c = ctx->cfg;
   const Layout& L = ctx->lay;
   const int W = c.max_blocks_per_seq;
   DecodeMeta m = decode_meta(ctx->ws + L.dmeta, c.max_batch, W);
+  if (ctx->p_nb > 0 && B == 1) {
+    TRY(run_persist<T>(ctx, m));
+    return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
+                      m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr,
+                      c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
+  }
   const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
   void* attn_o = ctx->ws + L.attn_o;
   (void)q;
@@ -1019,6 +1098,31 @@ extern "C" int step_init(const step_config* cfg, const step_weights* w, const st
       return hip_fail(e, "hipMemsetAsync(scratch)");
     if ((e = hipMemsetAsync(static_cast<char*>(ctx->v_pool[l]) + blk_bytes * (c.num_blocks - 1), 0, blk_bytes, s)) != hipSuccess)
       return hip_fail(e, "hipMemsetAsync(scratch)");
+  }
+  if (c.persistent_decode) {
+    // per-layer pointers for the persistent step, and its launch width: one block per CU of the
+    // 256 its tiling is built for (each of a block's four compute waves then owns one register tile
+    // of every projection, and each of the eight waves at least one LM-head row)
+    std::vector<PLayer> pl(c.layers);
+    for (int l = 0; l < c.layers; ++l)
+      pl[l] = PLayer{ctx->in_norm[l], ctx->qkv_w[l], ctx->qkv_b[l], ctx->q_norm[l], ctx->k_norm[l], ctx->o_w[l],
+                     ctx->post_norm[l], ctx->gate_up_w[l], ctx->down_w[l], ctx->k_pool[l], ctx->v_pool[l]};
+    if ((e = hipMemcpy(ctx->ws + ctx->lay.p_lw, pl.data(), sizeof(PLayer) * pl.size(), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(layer pointers)");
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return hip_fail(e, "hipDeviceGetAttribute");
+    const void* kfn = c.dtype == STEP_BF16 ? reinterpret_cast<const void*>(&k_persist_decode<BF16, 2, 4, 6, 2>)
+                                           : reinterpret_cast<const void*>(&k_persist_decode<F16, 2, 4, 6, 2>);
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, gr::kPThreads, 0)) != hipSuccess)
+      return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (per_cu < 1) return bail(fail(ctx, STEP_EUNSUPPORTED, "persistent decode kernel does not fit on a CU"));
+    if (cus < gr::kPBlocks)
+      return bail(fail(ctx, STEP_EUNSUPPORTED, "persistent decode needs %d CUs (one block each), the device has %d",
+                       gr::kPBlocks, cus));
+    if (c.vocab < 8 * gr::kPBlocks) return bail(fail(ctx, STEP_EUNSUPPORTED, "persistent decode needs vocab >= %d", 8 * gr::kPBlocks));
+    ctx->p_nb = gr::kPBlocks;
   }
   fill_decode_padding(c, ctx->h_stage[0]);
   if ((e = hipMemcpyAsync(ctx->ws + ctx->lay.dmeta, ctx->h_stage[0], ctx->lay.dmeta_bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -1357,12 +1461,23 @@ extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_
   ctx->prof_kind.assign(ctx->prof_ev.size(), -1);
   hipLaunchKernelGGL(k_hold, dim3(1), dim3(64), 0, ctx->stream, 1000);
   HIPCHK(ctx, hipGetLastError());
+  const bool stamps = ctx->p_nb > 0 && ctx->last_bucket == 1;
+  if (stamps) {
+    HIPCHK(ctx, hipMemsetAsync(ctx->ws + ctx->lay.p_stamps, 0, sizeof(unsigned long long) * gr::kPStamps, ctx->stream));
+  }
   ctx->launches = 0;
   ctx->prof_on = true;
+  ctx->p_stamp_next = stamps;
   const int rc = run_decode_any(ctx, ctx->last_bucket);
   ctx->prof_on = false;
+  ctx->p_stamp_next = false;
   g_prof_next = ProfSlot{};
   if (rc != STEP_OK) return rc;
+  if (stamps) {
+    ctx->p_stamps.assign(gr::kPStamps, 0ull);
+    HIPCHK(ctx, hipMemcpyAsync(ctx->p_stamps.data(), ctx->ws + ctx->lay.p_stamps, sizeof(unsigned long long) * gr::kPStamps,
+                               hipMemcpyDeviceToHost, ctx->stream));
+  }
   const int n = std::min(ctx->launches, max_kernels);
   HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
   for (int i = 0; i < n; ++i) {
@@ -1373,6 +1488,29 @@ extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_
   }
   ctx->step_count++;
   return ctx->launches;
+}
+
+extern "C" int step_phase_stamps(const step_ctx* ctx, int32_t max_stamps, double* h_us) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  if (max_stamps < 0 || (max_stamps > 0 && !h_us)) return STEP_EINVAL;
+  if (ctx->p_stamps.empty()) return 0;
+  const int n = std::min(max_stamps, gr::kPStamps);
+  const unsigned long long t0 = ctx->p_stamps[0];
+  for (int i = 0; i < n; ++i)
+    h_us[i] = ctx->p_stamps[i] ? static_cast<double>(ctx->p_stamps[i] - t0) * 0.01 : -1.0;   // 100 MHz clock
+  return gr::kPStamps;
+}
+
+extern "C" int step_device_status(step_ctx* ctx) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  if (ctx->p_nb == 0) return STEP_OK;
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  int* err = reinterpret_cast<int*>(ctx->ws + ctx->lay.p_ctl) + 2;
+  int v = 0;
+  HIPCHK(ctx, hipMemcpy(&v, err, sizeof v, hipMemcpyDeviceToHost));
+  if (v == 0) return STEP_OK;
+  HIPCHK(ctx, hipMemset(err, 0, sizeof v));
+  return fail(ctx, STEP_EHIP, "persistent decode step: a wait gave up (site %d); that step's outputs are invalid", v);
 }
 
 extern "C" const char* step_kernel_kind_name(int32_t kind) {

@@ -100,6 +100,17 @@ typedef struct {
    * will read them (HBM is otherwise idle during attention). A performance hint only: results are
    * the same bits either way. 0: off. */
   int32_t weight_prefetch;
+  /* 1: decode steps of one row (bucket 1) run as ONE persistent kernel of one block per CU plus the
+   * sampler, instead of about five kernels per layer: "Removing overhead: fusion, graphs and async
+   * scheduling", section "Fewer, larger matmuls" (fewer, larger kernels) taken to a single launch,
+   * "Fast decode: syncs, CUDA graphs and compilation", section "Where the time goes" (a batch-1 step
+   * of ~600 small kernels is bound by their overhead, not by bandwidth). The phases of a layer hand
+   * their outputs to the next through tagged device-memory words inside the kernel. Same results
+   * as the multi-kernel step up to rounding order. Built for 16-bit dtypes at hidden 1024, 16 x 128
+   * query dims, intermediate 3072, 2 query heads per KV head (Qwen3-0.6B's widths; any layer count
+   * and vocabulary) and max_position <= 8192; other configurations get STEP_EUNSUPPORTED at
+   * step_init. buckets[0] must be 1. Other buckets keep the multi-kernel step. 0: off. */
+  int32_t persistent_decode;
 } step_config;
 
 typedef struct {
@@ -197,6 +208,17 @@ int step_sample(step_ctx *ctx, const float *d_logits, int32_t rows, int32_t ld, 
  * step_decode(ctx, NULL). */
 int step_profile_decode(step_ctx *ctx, int32_t max_kernels, float *h_ms, int32_t *h_kind);
 const char *step_kernel_kind_name(int32_t kind);
+/* Persistent decode only (persistent_decode = 1): waits for the context's stream, then reports
+ * whether any wait inside a persistent decode step gave up since the last call (it bounds every
+ * wait, so a step always ends; one that gave up has invalid outputs). STEP_OK, or STEP_EHIP with the
+ * site in step_last_error; the flag is cleared. Without persistent_decode it returns STEP_OK. */
+int step_device_status(step_ctx *ctx);
+/* Phase timestamps of the last step_profile_decode of a persistent single-row step, in
+ * microseconds after the kernel's start (block 0's view; -1 where none was taken): slot 8 l + k for
+ * layer l holds k = 1 QKV input normed, 2 attention items done, 3 merges done, 4 O input arrived,
+ * 5 MLP input normed, 6 down input arrived; slot 8 L + 1 the final norm, 8 L + 2 the end. Writes
+ * up to max_stamps values into h_us and returns the number of slots (0 if none were taken). */
+int step_phase_stamps(const step_ctx *ctx, int32_t max_stamps, double *h_us);
 
 /* Rows of the bucket the last decode step ran at, and kernels launched per decode step. */
 int step_last_bucket(const step_ctx *ctx);

@@ -55,3 +55,36 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
         L._lib = None
         L.load(str(tmp_path / "missing.so"))
     L._lib = None
+
+
+def test_persistent_decode_config_is_validated():
+    """persistent_decode is accepted only at the widths its kernel is built for, with bucket 1 and
+    max_position <= 8192; the workspace grows by its hand-off words."""
+    import graph_replay_amd as g
+    import graph_replay_amd._lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libstep.so not built")
+
+    def cfg(**kw):
+        c = L.StepConfig(dtype=L.STEP_BF16, layers=28, hidden=1024, q_heads=16, kv_heads=8, head_dim=128,
+                         intermediate=3072, vocab=151936, qk_norm=1, qkv_bias=0, rms_eps=1e-6, rope_theta=1e6,
+                         block_size=16, num_blocks=100, max_blocks_per_seq=80, max_position=1280, max_batch=1,
+                         max_tokens=0, max_reqs=0, max_logit_rows=0, num_buckets=1, use_graphs=1)
+        c.buckets[0] = 1
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return c
+
+    base = g.step_workspace_bytes(cfg())
+    assert base > 0
+    with_p = g.step_workspace_bytes(cfg(persistent_decode=1))
+    assert with_p > base
+    assert g.step_workspace_bytes(cfg(persistent_decode=1, dtype=L.STEP_F16)) > 0
+    for bad in (dict(dtype=L.STEP_F32), dict(hidden=1536), dict(intermediate=8960), dict(kv_heads=4),
+                dict(max_position=8193), dict(persistent_decode=2)):
+        kw = dict(persistent_decode=1)
+        kw.update(bad)
+        assert g.step_workspace_bytes(cfg(**kw)) == 0, bad
+    c = cfg(persistent_decode=1, max_batch=2, num_buckets=1)
+    c.buckets[0] = 2
+    assert g.step_workspace_bytes(c) == 0            # bucket 1 is what the persistent step serves
