@@ -32,7 +32,8 @@
 //   P2  attention: item (kv head g, 128-key split s): QK-RMSNorm + RoPE of the G query heads and
 //       the key, the new K and V written to the paged pool by the split that holds them, and
 //       the split's (max, sum, unnormalised output) per query head, on the matrix cores.
-//   P2b merge: query head h combines its splits in split order -> attention output (dtype).
+//   P2b merge: item (query head h, 32-dim chunk c) combines the splits in split order ->
+//       attention output (dtype).
 //   P3  O projection.    P4  r += o; x = RMSNorm(r) * g_post; act = SiLU(gate) * up.
 //   P5  down projection.
 // After the last layer: r += down, final RMSNorm, the LM head over all waves -> fp32 logits.
@@ -46,13 +47,19 @@
 
 namespace gr {
 
-constexpr int kPSplit = 128;      // keys per attention item
+constexpr int kPSplit = 64;       // keys per attention item
+constexpr int kPTiles = kPSplit / 64;   // 16-key tiles per compute wave and item
 constexpr int kPMaxSplits = 64;   // splits per KV head the merge stages in LDS (max_position <= 8192)
 constexpr int kPSpin = 1 << 17;   // polls before a wait gives up (each poll is a memory round trip)
 constexpr int kPPhases = 6;       // tagged phases per layer
 constexpr int kPStamps = 512;     // timestamp slots (block 0, optional)
 constexpr int kPThreads = 512;    // 4 compute waves + 4 exchange waves
 constexpr int kPMaxLayers = 64;   // per-layer pointer table held in LDS
+constexpr int kPMergeChunks = 4;  // merge items per query head (32 of the 128 dims each)
+// Words that every block reads are written in kPReplicas copies, so that the 256 readers of a word
+// spread over eight lines instead of queueing on one.
+constexpr int kPReplicas = 8;
+constexpr int kPRepStride = 4096 + 32;   // words between copies (>= the largest replicated buffer)
 // Blocks per launch: one per CU of an MI355X. At this width every compute wave owns exactly one
 // register tile of each projection at the widths the kernel is built for, and every attention item
 // (at most kPBlocks of them) has a block of its own.
@@ -73,9 +80,11 @@ struct PersistArgs {
   const float *rope_cos, *rope_sin;
   uint64_t *x_qkv;                   // [(nq + 2 nkv) * 128]
   uint64_t *x_part;                  // [nq][splits_alloc][128 + 2]: max, sum, output
-  uint64_t *x_attn;                  // [nq * 128]
+  // read by every block: kPReplicas copies kPRepStride words apart, block b reading copy b mod
+  // kPReplicas (the blocks of one XCD share a copy)
+  uint64_t *x_attn;                  // [nq * 128 / 2] words of two values
   uint64_t *x_o, *x_down;            // [H]
-  uint64_t *x_act;                   // [I]
+  uint64_t *x_act;                   // [I / 3] words of three values
   unsigned* epoch;                   // advanced by the last block of each step
   unsigned* done;                    // arrival count, reset by the last block
   int* err;                          // 0, or the site where a wait gave up
@@ -94,13 +103,23 @@ __device__ inline uint64_t get_word(const uint64_t* p) {
 // tag, or three values and the tag's low 16 bits. A 16-bit tag still tells the awaited write from
 // the one before it (every word of such a buffer is rewritten at each of its phases, and
 // consecutive tags differ by 6 or 7), which is the only other content a waiting reader can see.
-__device__ inline void put_word2(uint64_t* p, uint16_t v0, uint16_t v1, uint32_t tag) {
-  put_word(p, __uint_as_float(static_cast<uint32_t>(v0) | (static_cast<uint32_t>(v1) << 16)), tag);
+__device__ inline void put_raw(uint64_t* p, uint64_t w) { __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline uint64_t word1(float v, uint32_t tag) { return (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v); }
+__device__ inline uint64_t word2(uint16_t v0, uint16_t v1, uint32_t tag) {
+  return (static_cast<uint64_t>(tag) << 32) | static_cast<uint64_t>(v0) | (static_cast<uint64_t>(v1) << 16);
 }
-__device__ inline void put_word3(uint64_t* p, uint16_t v0, uint16_t v1, uint16_t v2, uint32_t tag) {
-  const uint64_t w = static_cast<uint64_t>(v0) | (static_cast<uint64_t>(v1) << 16) | (static_cast<uint64_t>(v2) << 32) |
-                     (static_cast<uint64_t>(tag & 0xffffu) << 48);
-  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline uint64_t word3(uint16_t v0, uint16_t v1, uint16_t v2, uint32_t tag) {
+  return static_cast<uint64_t>(v0) | (static_cast<uint64_t>(v1) << 16) | (static_cast<uint64_t>(v2) << 32) |
+         (static_cast<uint64_t>(tag & 0xffffu) << 48);
+}
+// a word of a replicated buffer, to every copy
+__device__ inline void put_rep(uint64_t* base, int i, uint64_t w) {
+#pragma unroll
+  for (int r = 0; r < kPReplicas; ++r) put_raw(base + r * kPRepStride + i, w);
+}
+// this block's copy of a replicated buffer
+__device__ inline const uint64_t* my_copy(const uint64_t* base) {
+  return base + (blockIdx.x % kPReplicas) * kPRepStride;
 }
 
 // Block barrier that waits for this wave's LDS operations only; vector-memory loads in flight
@@ -118,11 +137,15 @@ __device__ inline void poll_words(int t, int n, uint32_t tag, int* err, int wher
   tag &= tmask;
   for (int i0 = t; i0 < n; i0 += 256 * B) {
     uint64_t v[B];
-    // first spin on one word of the B (1/B of the polling traffic while the producers are still
-    // at work), then read all B until they carry the tag
+    // While the producers are still at work one lane of the wave watches one word (1/(64 B) of the
+    // polling traffic of reading them all); then every lane reads all B until they carry the tag.
+    // Blocks and waves watch different words, so that no single line is polled by every CU.
     {
-      const int i = min(i0 + 256 * (B - 1), n - 1);
-      for (int it = 0; (static_cast<uint32_t>(get_word(addr(i)) >> tshift) & tmask) != tag; ++it) {
+      const int i = __builtin_amdgcn_readfirstlane((static_cast<int>(blockIdx.x) * 61 + (t >> 6) * 17) % n);
+      for (int it = 0;; ++it) {
+        uint32_t seen = 0;
+        if ((threadIdx.x & 63) == 0) seen = static_cast<uint32_t>(get_word(addr(i)) >> tshift) & tmask;
+        if (__builtin_amdgcn_readfirstlane(seen) == tag) break;
         if ((it & 63) == 63) {
           if (it >= kPSpin) { atomicCAS(err, 0, where); break; }
           if (ld_dev(err) != 0) break;
@@ -246,7 +269,7 @@ struct WTile {
       b[r] = bias ? bv : 0.f;
     }
   }
-  // dot products of tile t with x (this lane's packed xv): epi(r, row, dot + bias, paired dot) per
+  // dot products of tile t with x (this lane's packed xv): epi(r, row, dot, paired dot) per
   // live row, valid in lane 63; two products per instruction (v_dot2c_f32_bf16 / _f16, fp32
   // accumulation)
   template <class Epi>
@@ -264,7 +287,7 @@ struct WTile {
       }
 #pragma unroll
       for (int h = 0; h < NR; ++h) acc[h] = wave_sum63(acc[h]);
-      epi(r, gw + NW * i, acc[0] + b[r], acc[NR - 1]);   // the sums are in lane 63
+      epi(r, gw + NW * i, acc[0], acc[NR - 1]);   // the sums are in lane 63
     }
   }
 };
@@ -282,12 +305,13 @@ __device__ inline void lane_x(const uint16_t* xs, uint4 (&xv)[VR]) {
 template <class T>
 __device__ inline uint16_t bits16(float x) { return __builtin_bit_cast(uint16_t, T::from_f(x)); }
 
-// K and V tiles of one attention item: compute wave w takes the 16-key tiles w and w + 4 of the
-// split (D = 128: K fragment 4 x 16 B, V^T fragment 8 x 8 B per tile, as in the decode attention
-// kernel). Without an item (g < 0) the scratch block is loaded, so the load count is fixed.
+// K and V tiles of one attention item: compute wave w takes the 16-key tiles w + 4 kb (kb <
+// kPTiles) of the split (D = 128: K fragment 4 x 16 B, V^T fragment 8 x 8 B per tile, as in the
+// decode attention kernel). Without an item (g < 0) the scratch block is loaded, so the load count
+// is fixed.
 struct AttnTiles {
-  uint4 kf[2][4];
-  uint2 vf[2][8];
+  uint4 kf[kPTiles][4];
+  uint2 vf[kPTiles][8];
 };
 
 // pool block of tile wid + 4 kb of split s (the scratch block where the split has no such tile);
@@ -302,14 +326,14 @@ __device__ inline int attn_tile_block(const PersistArgs& a, int g, int s, int L,
   return __builtin_amdgcn_readfirstlane(pb >= 0 ? pb : a.num_blocks - 1);
 }
 
-__device__ inline void attn_tiles_load(AttnTiles& at, const PersistArgs& a, const PLayer& lw, int g, int pb0, int pb1) {
+__device__ inline void attn_tiles_load(AttnTiles& at, const PersistArgs& a, const PLayer& lw, int g, const int (&pbs)[kPTiles]) {
   constexpr int D = 128;
   const int lane = opaque(static_cast<int>(threadIdx.x & 63));
   const int col = lane & 15, grp = lane >> 4;
   const int gg = g < 0 ? 0 : g;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int pb = kb == 0 ? pb0 : pb1;
+  for (int kb = 0; kb < kPTiles; ++kb) {
+    const int pb = pbs[kb];
     const size_t ko = pool_k_at(pb, a.nkv, gg, col, D) + 8 * grp;          // elements; multiple of 8
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) at.kf[kb][ks] = ldg<uint4>(lw.k_pool, (ko + ks * 32) / 8);
@@ -350,6 +374,13 @@ struct PShared {
   PLayer lw[kPMaxLayers];
 };
 
+// 1 / rms of the residual row from the exchange waves' partial sums of squares (after the barrier
+// that follows norm_stage)
+template <int XS, int G>
+__device__ inline float norm_inv(const PShared<XS, G>& sh, int H, float eps) {
+  return 1.0f / sqrtf((sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3]) / static_cast<float>(H) + eps);
+}
+
 // Values every wave of a block derives the same way at the start of a step
 struct PStep {
   int NB, tok, L, p, slot, nsplit, n_items;
@@ -369,9 +400,7 @@ __device__ inline void run_step(Role& ro, const PStep& st, int layers, int nq) {
   for (int l = 0; l < layers; ++l) {
     ro.layer_start(l);
     ro.qkv_wait(l);              // P1
-    ro.norm_sum();
-    bar();
-    ro.norm_apply(0, l);
+    ro.norm_stage(0);
     bar();
     stamp(ro.a, 1 + 8 * l);
     ro.qkv(l);
@@ -387,7 +416,7 @@ __device__ inline void run_step(Role& ro, const PStep& st, int layers, int nq) {
       bar();
     }
     stamp(ro.a, 2 + 8 * l);
-    for (int h = st.NB - 1 - static_cast<int>(blockIdx.x); h < nq; h += st.NB) {   // P2b
+    for (int h = st.NB - 1 - static_cast<int>(blockIdx.x); h < nq * kPMergeChunks; h += st.NB) {   // P2b
       ro.merge_wait(l, h);
       bar();
       ro.merge(l, h);
@@ -399,9 +428,7 @@ __device__ inline void run_step(Role& ro, const PStep& st, int layers, int nq) {
     stamp(ro.a, 4 + 8 * l);
     ro.o_proj(l);
     ro.mlp_wait(l);              // P4
-    ro.norm_sum();
-    bar();
-    ro.norm_apply(1, l);
+    ro.norm_stage(1);
     bar();
     stamp(ro.a, 5 + 8 * l);
     ro.gate_up(l);
@@ -411,9 +438,7 @@ __device__ inline void run_step(Role& ro, const PStep& st, int layers, int nq) {
     ro.down(l);
   }
   ro.final_wait();               // final norm + LM head
-  ro.norm_sum();
-  bar();
-  ro.norm_apply(2, layers);
+  ro.norm_stage(2);
   bar();
   stamp(ro.a, 1 + 8 * layers);
   ro.lm_head();
@@ -471,23 +496,21 @@ struct ExchangeRole {
     poll_words<RJ>(et, H, tag, a.err, where, [&](int i) { return src + i; }, [&](int, int b, uint64_t w) { r[b] += word_f(w); });
   }
   __device__ void qkv_wait(int l) {
-    if (l > 0) add_poll(a.x_down, st.tag(l - 1, 5), 6);
+    if (l > 0) add_poll(my_copy(a.x_down), st.tag(l - 1, 5), 6);
   }
-  __device__ void norm_sum() {
+  // RMSNorm in one barrier: the four waves' sums of squares of r go to red, and xs[0] gets
+  // gain * r rounded to the dtype (gain 0: in_norm, 1: post_norm, 2: final_norm); the readers apply
+  // RMSNorm's 1 / rms, a per-row scalar, to their dot products (W (g r / rms) = (W (g r)) / rms).
+  __device__ void norm_stage(int which) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < RJ; ++j) ss += r[j] * r[j];
     ss = wave_sum63(ss);
     if (lane == 63) sh.red[wid - 4] = ss;
-  }
-  // x = RMSNorm(r) * gain (0: in_norm, 1: post_norm, 2: final_norm) rounded to the dtype -> xs[0]
-  __device__ void norm_apply(int which, int) {
-    const float tot = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
-    const float inv = 1.0f / sqrtf(tot / static_cast<float>(H) + a.eps);
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
       const float gn = which == 0 ? g[0][j] : which == 1 ? g[1][j] : g[2][j];
-      sh.xs[0][et + 256 * j] = bits16<T>(r[j] * inv * gn);
+      sh.xs[0][et + 256 * j] = bits16<T>(r[j] * gn);
     }
   }
   __device__ void qkv(int) {}
@@ -522,16 +545,25 @@ struct ExchangeRole {
   }
   __device__ void attn_products(int, int) {}
   __device__ void attn_partials(int, int) {}
-  __device__ void merge_wait(int l, int h) {
+  // merge item it = (query head it / 4, dims 32 (it % 4) .. + 32): each split's (max, sum) and
+  // those 32 output dims, staged as mst[s][0, 1, 2 ..]
+  __device__ void merge_wait(int l, int it) {
+    constexpr int CW = D / kPMergeChunks, RW = CW + 2;   // dims per item, words per split
+    const int h = it / kPMergeChunks, c = it % kPMergeChunks;
     const uint64_t* src = a.x_part + static_cast<size_t>(h) * a.splits_alloc * (D + 2);
-    poll_words<8>(et, st.nsplit * (D + 2), st.tag(l, 1), a.err, 3, [&](int i) { return src + i; },
-                  [&](int i, int, uint64_t w) { sh.mst[i / (D + 2)][i % (D + 2)] = word_f(w); });
+    poll_words<3>(et, st.nsplit * RW, st.tag(l, 1), a.err, 3, [&](int i) {
+      const int sp = i / RW, k = i % RW;
+      return src + sp * (D + 2) + (k < 2 ? k : 2 + c * CW + (k - 2));
+    }, [&](int i, int, uint64_t w) { sh.mst[i / RW][i % RW] = word_f(w); });
   }
-  // query head h: the splits' partials in split order -> attention output (dtype; zeros without
-  // keys), dims 2k and 2k + 1 in word h * 64 + k
-  __device__ void merge(int l, int h) {
-    if (et >= D) return;   // exchange waves 4 and 5
+  // the splits' partials in split order -> attention output (dtype; zeros without keys), dims 2k
+  // and 2k + 1 of head h in word h * 64 + k
+  __device__ void merge(int l, int it) {
+    constexpr int CW = D / kPMergeChunks;
+    if (et >= 64) return;   // exchange wave 4 (lanes past CW idle in the arithmetic)
+    const int h = it / kPMergeChunks, c = it % kPMergeChunks;
     const int ns = st.nsplit;
+    const int d = min(et, CW - 1);
     float out = 0.f;
     if (ns > 0) {
       float M = -INFINITY;
@@ -540,26 +572,29 @@ struct ExchangeRole {
       for (int s = 0; s < ns; ++s) {
         const float f = __expf(sh.mst[s][0] - M);
         Ls += sh.mst[s][1] * f;
-        O += sh.mst[s][2 + et] * f;
+        O += sh.mst[s][2 + d] * f;
       }
       out = round_to<T>(O / Ls);
     }
     const float nb = __shfl_down(out, 1, 64);
-    if ((et & 1) == 0) put_word2(a.x_attn + static_cast<size_t>(h) * (D / 2) + et / 2, bits16<T>(out), bits16<T>(nb), st.tag(l, 2));
+    const int dim = c * CW + et;
+    if (et < CW && (et & 1) == 0) put_rep(a.x_attn, h * (D / 2) + dim / 2, word2(bits16<T>(out), bits16<T>(nb), st.tag(l, 2)));
   }
   __device__ void o_wait(int l) {
-    poll_words<VQ>(et, a.nq * D / 2, st.tag(l, 2), a.err, 4, [&](int i) { return a.x_attn + i; },
+    const uint64_t* src = my_copy(a.x_attn);
+    poll_words<VQ>(et, a.nq * D / 2, st.tag(l, 2), a.err, 4, [&](int i) { return src + i; },
                    [&](int i, int, uint64_t w) {
                      sh.xs[1][2 * i] = word_h(w, 0);
                      sh.xs[1][2 * i + 1] = word_h(w, 1);
                    });
   }
   __device__ void o_proj(int) {}
-  __device__ void mlp_wait(int l) { add_poll(a.x_o, st.tag(l, 3), 5); }
+  __device__ void mlp_wait(int l) { add_poll(my_copy(a.x_o), st.tag(l, 3), 5); }
   __device__ void gate_up(int) {}
   __device__ void down_wait(int l) {
     // word w holds act[w], act[w + I/3], act[w + 2 I/3] (the three gate|up rows of compute wave w)
-    poll_words<(VI * 2 + 2) / 3>(et, I / 3, st.tag(l, 4), a.err, 7, [&](int i) { return a.x_act + i; },
+    const uint64_t* src = my_copy(a.x_act);
+    poll_words<(VI * 2 + 2) / 3>(et, I / 3, st.tag(l, 4), a.err, 7, [&](int i) { return src + i; },
                                  [&](int i, int, uint64_t w) {
                                    sh.xs[1][i] = word_h(w, 0);
                                    sh.xs[1][i + I / 3] = word_h(w, 1);
@@ -573,7 +608,7 @@ struct ExchangeRole {
     }
   }
   __device__ void down(int) {}
-  __device__ void final_wait() { add_poll(a.x_down, st.tag(a.layers - 1, 5), 8); }
+  __device__ void final_wait() { add_poll(my_copy(a.x_down), st.tag(a.layers - 1, 5), 8); }
   __device__ void lm_head();
 };
 
@@ -591,13 +626,13 @@ struct LmHead {
     R = (a.vocab - 1 - gwl) / NWL + 1;
   }
   __device__ void first(const PersistArgs& a, Tile& ta) const { ta.load(a.lm_head, nullptr, a.vocab, gwl, NWL, R, 0); }
-  __device__ void rest(const PersistArgs& a, const uint16_t* xs, Tile& ta) const {
+  __device__ void rest(const PersistArgs& a, const uint16_t* xs, Tile& ta, float inv) const {
     Tile tb;
     const int lane = threadIdx.x & 63;
     uint4 xv[VH];
     lane_x<VH>(xs, xv);
     auto epi = [&](int, int row, float y, float) {
-      if (lane == 63) a.logits[row] = y;
+      if (lane == 63) a.logits[row] = y * inv;
     };
     const int nt = (R + TL - 1) / TL;
     for (int t = 0; t < nt; t += 2) {
@@ -615,7 +650,7 @@ __device__ void ExchangeRole<T, VH, VQ, VI, G>::lm_head() {
   lm.init(a);
   typename LmHead<T, VH>::Tile ta;
   lm.first(a, ta);
-  lm.rest(a, sh.xs[0], ta);
+  lm.rest(a, sh.xs[0], ta, norm_inv(sh, H, a.eps));
 }
 
 // Compute role (waves 0-3): the projections' weights in registers, issued one phase ahead, their
@@ -626,13 +661,14 @@ struct ComputeRole {
   static constexpr int D = 128, H = 512 * VH, I = 512 * VI, XS_ = 512 * (VI > VQ ? (VI > VH ? VI : VH) : (VQ > VH ? VQ : VH));
   static constexpr int TQ = 4, TO = 1, TG = 3, TD = 1;   // rows per register tile (one tile each at 256 blocks)
   static_assert(I == TG * 4 * kPBlocks, "the gate|up rows of a compute wave fill one packed word");
+  static_assert(H <= kPRepStride && I / 3 <= kPRepStride && 512 * VQ / 2 <= kPRepStride, "replica stride");
   static_assert(TQ == LmHead<T, VH>::TL, "the QKV tile carries the first LM-head tile");
   const PersistArgs& a;
   const PStep& st;
   PShared<XS_, G>& sh;
   const int lane, wid, gw, NW, NQKV;
   int R_qkv, R_o, R_gu, R_dn;
-  int g0, pb0, pb1;            // the block's first attention item: KV head (-1: none), tile blocks
+  int g0, pbs[kPTiles];        // the block's attention item: KV head (-1: none), its tiles' pool blocks
   PLayer lw;
   WTile<T, VH, 1, TQ> wq;
   WTile<T, VQ, 1, TO> wo;
@@ -656,25 +692,25 @@ struct ComputeRole {
     const bool has = it < st.n_items;
     g0 = has ? it / st.nsplit : -1;
     const int s0 = has ? it % st.nsplit : 0;
-    pb0 = attn_tile_block(a, g0, s0, st.L, 0);
-    pb1 = attn_tile_block(a, g0, s0, st.L, 1);
+#pragma unroll
+    for (int kb = 0; kb < kPTiles; ++kb) pbs[kb] = attn_tile_block(a, g0, s0, st.L, kb);
     wq.load(sh.lw[0].qkv_w, sh.lw[0].qkv_b, NQKV, gw, NW, R_qkv, 0);
   }
   // this layer's attention tiles and O weights go out behind the QKV weights
   __device__ void layer_start(int l) {
     lw = sh.lw[l];
-    attn_tiles_load(at, a, lw, g0, pb0, pb1);
+    attn_tiles_load(at, a, lw, g0, pbs);
     wo.load(lw.o_w, nullptr, H, gw, NW, R_o, 0);
   }
   __device__ void qkv_wait(int) {}
-  __device__ void norm_sum() {}
-  __device__ void norm_apply(int, int) {}
+  __device__ void norm_stage(int) {}
   __device__ void qkv(int l) {
     uint4 xv[VH];
     lane_x<VH>(sh.xs[0], xv);
     const uint32_t tg = st.tag(l, 0);
-    wq.dot(xv, gw, NW, R_qkv, 0, [&](int, int row, float y, float) {
-      if (lane == 63) put_word(a.x_qkv + row, y, tg);
+    const float inv = norm_inv(sh, H, a.eps);
+    wq.dot(xv, gw, NW, R_qkv, 0, [&](int r, int row, float y, float) {
+      if (lane == 63) put_word(a.x_qkv + row, y * inv + wq.b[r], tg);
     });
   }
   __device__ void attn_wait(int, int) {}   // the tiles of the block's (only) item went out at layer start
@@ -703,7 +739,7 @@ struct ComputeRole {
       if ((bn & 3) == wid) {
         const int kb = bn >> 2;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kPTiles; ++q) {
           if (q != kb) continue;
           if (col == on) {
 #pragma unroll
@@ -746,16 +782,16 @@ struct ComputeRole {
     for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
     if (wid < nblk) {
-      f32x4_t sc[2];
+      f32x4_t sc[kPTiles];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kPTiles; ++kb) {
         sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16x16x32<T>(at.kf[kb][ks], qf[ks], sc[kb]);
       }
       float bm = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kPTiles; ++kb) {
         const int tb = t0 + (wid + 4 * kb) * kBlk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -767,9 +803,9 @@ struct ComputeRole {
       bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
       m = bm;                                                   // finite: tile wid has a live key
       float ps = 0.f;
-      uint2 pt[2];
+      uint2 pt[kPTiles];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kPTiles; ++kb) {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -782,7 +818,7 @@ struct ComputeRole {
       ps += __shfl_xor(ps, 32, 64);
       lsum = ps;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kPTiles; ++kb) {
         const int tb = t0 + (wid + 4 * kb) * kBlk;
         if (tb + kBlk > t1) {
           // a masked key adds nothing, even if its slot holds NaN (0 * NaN would not be 0)
@@ -843,7 +879,7 @@ struct ComputeRole {
     lane_x<VQ>(sh.xs[1], xv);
     const uint32_t tg = st.tag(l, 3);
     wo.dot(xv, gw, NW, R_o, 0, [&](int, int row, float y, float) {
-      if (lane == 63) put_word(a.x_o + row, y, tg);
+      if (lane == 63) put_rep(a.x_o, row, word1(y, tg));
     });
   }
   __device__ void mlp_wait(int) {}
@@ -853,8 +889,9 @@ struct ComputeRole {
     lane_x<VH>(sh.xs[0], xv);
     const uint32_t tg = st.tag(l, 4);
     uint16_t act[TG];
-    wg.dot(xv, gw, NW, R_gu, 0, [&](int r, int, float gt, float up) { act[r] = bits16<T>(silu(gt) * up); });
-    if (lane == 63) put_word3(a.x_act + gw, act[0], act[1], act[2], tg);   // rows gw, gw + NW, gw + 2 NW
+    const float inv = norm_inv(sh, H, a.eps);
+    wg.dot(xv, gw, NW, R_gu, 0, [&](int r, int, float gt, float up) { act[r] = bits16<T>(silu(gt * inv) * (up * inv)); });
+    if (lane == 63) put_rep(a.x_act, gw, word3(act[0], act[1], act[2], tg));   // rows gw, gw + NW, gw + 2 NW
   }
   __device__ void down_wait(int) {}
   // the next layer's QKV weights (or the first LM-head tile: same tile shape) go out before the
@@ -868,11 +905,11 @@ struct ComputeRole {
     lane_x<VI>(sh.xs[1], xv);
     const uint32_t tg = st.tag(l, 5);
     wd.dot(xv, gw, NW, R_dn, 0, [&](int, int row, float y, float) {
-      if (lane == 63) put_word(a.x_down + row, y, tg);
+      if (lane == 63) put_rep(a.x_down, row, word1(y, tg));
     });
   }
   __device__ void final_wait() {}
-  __device__ void lm_head() { lm.rest(a, sh.xs[0], wq); }
+  __device__ void lm_head() { lm.rest(a, sh.xs[0], wq, norm_inv(sh, H, a.eps)); }
 };
 
 // The step. VH, VQ, VI: 16-byte vectors per lane of a row of length H, nq * 128 and I (each a

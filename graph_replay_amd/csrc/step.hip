@@ -242,10 +242,11 @@ bool compute_layout(const step_config& c, Layout& L) {
     L.p_lw = take(sizeof(gr::PLayer) * static_cast<size_t>(c.layers));
     L.p_qkv = take(sizeof(uint64_t) * static_cast<size_t>(QKV));
     L.p_part = take(sizeof(uint64_t) * static_cast<size_t>(nq) * L.p_splits * (d + 2));
-    L.p_attn = take(sizeof(uint64_t) * static_cast<size_t>(nq) * d);
-    L.p_o = take(sizeof(uint64_t) * static_cast<size_t>(H));
-    L.p_act = take(sizeof(uint64_t) * static_cast<size_t>(I));
-    L.p_down = take(sizeof(uint64_t) * static_cast<size_t>(H));
+    const size_t rep_bytes = sizeof(uint64_t) * static_cast<size_t>(gr::kPReplicas) * gr::kPRepStride;
+    L.p_attn = take(rep_bytes);
+    L.p_o = take(rep_bytes);
+    L.p_act = take(rep_bytes);
+    L.p_down = take(rep_bytes);
     L.p_ctl = take(4 * sizeof(unsigned));          // epoch | done | err | spare
     L.p_stamps = take(sizeof(unsigned long long) * gr::kPStamps);
   }

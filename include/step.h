@@ -107,9 +107,11 @@ typedef struct {
    * of ~600 small kernels is bound by their overhead, not by bandwidth). The phases of a layer hand
    * their outputs to the next through tagged device-memory words inside the kernel. Same results
    * as the multi-kernel step up to rounding order. Built for 16-bit dtypes at hidden 1024, 16 x 128
-   * query dims, intermediate 3072, 2 query heads per KV head (Qwen3-0.6B's widths; any layer count
-   * and vocabulary) and max_position <= 8192; other configurations get STEP_EUNSUPPORTED at
-   * step_init. buckets[0] must be 1. Other buckets keep the multi-kernel step. 0: off. */
+   * query dims, intermediate 3072, 2 query heads per KV head (Qwen3-0.6B's widths; up to 64 layers,
+   * vocabulary >= 2048), max_position <= 64 * 256 / kv_heads (2048 at those widths: one 64-key
+   * attention split per block) and a device of at least 256 CUs (one block each); other
+   * configurations get STEP_EUNSUPPORTED at step_init. buckets[0] must be 1. Other buckets keep
+   * the multi-kernel step. 0: off. */
   int32_t persistent_decode;
 } step_config;
 
