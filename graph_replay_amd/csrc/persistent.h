@@ -695,13 +695,15 @@ struct ComputeRole {
 #pragma unroll
     for (int kb = 0; kb < kPTiles; ++kb) pbs[kb] = attn_tile_block(a, g0, s0, st.L, kb);
     wq.load(sh.lw[0].qkv_w, sh.lw[0].qkv_b, NQKV, gw, NW, R_qkv, 0);
+    attn_tiles_load(at, a, sh.lw[0], g0, pbs);
+    wo.load(sh.lw[0].o_w, nullptr, H, gw, NW, R_o, 0);
   }
-  // this layer's attention tiles and O weights go out behind the QKV weights
-  __device__ void layer_start(int l) {
-    lw = sh.lw[l];
-    attn_tiles_load(at, a, lw, g0, pbs);
-    wo.load(lw.o_w, nullptr, H, gw, NW, R_o, 0);
-  }
+  // Weights (and attention tiles) go out two phases or more before their use, each batch after the
+  // issuing phase's own outputs are stored (with the whole chip loading weights at once, issuing
+  // loads can stall the wave until queue slots free up): gate|up after QKV, down after O, the next
+  // layer's QKV after gate|up, its attention tiles and O after down. The order keeps every wait
+  // exact: each use waits only for its own batch and the older ones.
+  __device__ void layer_start(int l) { lw = sh.lw[l]; }
   __device__ void qkv_wait(int) {}
   __device__ void norm_stage(int) {}
   __device__ void qkv(int l) {
@@ -712,6 +714,9 @@ struct ComputeRole {
     wq.dot(xv, gw, NW, R_qkv, 0, [&](int r, int row, float y, float) {
       if (lane == 63) put_word(a.x_qkv + row, y * inv + wq.b[r], tg);
     });
+    // an attention block issues them after its attention products instead (its exchange waves are
+    // about to wait for this step's q, k and v, and loads in flight on the CU would delay that wait)
+    if (g0 < 0) wg.load(lw.gate_up_w, nullptr, I, gw, NW, R_gu, 0);
   }
   __device__ void attn_wait(int, int) {}   // the tiles of the block's (only) item went out at layer start
   __device__ void attn_rope(int, int) {}
@@ -869,22 +874,22 @@ struct ComputeRole {
         put_word(pp + 1, Ls, tg);
       }
     }
+    wg.load(lw.gate_up_w, nullptr, I, gw, NW, R_gu, 0);
   }
   __device__ void merge_wait(int, int) {}
   __device__ void merge(int, int) {}
   __device__ void o_wait(int) {}
   __device__ void o_proj(int l) {
-    wg.load(lw.gate_up_w, nullptr, I, gw, NW, R_gu, 0);
     uint4 xv[VQ];
     lane_x<VQ>(sh.xs[1], xv);
     const uint32_t tg = st.tag(l, 3);
     wo.dot(xv, gw, NW, R_o, 0, [&](int, int row, float y, float) {
       if (lane == 63) put_rep(a.x_o, row, word1(y, tg));
     });
+    wd.load(lw.down_w, nullptr, H, gw, NW, R_dn, 0);
   }
   __device__ void mlp_wait(int) {}
   __device__ void gate_up(int l) {
-    wd.load(lw.down_w, nullptr, H, gw, NW, R_dn, 0);
     uint4 xv[VH];
     lane_x<VH>(sh.xs[0], xv);
     const uint32_t tg = st.tag(l, 4);
@@ -892,21 +897,26 @@ struct ComputeRole {
     const float inv = norm_inv(sh, H, a.eps);
     wg.dot(xv, gw, NW, R_gu, 0, [&](int r, int, float gt, float up) { act[r] = bits16<T>(silu(gt * inv) * (up * inv)); });
     if (lane == 63) put_rep(a.x_act, gw, word3(act[0], act[1], act[2], tg));   // rows gw, gw + NW, gw + 2 NW
-  }
-  __device__ void down_wait(int) {}
-  // the next layer's QKV weights (or the first LM-head tile: same tile shape) go out before the
-  // down products, through one load sequence either way (the waits stay exact)
-  __device__ void down(int l) {
+    // the next layer's QKV weights (or the first LM-head tile: same tile shape), through one load
+    // sequence either way (the waits stay exact)
     const bool last = l + 1 == a.layers;
     const PLayer& nx = sh.lw[last ? l : l + 1];
     wq.load(last ? a.lm_head : nx.qkv_w, last ? nullptr : nx.qkv_b, last ? a.vocab : NQKV, last ? lm.gwl : gw,
             last ? lm.NWL : NW, last ? lm.R : R_qkv, 0);
+  }
+  __device__ void down_wait(int) {}
+  // the next layer's attention tiles and O weights go out after the down products (after the last
+  // layer: the same loads again, never used, so that the load sequence is the same every layer)
+  __device__ void down(int l) {
     uint4 xv[VI];
     lane_x<VI>(sh.xs[1], xv);
     const uint32_t tg = st.tag(l, 5);
     wd.dot(xv, gw, NW, R_dn, 0, [&](int, int row, float y, float) {
       if (lane == 63) put_rep(a.x_down, row, word1(y, tg));
     });
+    const PLayer& nx = sh.lw[l + 1 < a.layers ? l + 1 : l];
+    attn_tiles_load(at, a, nx, g0, pbs);
+    wo.load(nx.o_w, nullptr, H, gw, NW, R_o, 0);
   }
   __device__ void final_wait() {}
   __device__ void lm_head() { lm.rest(a, sh.xs[0], wq, norm_inv(sh, H, a.eps)); }
