@@ -56,8 +56,8 @@ def kinds(trace: str) -> None:
         k = _kind_bs1(r["Kernel_Name"], grid)
         if k:
             acc.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    print("\nPer decode-step kind (kernel trace of the same run; the two projections that share the")
-    print("`k_gemv<BF16, 1, 2, 2>` instantiation are told apart by grid size):\n")
+    print("\nPer decode-step kind (kernel trace of the same run; the two projections of the multi-kernel")
+    print("step that share the `k_gemv<BF16, 1, 2, 2>` instantiation are told apart by grid size):\n")
     print("| kind | calls | avg (us) | median (us) |")
     print("|---|---:|---:|---:|")
     for k, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
@@ -76,6 +76,8 @@ def _copy_factor(d: str) -> float:
 
 # Which decode-step kernel kind a (kernel, grid size) dispatch of the batch-1 Qwen3-0.6B step is.
 def _kind_bs1(name: str, grid: int) -> str:
+    if "k_persist_decode" in name:
+        return "decode_step_persistent"
     if "k_attn_rows" in name:
         return "attn_decode"
     if "k_sample" in name:
