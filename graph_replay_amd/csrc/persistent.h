@@ -44,6 +44,7 @@
 // needs one block's resources per CU.
 #pragma once
 #include "attention.h"
+#include "sample.h"
 
 namespace gr {
 
@@ -75,7 +76,8 @@ struct PersistArgs {
   float eps, scale;
   const PLayer* lw;                  // [layers], device memory
   const void *embed, *lm_head, *final_norm;
-  const int *ids, *pos, *slot, *len, *bt;   // row 0 of the decode metadata
+  int *ids, *pos, *slot, *len;       // row 0 of the decode metadata (advanced in place when sampling)
+  const int* bt;
   int bt_stride, num_blocks, splits_alloc;
   const float *rope_cos, *rope_sin;
   uint64_t *x_qkv;                   // [(nq + 2 nkv) * 128]
@@ -90,6 +92,15 @@ struct PersistArgs {
   int* err;                          // 0, or the site where a wait gave up
   unsigned long long* stamps;        // optional [kPStamps] s_memrealtime stamps of block 0
   float* logits;                     // [vocab] row 0
+  // Sampling fused into the LM head (sample != 0): the token the separate sampler would draw from
+  // these logits (Gumbel-max with the same Philox uniforms; argmax at temperature 0), then the
+  // same in-place advance of row 0 and of the step counter, by the last block.
+  int sample;
+  const float* temp;                 // [1] temperature
+  uint64_t* rng;                     // {seed, step}
+  uint64_t* cand;                    // [gridDim.x] each block's best (score key << 32 | ~index)
+  int* tokens;                       // [1]
+  int* history;                      // [max_position] or nullptr
 };
 
 __device__ inline void put_word(uint64_t* p, float v, uint32_t tag) {
@@ -196,6 +207,18 @@ __device__ inline float wave_sum63(float v) {
   v = dpp_add<0x140, 0xf>(v);   // row_mirror
   v = dpp_add<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
   v = dpp_add<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// the largest 64-bit value over the wave, in every lane
+__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, 64);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, 64);
+    const unsigned long long w = (static_cast<unsigned long long>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
   return v;
 }
 
@@ -372,6 +395,8 @@ struct PShared {
   // complete in order, so a table read from memory behind the weight loads in flight would wait
   // for all of them, where an LDS read does not.
   PLayer lw[kPMaxLayers];
+  unsigned long long cand[8];          // per-wave sampling candidates
+  int last;                            // this block is the last of the step to finish
 };
 
 // 1 / rms of the residual row from the exchange waves' partial sums of squares (after the barrier
@@ -385,6 +410,8 @@ __device__ inline float norm_inv(const PShared<XS, G>& sh, int H, float eps) {
 struct PStep {
   int NB, tok, L, p, slot, nsplit, n_items;
   uint32_t tag0;
+  float T;                 // sampling temperature, seed and Philox step counter
+  uint64_t seed, stepc;
   __device__ uint32_t tag(int l, int ph) const { return tag0 + static_cast<uint32_t>(kPPhases * l + ph); }
 };
 
@@ -626,13 +653,23 @@ struct LmHead {
     R = (a.vocab - 1 - gwl) / NWL + 1;
   }
   __device__ void first(const PersistArgs& a, Tile& ta) const { ta.load(a.lm_head, nullptr, a.vocab, gwl, NWL, R, 0); }
-  __device__ void rest(const PersistArgs& a, const uint16_t* xs, Tile& ta, float inv) const {
+  // the logits of this wave's rows; with sampling, the wave's best (score key, ~index) into *best
+  __device__ void rest(const PersistArgs& a, const PStep& st, const uint16_t* xs, Tile& ta, float inv,
+                       unsigned long long* best) const {
     Tile tb;
     const int lane = threadIdx.x & 63;
     uint4 xv[VH];
     lane_x<VH>(xs, xv);
+    // lane j keeps the logits of the wave's rows j and j + 64 (the host keeps R <= 128)
+    float z0 = 0.f, z1 = 0.f;
+    int k = 0;
     auto epi = [&](int, int row, float y, float) {
-      if (lane == 63) a.logits[row] = y * inv;
+      const float z = y * inv;
+      if (lane == 63) a.logits[row] = z;
+      const float zb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 63));
+      z0 = lane == k ? zb : z0;
+      z1 = lane + 64 == k ? zb : z1;
+      ++k;
     };
     const int nt = (R + TL - 1) / TL;
     for (int t = 0; t < nt; t += 2) {
@@ -641,6 +678,21 @@ struct LmHead {
       if (t + 2 < nt) ta.load(a.lm_head, nullptr, a.vocab, gwl, NWL, R, t + 2);
       if (t + 1 < nt) tb.dot(xv, gwl, NWL, R, t + 1, epi);
     }
+    if (!a.sample) return;
+    // scores as the separate sampler forms them: z at temperature 0, else z / T plus Gumbel noise
+    // of the (row 0, column) uniform; the largest key is the largest score, ties to the lowest index
+    unsigned long long key = 0ull;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      const int col = gwl + NWL * i;
+      float sc = h ? z1 : z0;
+      if (st.T > 0.f) sc = gumbel_score(sc / st.T, philox_uniform(st.seed, st.stepc, 0, col));
+      const unsigned long long kk = (static_cast<unsigned long long>(fkey(sc)) << 32) | static_cast<uint32_t>(~col);
+      key = (i < R && kk > key) ? kk : key;
+    }
+    key = wave_max_u64(key);
+    if (lane == 0) *best = key;
   }
 };
 
@@ -650,7 +702,7 @@ __device__ void ExchangeRole<T, VH, VQ, VI, G>::lm_head() {
   lm.init(a);
   typename LmHead<T, VH>::Tile ta;
   lm.first(a, ta);
-  lm.rest(a, sh.xs[0], ta, norm_inv(sh, H, a.eps));
+  lm.rest(a, st, sh.xs[0], ta, norm_inv(sh, H, a.eps), &sh.cand[threadIdx.x >> 6]);
 }
 
 // Compute role (waves 0-3): the projections' weights in registers, issued one phase ahead, their
@@ -919,7 +971,7 @@ struct ComputeRole {
     wo.load(nx.o_w, nullptr, H, gw, NW, R_o, 0);
   }
   __device__ void final_wait() {}
-  __device__ void lm_head() { lm.rest(a, sh.xs[0], wq, norm_inv(sh, H, a.eps)); }
+  __device__ void lm_head() { lm.rest(a, st, sh.xs[0], wq, norm_inv(sh, H, a.eps), &sh.cand[threadIdx.x >> 6]); }
 };
 
 // The step. VH, VQ, VI: 16-byte vectors per lane of a row of length H, nq * 128 and I (each a
@@ -937,6 +989,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
   st.L = a.len[0];
   st.p = min(max(a.pos[0], 0), a.max_position - 1);
   st.slot = a.slot[0];
+  st.T = a.sample ? a.temp[0] : 0.f;
+  st.seed = a.sample ? a.rng[0] : 0ull;
+  st.stepc = a.sample ? a.rng[1] : 0ull;
   {
     constexpr int kw = sizeof(PLayer) / sizeof(uint64_t);
     static_assert(sizeof(PLayer) % sizeof(uint64_t) == 0, "PLayer is a whole number of words");
@@ -956,12 +1011,39 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
     ComputeRole<T, VH, VQ, VI, G> ro(a, st, sh);
     run_step(ro, st, a.layers, a.nq);
   }
-  // the last block to finish advances the epoch for the next step
+  // the last block to finish takes the token (when sampling) and advances the epoch for the next
+  // step; every block read the step's inputs before it counted itself in
   stores_done();
   __syncthreads();
-  if (threadIdx.x == 0 && arrive_last(a.done, gridDim.x)) {
-    __hip_atomic_store(a.epoch, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    if (a.sample) {
+      unsigned long long b = sh.cand[0];
+      for (int w = 1; w < 8; ++w) b = sh.cand[w] > b ? sh.cand[w] : b;
+      put_raw(reinterpret_cast<uint64_t*>(a.cand) + blockIdx.x, b);
+      stores_done();
+    }
+    sh.last = arrive_last(a.done, gridDim.x);
   }
+  __syncthreads();
+  if (!sh.last) return;
+  if (a.sample) {
+    unsigned long long b = 0ull;
+    for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += kPThreads) {
+      const unsigned long long w = get_word(a.cand + i);
+      b = w > b ? w : b;
+    }
+    b = wave_max_u64(b);
+    if ((threadIdx.x & 63) == 0) sh.cand[threadIdx.x >> 6] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 0; w < 8; ++w) b = sh.cand[w] > b ? sh.cand[w] : b;
+      const int tok = static_cast<int>(~static_cast<uint32_t>(b));
+      a.tokens[0] = tok;
+      advance_row(tok, a.ids, a.pos, a.len, a.slot, a.bt, a.bt_stride, a.history, a.max_position);
+      a.rng[1] = st.stepc + 1;
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(a.epoch, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace gr

@@ -33,6 +33,47 @@ __device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
   }
 }
 
+// The Gumbel-max score of a temperature-scaled logit zd = z / T (T > 0) with uniform u.
+__device__ inline float gumbel_score(float zd, float u) {
+  const float uu = fminf(fmaxf(u, 1e-10f), 1.0f);
+  return zd - logf(-logf(uu));
+}
+
+// The uniform of (row, column) under the counter scheme above, from one Philox call.
+__device__ inline float philox_uniform(uint64_t seed, uint64_t step, int row, int col) {
+  uint32_t w[4] = {static_cast<uint32_t>(col >> 2), static_cast<uint32_t>(row), static_cast<uint32_t>(step),
+                   static_cast<uint32_t>(step >> 32)};
+  philox4x32_10(w, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  const int j = col & 3;
+  const uint32_t x = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
+  return static_cast<float>(x >> 8) * 5.9604644775390625e-08f;
+}
+
+// The in-place advance of one decode row whose token is tok: the token is recorded at the input's
+// position and becomes the next input, and the position and key count move by one; a row out of
+// positions (hist_ld) or of reserved blocks turns into a padding row. Padding rows (len 0) stay.
+__device__ inline void advance_row(int tok, int* ids, int* pos, int* lens, int* slots, const int* bt_row,
+                                   int bt_stride, int* hist_row, int hist_ld) {
+  const int len = *lens;
+  if (len <= 0) return;
+  const int p = *pos;
+  if (hist_row && p < hist_ld) hist_row[p] = tok;
+  const int np = p + 1;
+  const int blk = np / 16;
+  const int entry = (blk < bt_stride) ? bt_row[blk] : -1;
+  if (np >= hist_ld || entry < 0) {
+    *ids = 0;
+    *pos = 0;
+    *lens = 0;
+    *slots = -1;
+  } else {
+    *ids = tok;
+    *pos = np;
+    *lens = len + 1;
+    *slots = entry * 16 + np % 16;
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // Top-k / top-p filters before the Gumbel-max argmax (same page and section: the filters run before
 // the argmax and set filtered logits to -inf; a fixed k keeps shapes static, and top-p is a sort and
@@ -398,11 +439,10 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       if (c + j >= c1) break;
       float sc = zz[j];
       if (T > 0.f) {
-        const float uu = fminf(fmaxf(u[j], 1e-10f), 1.0f);
         const float zd = sc / T;
         const uint32_t key = fkey(zd);
         const bool kept = key > cut.x || (key == cut.x && c + j < static_cast<int>(cut.y));
-        sc = kept ? zd - logf(-logf(uu)) : -INFINITY;
+        sc = kept ? gumbel_score(zd, u[j]) : -INFINITY;
       }
       best_merge(bv, bi, sc, c + j);
     }
@@ -427,28 +467,10 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   if (threadIdx.x != 0) return;
   const int tok = bi;
   a.tokens_out[row] = tok;
-  if (a.advance) {
-    const int len = a.seq_lens[row];
-    if (len > 0) {
-      const int p = a.positions[row];
-      if (a.history && p < a.hist_ld) a.history[static_cast<size_t>(row) * a.hist_ld + p] = tok;
-      const int np = p + 1;
-      const int blk = np / 16;
-      const int entry = (blk < a.bt_stride) ? a.block_table[static_cast<size_t>(row) * a.bt_stride + blk] : -1;
-      if (np >= a.hist_ld || entry < 0) {
-        // out of positions or of reserved blocks: the row turns into a padding row
-        a.input_ids[row] = 0;
-        a.positions[row] = 0;
-        a.seq_lens[row] = 0;
-        a.slots[row] = -1;
-      } else {
-        a.input_ids[row] = tok;
-        a.positions[row] = np;
-        a.seq_lens[row] = len + 1;
-        a.slots[row] = entry * 16 + np % 16;
-      }
-    }
-  }
+  if (a.advance)
+    advance_row(tok, a.input_ids + row, a.positions + row, a.seq_lens + row, a.slots + row,
+                a.block_table + static_cast<size_t>(row) * a.bt_stride, a.bt_stride,
+                a.history ? a.history + static_cast<size_t>(row) * a.hist_ld : nullptr, a.hist_ld);
   if (a.rng && arrive_last(a.done_cnt, gridDim.x)) {
     uint64_t* r = const_cast<uint64_t*>(a.rng);
     r[1] = step + 1;

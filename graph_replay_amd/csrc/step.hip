@@ -40,7 +40,7 @@ struct Layout {  // byte offsets into the workspace
   size_t attn_part, attn_cnt, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
   size_t samp_topk, samp_topp, samp_filt;
   // persistent decode step: per-layer pointers, tagged hand-off words, control words, stamps
-  size_t p_lw, p_qkv, p_part, p_attn, p_o, p_act, p_down, p_ctl, p_stamps;
+  size_t p_lw, p_qkv, p_part, p_attn, p_o, p_act, p_down, p_ctl, p_stamps, p_cand;
   int p_splits;                       // attention splits per KV head the partial words hold
   size_t total;
   int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
@@ -249,6 +249,7 @@ bool compute_layout(const step_config& c, Layout& L) {
     L.p_down = take(rep_bytes);
     L.p_ctl = take(4 * sizeof(unsigned));          // epoch | done | err | spare
     L.p_stamps = take(sizeof(unsigned long long) * gr::kPStamps);
+    L.p_cand = take(sizeof(uint64_t) * gr::kPBlocks);
   }
   L.total = off;
   (void)RM;
@@ -308,6 +309,10 @@ int validate_config(step_ctx* ctx, const step_config* c) {
     if (c->max_position > max_keys)
       return fail(ctx, STEP_EUNSUPPORTED, "persistent_decode needs max_position <= %d", max_keys);
     if (c->buckets[0] != 1) return fail(ctx, STEP_EINVAL, "persistent_decode serves bucket 1, which the buckets must hold");
+    // every LM-head wave owns at least one row and at most 128 (the fused sampler keeps two per lane)
+    if (c->vocab < 8 * gr::kPBlocks || c->vocab > 128 * 8 * gr::kPBlocks)
+      return fail(ctx, STEP_EUNSUPPORTED, "persistent_decode needs %d <= vocab <= %d", 8 * gr::kPBlocks,
+                  128 * 8 * gr::kPBlocks);
   }
   return STEP_OK;
 }
@@ -819,6 +824,10 @@ int run_persist(step_ctx* ctx, const DecodeMeta& m) {
     a.epoch = ctl; a.done = ctl + 1; a.err = reinterpret_cast<int*>(ctl + 2);
     a.stamps = ctx->p_stamp_next ? reinterpret_cast<unsigned long long*>(ws + L.p_stamps) : nullptr;
     a.logits = ctx->logits;
+    // without top-k / top-p filters the sampler runs inside the kernel, after the LM head
+    a.sample = c.sampling_filters ? 0 : 1;
+    a.temp = m.temp; a.rng = m.rng; a.tokens = ctx->tokens; a.history = ctx->history;
+    a.cand = reinterpret_cast<uint64_t*>(ws + L.p_cand);
     pre_launch(ctx, KK_PERSIST);
     launch((k_persist_decode<T, 2, 4, 6, 2>), dim3(ctx->p_nb), dim3(gr::kPThreads), 0, ctx->stream, a);
     const hipError_t e = hipGetLastError();
@@ -835,6 +844,7 @@ int run_decode(step_ctx* ctx, int B) {
   DecodeMeta m = decode_meta(ctx->ws + L.dmeta, c.max_batch, W);
   if (ctx->p_nb > 0 && B == 1) {
     TRY(run_persist<T>(ctx, m));
+    if (!c.sampling_filters) return STEP_OK;
     return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
                       m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr,
                       c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
@@ -1122,7 +1132,6 @@ extern "C" int step_init(const step_config* cfg, const step_weights* w, const st
     if (cus < gr::kPBlocks)
       return bail(fail(ctx, STEP_EUNSUPPORTED, "persistent decode needs %d CUs (one block each), the device has %d",
                        gr::kPBlocks, cus));
-    if (c.vocab < 8 * gr::kPBlocks) return bail(fail(ctx, STEP_EUNSUPPORTED, "persistent decode needs vocab >= %d", 8 * gr::kPBlocks));
     ctx->p_nb = gr::kPBlocks;
   }
   fill_decode_padding(c, ctx->h_stage[0]);

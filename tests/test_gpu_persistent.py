@@ -88,7 +88,7 @@ def test_persistent_step_matches_oracle_and_multikernel(torch_cuda):
             assert near_tie_ok(tp, gm, TOL["bf16"]), i
             break
         assert max_abs(gp, gm) <= TOL["bf16"], (i, max_abs(gp, gm))
-    assert dp.kernels_per_decode(1) == 2
+    assert dp.kernels_per_decode(1) == 1   # the sampler runs inside the step kernel
     dp.close()
     dm.close()
 
@@ -169,7 +169,7 @@ def test_persistent_bs1_workload_prefill_then_graph_greedy_loop(torch_cuda):
     dec.device_status()
     hist = dec.history[0, n:n + steps].cpu().numpy()
     prof = dec.profile_decode()
-    assert [k for k, _ in prof] == ["decode_step_persistent", "sample"]
+    assert [k for k, _ in prof] == ["decode_step_persistent"]
     st = dec.phase_stamps()
     dec.device_status()
     dec.close()
@@ -187,3 +187,61 @@ def test_persistent_bs1_workload_prefill_then_graph_greedy_loop(torch_cuda):
         assert max_abs(lg, ref[i]) <= TOL["bf16"], (i, max_abs(lg, ref[i]))
     bad = [i for i in range(steps) if not near_tie_ok(int(hist[i]), ref[i], TOL["bf16"])]
     assert not bad, bad
+
+
+def test_persistent_fused_sampling_equals_separate_sampler(torch_cuda):
+    """The sampler fused into the persistent step's LM head against the separate sampling kernels
+    behind the same step kernel (sampling_filters = 1 with the filters off), at temperature 0.8 over
+    the full 151,936-token vocabulary (74 or 75 rows per LM-head wave): the same logits bitwise, the
+    same token, history and continued state at every step (bit-exact); each token also equals
+    step_sample's draw from the kernel's own logits at the step's Philox counter, and at temperature
+    0 the lowest-index argmax."""
+    torch = torch_cuda
+    shape = synth.QWEN3_0_6B.replace(layers=2)
+    W = synth.make_weights(shape, 0)
+    n = 300
+    sc = Scenario(shape, W, [n], steps=8, seed=1103)
+    table, bt = sc.tables[0], sc.table_array()
+    kw = dict(num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=n + 32, max_batch=1,
+              buckets=[1], history=True, persistent_decode=True)
+    df = _decoder(shape, W, **kw)
+    ds = _decoder(shape, W, sampling_filters=True, **kw)
+    for d in (df, ds):
+        sc.inject(d)
+    seed = 0x5EED_1103
+    for temp in (0.8, 0.0):
+        log("fused sampling, temperature", temp)
+        tok = int(sc.tokens[0])
+        args = ([tok], [n], [n + 1], [oracle.slot_of(table, n, 16)], bt)
+        toks = {}
+        for name, d in (("fused", df), ("separate", ds)):
+            d.decode(*args, temperature=np.full(1, temp, np.float32), seed=seed)
+            torch.cuda.synchronize()
+            d.device_status()
+            out = []
+            for i in range(4):
+                if i:
+                    d.decode_continue()
+                    torch.cuda.synchronize()
+                    d.device_status()
+                lg = d.logits[0:1].clone()
+                t = int(d.tokens[0].item())
+                out.append((lg.cpu().numpy()[0], t))
+                if name == "fused":
+                    # the step counter of host-fed step k is k (0 first), moved on by one per step
+                    c = (0 if temp > 0 else 4) + i
+                    want = int(d.sample(lg, temperature=np.full(1, temp, np.float32), seed=seed, counter=c)[0].item())
+                    assert t == want, (temp, i, t, want)
+                    if temp == 0:
+                        assert t == int(oracle.argmax_lowest(out[-1][0])), i
+            toks[name] = (out, d.history[0, n:n + 4].cpu().numpy().copy())
+        (of, hf), (os_, hs) = toks["fused"], toks["separate"]
+        for i in range(4):
+            assert np.array_equal(of[i][0], os_[i][0]), (temp, i)
+            assert of[i][1] == os_[i][1], (temp, i)
+        assert np.array_equal(hf, hs), (hf, hs)
+        assert hf.tolist() == [t for _, t in of]
+    assert df.kernels_per_decode(1) == 1
+    assert ds.kernels_per_decode(1) == 3   # step kernel, filter, sampler
+    df.close()
+    ds.close()

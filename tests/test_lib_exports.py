@@ -58,8 +58,9 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
 
 
 def test_persistent_decode_config_is_validated():
-    """persistent_decode is accepted only at the widths its kernel is built for, with bucket 1 and
-    max_position <= 8192; the workspace grows by its hand-off words."""
+    """persistent_decode is accepted only at the widths its kernel is built for, with bucket 1,
+    max_position <= 64 keys x 256 blocks / 8 KV heads = 2048 and 2048 <= vocab <= 262144 (every one of
+    the 2048 LM-head waves owns 1 to 128 rows); the workspace grows by its hand-off words."""
     import graph_replay_amd as g
     import graph_replay_amd._lib as L
     if not os.path.exists(L.LIB_PATH):
@@ -81,10 +82,12 @@ def test_persistent_decode_config_is_validated():
     assert with_p > base
     assert g.step_workspace_bytes(cfg(persistent_decode=1, dtype=L.STEP_F16)) > 0
     for bad in (dict(dtype=L.STEP_F32), dict(hidden=1536), dict(intermediate=8960), dict(kv_heads=4),
-                dict(max_position=8193), dict(persistent_decode=2)):
+                dict(max_position=2049), dict(vocab=2047), dict(vocab=262145), dict(persistent_decode=2)):
         kw = dict(persistent_decode=1)
         kw.update(bad)
         assert g.step_workspace_bytes(cfg(**kw)) == 0, bad
+    for good in (dict(max_position=2048), dict(vocab=2048), dict(vocab=262144)):
+        assert g.step_workspace_bytes(cfg(persistent_decode=1, **good)) > 0, good
     c = cfg(persistent_decode=1, max_batch=2, num_buckets=1)
     c.buckets[0] = 2
     assert g.step_workspace_bytes(c) == 0            # bucket 1 is what the persistent step serves
