@@ -590,8 +590,10 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   }
   SampleArgs a{};
   a.logits = logits; a.ld = ld; a.vocab = vocab;
+  // one or two 1,024-column passes per thread while the grid stays within 4,096 blocks: a thread's
+  // passes are serial memory round trips, so short chunks finish sooner
   int chunk = 1024;
-  while (chunk < 16384 && static_cast<long>(rows) * ((vocab + chunk * 2 - 1) / (chunk * 2)) >= 256) chunk *= 2;
+  while (chunk < 16384 && static_cast<long>(rows) * ((vocab + chunk - 1) / chunk) > 4096) chunk *= 2;
   a.chunk = chunk;
   a.temperature = temp; a.uniforms = uniforms; a.rng = rng; a.seed = seed; a.step = stepc;
   a.part_val = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_val);
