@@ -15,10 +15,11 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib
-from ._lib import (STEP_BF16, STEP_F16, STEP_F32, StepBatch, StepBuffers, StepConfig, StepPacked, StepWeights)
+from ._lib import (STEP_BF16, STEP_F16, STEP_F32, MoeLayer, StepBatch, StepBuffers, StepConfig, StepPacked,
+                   StepWeights)
 
 __all__ = ["Decoder", "StepError", "step_workspace_bytes", "step_init", "step_decode", "step_mixed", "step_sample",
-           "step_destroy", "load"]
+           "step_destroy", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "MoeLayer"]
 
 load = _lib.load
 
@@ -104,6 +105,91 @@ def step_device_status(ctx) -> None:
 def step_destroy(ctx) -> None:
     if ctx:
         _lib.load().step_destroy(ctx)
+
+
+# -------------------------------------------------------------------------------- MoE layer (moe.h)
+
+def _moe_raise(rc: int) -> None:
+    if rc == _lib.STEP_OK:
+        return
+    msg = _lib.load().moe_last_error().decode()
+    if rc == _lib.STEP_EINVAL:
+        raise ValueError(msg)
+    raise StepError(rc, msg)
+
+
+def moe_align_rows(total: int, num_experts: int, block_m: int) -> int:
+    """Rows of the grouped layout (-1 when the sizes are out of range)."""
+    return int(_lib.load().moe_align_rows(total, num_experts, block_m))
+
+
+def _check_dev(name, t, dtype, torch):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def moe_align(expert_ids, num_experts: int, block_m: int):
+    """expert_ids: int32 CUDA tensor [N, k] (or flat). Returns (sorted_ids, block_expert, num_padded)
+    int32 CUDA tensors, enqueued on the current stream."""
+    import torch
+    _check_dev("expert_ids", expert_ids, torch.int32, torch)
+    total = expert_ids.numel()
+    rows = moe_align_rows(total, num_experts, block_m)
+    if rows < 0:
+        raise ValueError(f"moe_align: sizes out of range (total {total}, experts {num_experts}, block_m {block_m})")
+    dev = expert_ids.device
+    sorted_ids = torch.empty(rows, dtype=torch.int32, device=dev)
+    block_expert = torch.empty(rows // block_m, dtype=torch.int32, device=dev)
+    num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    ip = lambda t: C.cast(C.c_void_p(t.data_ptr()), _lib.I32P)
+    _moe_raise(_lib.load().moe_align(ip(expert_ids), total, num_experts, block_m, ip(sorted_ids), ip(block_expert),
+                                     ip(num_padded), C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
+    return sorted_ids, block_expert, num_padded
+
+
+def _moe_struct(x, gate_up, down, weights, expert_ids, out):
+    import torch
+    code = {torch.bfloat16: STEP_BF16, torch.float16: STEP_F16}.get(x.dtype)
+    if code is None:
+        raise ValueError("moe_forward: x must be bfloat16 or float16")
+    for name, t in (("x", x), ("gate_up", gate_up), ("down", down), ("out", out)):
+        _check_dev(name, t, x.dtype, torch)
+    _check_dev("weights", weights, torch.float32, torch)
+    _check_dev("expert_ids", expert_ids, torch.int32, torch)
+    n, d = x.shape
+    E, two_i, d2 = gate_up.shape
+    if d2 != d or tuple(down.shape) != (E, d, two_i // 2) or expert_ids.dim() != 2 or expert_ids.shape[0] != n \
+            or tuple(weights.shape) != tuple(expert_ids.shape) or tuple(out.shape) != (n, d) or two_i % 2:
+        raise ValueError("moe_forward: shapes must be x [N, D], gate_up [E, 2I, D], down [E, D, I], "
+                         "weights / expert_ids [N, k], out [N, D]")
+    return MoeLayer(dtype=code, n_tokens=n, top_k=expert_ids.shape[1], num_experts=E, hidden=d, inter=two_i // 2,
+                    d_x=x.data_ptr(), d_gate_up=gate_up.data_ptr(), d_down=down.data_ptr(),
+                    d_weights=C.cast(C.c_void_p(weights.data_ptr()), _lib.F32P),
+                    d_expert_ids=C.cast(C.c_void_p(expert_ids.data_ptr()), _lib.I32P), d_out=out.data_ptr())
+
+
+def moe_workspace_bytes(x, gate_up, down, weights, expert_ids, out) -> int:
+    return int(_lib.load().moe_workspace_bytes(C.byref(_moe_struct(x, gate_up, down, weights, expert_ids, out))))
+
+
+def moe_forward(x, gate_up, down, weights, expert_ids, out=None, workspace=None):
+    """The MoE MLP layer through libstep's moe_forward on the current stream. out [N, D] and the
+    uint8 workspace are allocated here when not given (pass both for graph capture)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x)
+    L = _moe_struct(x, gate_up, down, weights, expert_ids, out)
+    lib = _lib.load()
+    need = int(lib.moe_workspace_bytes(C.byref(L)))
+    if need == 0:
+        _moe_raise(lib.moe_forward(C.byref(L), None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace.numel() < need:
+        raise ValueError(f"moe_forward: workspace of {workspace.numel()} bytes, needs {need}")
+    _moe_raise(lib.moe_forward(C.byref(L), C.c_void_p(workspace.data_ptr()), workspace.numel(),
+                               C.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)))
+    return out
 
 
 # ------------------------------------------------------------------------------------------ owner

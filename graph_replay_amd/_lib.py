@@ -1,4 +1,4 @@
-"""ctypes declarations of libstep's C ABI (include/step.h). Argument marshalling only."""
+"""ctypes declarations of libstep's C ABI (include/step.h, include/moe.h). Argument marshalling only."""
 import ctypes as C
 import os
 
@@ -54,6 +54,11 @@ class StepPacked(C.Structure):
         ("h_top_k", I32P), ("h_top_p", F32P)]
 
 
+class MoeLayer(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("dtype", "n_tokens", "top_k", "num_experts", "hidden", "inter")] + [
+        ("d_x", P), ("d_gate_up", P), ("d_down", P), ("d_weights", F32P), ("d_expert_ids", I32P), ("d_out", P)]
+
+
 EXPORTS = {
     "step_workspace_bytes": (C.c_size_t, [C.POINTER(StepConfig)]),
     "step_init": (C.c_int, [C.POINTER(StepConfig), C.POINTER(StepWeights), C.POINTER(StepBuffers), P,
@@ -71,6 +76,11 @@ EXPORTS = {
     "step_device_status": (C.c_int, [P]),
     "step_phase_stamps": (C.c_int, [P, C.c_int32, C.POINTER(C.c_double)]),
     "step_destroy": (None, [P]),
+    "moe_align_rows": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32]),
+    "moe_align": (C.c_int, [I32P, C.c_int32, C.c_int32, C.c_int32, I32P, I32P, I32P, P]),
+    "moe_workspace_bytes": (C.c_size_t, [C.POINTER(MoeLayer)]),
+    "moe_forward": (C.c_int, [C.POINTER(MoeLayer), P, C.c_size_t, P]),
+    "moe_last_error": (C.c_char_p, []),
 }
 
 _lib = None

@@ -1,0 +1,248 @@
+// Mixture-of-experts MLP layer with no host reads: expert grouping and grouped GEMMs.
+//
+// "Removing overhead: fusion, graphs and async scheduling", section "A MoE layer that never asks
+// the host": the N * k (token, slot) assignments are grouped by expert, each group padded to a
+// multiple of BLOCK_M rows, with shapes that depend on N, k, E and BLOCK_M only; then one launch
+// per projection multiplies each BLOCK_M-row block by its expert's weights, padding rows masked.
+//
+//   k_moe_align   the grouping (sorted_ids, block_expert, num_padded), one block: expert counts by
+//                 LDS atomics, the padded group starts by a block scan, then each assignment's
+//                 place = its group's start + the number of earlier assignments of its expert,
+//                 ranked 64 at a time by one wave (same-expert lanes found with one ballot per id
+//                 bit), so the order inside a group is assignment order, as a stable sort gives.
+//   k_moe_gemm    one grouped GEMM on the matrix cores. Block = (16-row group block, tile of
+//                 output columns): the expert's weight rows are the 16-row MFMA operand, the
+//                 block's 16 gathered rows the other one, and the four waves take interleaved
+//                 32-wide K steps whose partial tiles are summed in wave order through LDS.
+//                 GATE_UP: rows from the token (assignment / k); each tile is 8 gate rows and
+//                 the matching 8 up rows, and the epilogue writes SiLU(gate) * up in the dtype,
+//                 one row per assignment (the page's SiLU-and-mul, fused). DOWN: rows from the
+//                 assignment, scaled by its router weight, fp32 rows per assignment.
+//   k_moe_sum     out[t] = the sum of token t's k rows in slot order (ids outside [0, E) add
+//                 nothing), rounded to the dtype.
+//
+// Expert ids outside [0, E) belong to no group. Blocks whose first row lies at or past
+// num_padded exit at once, so the grid is sized for the worst case.
+#pragma once
+#include "common.h"
+#include "gemm.h"
+
+namespace gr {
+
+constexpr int kMoeBlockM = 16;        // rows per group block of the grouped GEMMs
+constexpr int kMoeMaxExperts = 1024;
+constexpr int kMoeAlignThreads = 1024;
+constexpr int kMoeStage = 4096;       // assignments ranked per LDS pass
+
+__global__ __launch_bounds__(kMoeAlignThreads) void k_moe_align(const int* __restrict__ ids, int total, int E, int bm,
+                                                                int m_max, int* __restrict__ sorted_ids,
+                                                                int* __restrict__ block_expert, int* __restrict__ num_padded) {
+  __shared__ int cnt[kMoeMaxExperts], pstart[kMoeMaxExperts], run[kMoeMaxExperts];
+  __shared__ int wsum[kMoeAlignThreads / 64];
+  __shared__ int stage[kMoeStage];
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  for (int e = t; e < E; e += kMoeAlignThreads) {
+    cnt[e] = 0;
+    run[e] = 0;
+  }
+  __syncthreads();
+  for (int i = t; i < total; i += kMoeAlignThreads) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the padded counts (E <= kMoeAlignThreads: one expert per thread)
+  const int c = t < E ? cnt[t] : 0;
+  const int pad = (c + bm - 1) / bm * bm;
+  int incl = pad;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += wsum[w];
+  const int start = before + incl - pad;
+  if (t < E) pstart[t] = start;
+  if (t == kMoeAlignThreads - 1) num_padded[0] = before + incl;   // the grand total
+  __syncthreads();
+  const int npad = pstart[E - 1] + (cnt[E - 1] + bm - 1) / bm * bm;
+  // padding rows of each group and the blocks each group owns
+  if (t < E) {
+    for (int r = start + c; r < start + pad; ++r) sorted_ids[r] = total;
+    for (int b = start / bm; b < (start + pad) / bm; ++b) block_expert[b] = t;
+  }
+  for (int r = npad + t; r < m_max; r += kMoeAlignThreads) sorted_ids[r] = total;
+  for (int b = npad / bm + t; b < m_max / bm; b += kMoeAlignThreads) block_expert[b] = E - 1;
+  // places of the assignments, in assignment order
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  for (int c0 = 0; c0 < total; c0 += kMoeStage) {
+    const int n = min(kMoeStage, total - c0);
+    for (int i = t; i < n; i += kMoeAlignThreads) stage[i] = ids[c0 + i];
+    __syncthreads();
+    if (wid == 0) {
+      const unsigned long long lt = (1ull << lane) - 1ull;
+      for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const int e = i < n ? stage[i] : -1;
+        const bool ok = e >= 0 && e < E;
+        unsigned long long peers = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = ok && ((e >> b) & 1);
+          const unsigned long long m = __ballot(bit);
+          peers &= bit ? m : ~m;
+        }
+        const int r0 = ok ? run[e] : 0;
+        if (ok) {
+          sorted_ids[pstart[e] + r0 + __popcll(peers & lt)] = c0 + i;
+          if ((peers & lt) == 0ull) run[e] = r0 + __popcll(peers);   // the group's lowest lane
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+struct MoeGemmArgs {
+  const void* W;              // [E][wrows][K] expert weights
+  const void* A;              // GATE_UP: token rows [N][K]; DOWN: activation rows [N * k][K]
+  const int* sorted_ids;      // [m_max]
+  const int* block_expert;    // [m_max / 16]
+  const int* num_padded;      // [1]
+  const float* weights;       // DOWN: router weight per assignment [N * k]
+  void* out;                  // GATE_UP: activation rows (dtype) [N * k][ncols]; DOWN: fp32 rows [N * k][ncols]
+  int ncols;                  // output columns: the expert width I (GATE_UP) or the hidden size D (DOWN)
+  int K;                      // reduction length, a multiple of 32
+  int total, top_k;
+};
+
+// RT tiles per block; GATE_UP tiles are 8 output columns (8 gate + 8 up weight rows), DOWN tiles 16.
+template <class T, bool GATE_UP, int RT, int UN>
+__global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
+  using S = typename T::S;
+  __shared__ f32x4_t part[4][RT][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * kMoeBlockM;
+  if (m0 >= a.num_padded[0]) return;
+  const int K = a.K;
+  const int wrows = GATE_UP ? 2 * a.ncols : a.ncols;
+  const int expert = a.block_expert[blockIdx.x];
+  const S* W = static_cast<const S*>(a.W) + static_cast<size_t>(expert) * wrows * K;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  const int koff = 8 * (lane >> 4);
+  // this lane's weight row in each tile (clamped in bounds; rows past the end are zeroed)
+  const S* wp[RT];
+  bool wok[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int wrow;
+    if (GATE_UP) {
+      const int j = (blockIdx.y * RT + r) * 8 + (lane & 7);
+      wrow = ((lane & 15) < 8) ? j : a.ncols + j;
+      wok[r] = j < a.ncols;
+    } else {
+      wrow = (blockIdx.y * RT + r) * 16 + (lane & 15);
+      wok[r] = wrow < a.ncols;
+    }
+    wp[r] = W + static_cast<size_t>(min(wrow, wrows - 1)) * K + koff;
+  }
+  // this lane's gathered row (the group block's row lane % 16); padding rows read row 0, zeroed
+  const int asg = a.sorted_ids[m0 + (lane & 15)];
+  const bool aok = asg < a.total;
+  const int src = aok ? (GATE_UP ? asg / a.top_k : asg) : 0;
+  const S* ap = static_cast<const S*>(a.A) + static_cast<size_t>(src) * K + koff;
+
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ksteps = K / 32;
+  int ks = wid;
+  for (; ks + 4 * (UN - 1) < ksteps; ks += 4 * UN) {
+    uint4 wv[UN][RT], av[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int k = (ks + 4 * u) * 32;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        wv[u][r] = *reinterpret_cast<const uint4*>(wp[r] + k);
+        if (!wok[r]) wv[u][r] = zero4;
+      }
+      av[u] = *reinterpret_cast<const uint4*>(ap + k);
+      if (!aok) av[u] = zero4;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] = mfma16x16x32<T>(wv[u][r], av[u], acc[r]);
+  }
+  for (; ks < ksteps; ks += 4) {
+    const int k = ks * 32;
+    uint4 wv[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      wv[r] = *reinterpret_cast<const uint4*>(wp[r] + k);
+      if (!wok[r]) wv[r] = zero4;
+    }
+    uint4 av = *reinterpret_cast<const uint4*>(ap + k);
+    if (!aok) av = zero4;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = mfma16x16x32<T>(wv[r], av, acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < RT; ++r) part[wid][r][lane] = acc[r];
+  __syncthreads();
+  // wave r finishes tile r (RT <= 4), summing the four waves in order
+  const int r = wid;
+  if (r >= RT) return;
+  f32x4_t sum = part[0][r][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) sum += part[w][r][lane];
+  const int row = lane & 15;          // the group block's row (one assignment)
+  const int cb = 4 * (lane >> 4);     // first of the 4 weight rows this lane holds
+  // the assignment of this lane's column (the MFMA result holds weight rows x block rows)
+  if (GATE_UP) {
+    // lanes 0..31 hold gate rows 0..7 of the tile, lanes 32..63 the matching up rows
+    f32x4_t up;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) up[i] = __shfl(sum[i], lane + 32, 64);
+    if (lane < 32 && aok) {
+      S* out = static_cast<S*>(a.out) + static_cast<size_t>(asg) * a.ncols;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = (blockIdx.y * RT + r) * 8 + cb + i;
+        if (j < a.ncols) out[j] = T::from_f(silu(sum[i]) * up[i]);
+      }
+    }
+  } else if (aok) {
+    const float wgt = a.weights[asg];
+    float* out = static_cast<float*>(a.out) + static_cast<size_t>(asg) * a.ncols;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = (blockIdx.y * RT + r) * 16 + cb + i;
+      if (n < a.ncols) out[n] = sum[i] * wgt;
+    }
+  }
+  (void)row;
+}
+
+// out[t][c] = sum over slots j of rows[t * k + j][c] (valid experts only), in slot order.
+template <class T>
+__global__ __launch_bounds__(256) void k_moe_sum(const float* __restrict__ rows, const int* __restrict__ ids, int k,
+                                                 int E, int D, void* __restrict__ out) {
+  using S = typename T::S;
+  const int tk = blockIdx.x;
+  S* o = static_cast<S*>(out) + static_cast<size_t>(tk) * D;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[tk * k + j];
+      if (e >= 0 && e < E) s += rows[(static_cast<size_t>(tk) * k + j) * D + c];
+    }
+    o[c] = T::from_f(s);
+  }
+}
+
+}  // namespace gr

@@ -1,0 +1,162 @@
+// C ABI of the mixture-of-experts layer (include/moe.h): argument checks, the workspace layout,
+// and the four launches of moe.h's kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "moe.h"
+#include "../../include/moe.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct MoeLayout {
+  size_t sorted, bexp, npad, act, rows, total;
+  int m_max;
+};
+
+// -1 when out of range
+long long rows_for(long long total, long long E, long long bm) {
+  if (total < 0 || E < 1 || E > MOE_MAX_EXPERTS || bm < 1 || bm > 65536) return -1;
+  const long long m = total + E * (bm - 1);
+  const long long r = (m + bm - 1) / bm * bm;
+  return r > 0x7fffffffLL ? -1 : r;
+}
+
+// checks a layer's sizes; fills the workspace layout
+int check_layer(const moe_layer* L, MoeLayout* lay) {
+  if (!L) return fail(STEP_EINVAL, "layer is NULL");
+  if (L->dtype != STEP_BF16 && L->dtype != STEP_F16)
+    return fail(STEP_EUNSUPPORTED, "moe dtype %d: only STEP_BF16 and STEP_F16 have kernels", L->dtype);
+  if (L->n_tokens < 0 || L->top_k < 1 || L->num_experts < 1 || L->num_experts > MOE_MAX_EXPERTS)
+    return fail(STEP_EINVAL, "moe sizes: n_tokens %d, top_k %d, num_experts %d (1..%d)", L->n_tokens, L->top_k,
+                L->num_experts, MOE_MAX_EXPERTS);
+  if (L->hidden <= 0 || L->hidden % 32 || L->inter <= 0 || L->inter % 32)
+    return fail(STEP_EINVAL, "moe hidden %d and inter %d must be positive multiples of 32", L->hidden, L->inter);
+  const long long total = static_cast<long long>(L->n_tokens) * L->top_k;
+  if (total > 0x7fffffffLL) return fail(STEP_EINVAL, "n_tokens * top_k does not fit an int32");
+  const long long m = rows_for(total, L->num_experts, MOE_BLOCK_M);
+  if (m < 0) return fail(STEP_EINVAL, "grouped rows do not fit an int32");
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  lay->m_max = static_cast<int>(m);
+  lay->sorted = take(sizeof(int32_t) * static_cast<size_t>(m));
+  lay->bexp = take(sizeof(int32_t) * static_cast<size_t>(m / MOE_BLOCK_M));
+  lay->npad = take(sizeof(int32_t));
+  lay->act = take(2 * static_cast<size_t>(total) * L->inter);
+  lay->rows = take(sizeof(float) * static_cast<size_t>(total) * L->hidden);
+  lay->total = off;
+  return STEP_OK;
+}
+
+int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? STEP_OK : fail(STEP_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+int align_launch(const int32_t* ids, int total, int E, int bm, int m_max, int32_t* sorted, int32_t* bexp,
+                 int32_t* npad, hipStream_t s) {
+  hipLaunchKernelGGL(gr::k_moe_align, dim3(1), dim3(gr::kMoeAlignThreads), 0, s, ids, total, E, bm, m_max, sorted, bexp,
+                     npad);
+  return launched("moe align");
+}
+
+template <class T>
+int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
+  const int total = L->n_tokens * L->top_k;
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + lay.bexp);
+  int32_t* npad = reinterpret_cast<int32_t*>(ws + lay.npad);
+  int rc = align_launch(L->d_expert_ids, total, L->num_experts, MOE_BLOCK_M, lay.m_max, sorted, bexp, npad, s);
+  if (rc != STEP_OK) return rc;
+  const int mblocks = lay.m_max / MOE_BLOCK_M;
+  gr::MoeGemmArgs g{};
+  g.sorted_ids = sorted;
+  g.block_expert = bexp;
+  g.num_padded = npad;
+  g.total = total;
+  g.top_k = L->top_k;
+  // gate|up: K = hidden, 8 activation columns per tile, 4 tiles per block
+  constexpr int RT = 4;
+  g.W = L->d_gate_up;
+  g.A = L->d_x;
+  g.out = ws + lay.act;
+  g.ncols = L->inter;
+  g.K = L->hidden;
+  hipLaunchKernelGGL((gr::k_moe_gemm<T, true, RT, 4>), dim3(mblocks, (L->inter + 8 * RT - 1) / (8 * RT)), dim3(256), 0,
+                     s, g);
+  if ((rc = launched("moe gate|up")) != STEP_OK) return rc;
+  // down: K = inter, 16 output columns per tile
+  g.W = L->d_down;
+  g.A = ws + lay.act;
+  g.out = ws + lay.rows;
+  g.weights = L->d_weights;
+  g.ncols = L->hidden;
+  g.K = L->inter;
+  hipLaunchKernelGGL((gr::k_moe_gemm<T, false, RT, 2>), dim3(mblocks, (L->hidden + 16 * RT - 1) / (16 * RT)), dim3(256),
+                     0, s, g);
+  if ((rc = launched("moe down")) != STEP_OK) return rc;
+  hipLaunchKernelGGL(gr::k_moe_sum<T>, dim3(L->n_tokens), dim3(256), 0, s,
+                     reinterpret_cast<const float*>(ws + lay.rows), L->d_expert_ids, L->top_k, L->num_experts, L->hidden,
+                     L->d_out);
+  return launched("moe sum");
+}
+
+}  // namespace
+
+extern "C" int32_t moe_align_rows(int32_t total, int32_t num_experts, int32_t block_m) {
+  return static_cast<int32_t>(rows_for(total, num_experts, block_m));
+}
+
+extern "C" int moe_align(const int32_t* d_expert_ids, int32_t total, int32_t num_experts, int32_t block_m,
+                         int32_t* d_sorted_ids, int32_t* d_block_expert, int32_t* d_num_padded, void* stream) {
+  g_err.clear();
+  const long long m = rows_for(total, num_experts, block_m);
+  if (m < 0) return fail(STEP_EINVAL, "moe_align: total %d, num_experts %d (1..%d), block_m %d (1..65536)", total,
+                         num_experts, MOE_MAX_EXPERTS, block_m);
+  if ((total > 0 && !d_expert_ids) || !d_sorted_ids || !d_block_expert || !d_num_padded)
+    return fail(STEP_EINVAL, "moe_align: NULL device pointer");
+  return align_launch(d_expert_ids, total, num_experts, block_m, static_cast<int>(m), d_sorted_ids, d_block_expert,
+                      d_num_padded, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t moe_workspace_bytes(const moe_layer* layer) {
+  MoeLayout lay;
+  if (check_layer(layer, &lay) != STEP_OK) return 0;
+  return lay.total;
+}
+
+extern "C" int moe_forward(const moe_layer* layer, void* d_workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MoeLayout lay;
+  int rc = check_layer(layer, &lay);
+  if (rc != STEP_OK) return rc;
+  if (layer->n_tokens == 0) return STEP_OK;
+  if (!layer->d_x || !layer->d_gate_up || !layer->d_down || !layer->d_weights || !layer->d_expert_ids ||
+      !layer->d_out || !d_workspace)
+    return fail(STEP_EINVAL, "moe_forward: NULL device pointer");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256)
+    return fail(STEP_EINVAL, "moe_forward: workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(STEP_EINVAL, "moe_forward: workspace %zu bytes, needs %zu", workspace_bytes, lay.total);
+  char* ws = static_cast<char*>(d_workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return layer->dtype == STEP_BF16 ? forward<gr::BF16>(layer, ws, lay, s) : forward<gr::F16>(layer, ws, lay, s);
+}
+
+extern "C" const char* moe_last_error(void) { return g_err.c_str(); }

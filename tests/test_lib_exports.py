@@ -1,4 +1,4 @@
-"""The C-ABI library loads on the host and exports every symbol include/step.h declares (no GPU calls)."""
+"""The C-ABI library loads on the host and exports every symbol include/*.h declares (no GPU calls)."""
 import ctypes as C
 import os
 import re
@@ -9,15 +9,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "step.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(step_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in ("step.h", "moe.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b((?:step|moe)_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary_calls():
     names = _declared()
     for n in ("step_init", "step_decode", "step_mixed", "step_sample", "step_workspace_bytes", "step_destroy",
               "step_last_error"):
+        assert n in names
+    for n in ("moe_align", "moe_align_rows", "moe_forward", "moe_workspace_bytes", "moe_last_error"):
         assert n in names
 
 
@@ -91,3 +96,33 @@ def test_persistent_decode_config_is_validated():
     c = cfg(persistent_decode=1, max_batch=2, num_buckets=1)
     c.buckets[0] = 2
     assert g.step_workspace_bytes(c) == 0            # bucket 1 is what the persistent step serves
+
+
+def test_moe_sizes_are_host_only_and_validate():
+    """moe_align_rows and moe_workspace_bytes run on the host; bad sizes give -1 / 0, and the
+    worst-case row count is total + E * (block_m - 1) rounded up to block_m."""
+    import graph_replay_amd._lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libstep.so not built")
+    lib = L.load()
+    assert lib.moe_align_rows(6, 4, 4) == 20
+    assert lib.moe_align_rows(256, 128, 16) == 2176
+    assert lib.moe_align_rows(0, 1, 1) == 0
+    for bad in ((-1, 4, 4), (6, 0, 4), (6, 1025, 4), (6, 4, 0), (2**31 - 8, 1024, 16)):
+        assert lib.moe_align_rows(*bad) == -1, bad
+
+    def layer(**kw):
+        m = L.MoeLayer(dtype=L.STEP_BF16, n_tokens=32, top_k=8, num_experts=128, hidden=2048, inter=768)
+        for k, v in kw.items():
+            setattr(m, k, v)
+        return m
+
+    ws = lib.moe_workspace_bytes(C.byref(layer()))
+    total = 32 * 8
+    assert ws >= 2176 * 4 + 136 * 4 + 4 + total * 768 * 2 + total * 2048 * 4
+    for bad in (dict(dtype=L.STEP_F32), dict(n_tokens=-1), dict(top_k=0), dict(num_experts=0),
+                dict(num_experts=1025), dict(hidden=2047), dict(inter=700), dict(hidden=0)):
+        assert lib.moe_workspace_bytes(C.byref(layer(**bad))) == 0, bad
+    assert lib.moe_forward(C.byref(layer(dtype=L.STEP_F32)), None, 0, None) == L.STEP_EUNSUPPORTED
+    assert b"dtype" in lib.moe_last_error()
+    assert lib.moe_forward(C.byref(layer(inter=700)), None, 0, None) == L.STEP_EINVAL
