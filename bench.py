@@ -6,11 +6,13 @@ prefill, run as one persistent kernel with the sampler inside (--no-persistent: 
 the same JSON line carries the batch-32 workload (contexts uniform in [128, 2048], shuffled paged
 KV, Gumbel-max at T = 1) under "bs32". Inputs are resident in HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-bs32] [--no-mixed] [--no-cpu]
-                    [--no-persistent]
+    python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--no-bs32] [--no-mixed] [--no-moe]
+                    [--no-cpu] [--no-persistent] [--workload both|bs1|bs32|mixed|moe]
 
 The line also carries the Qwen2.5-1.5B-shape mixed step (prefill chunks + decode rows, 544 packed
-tokens) under "mixed": the bucketed plan replayed as a hipGraph against the exact-size eager plan.
+tokens) under "mixed": the bucketed plan replayed as a hipGraph against the exact-size eager plan;
+and under "moe" the Qwen3-30B-A3B expert layer (grouping + two grouped GEMMs + k-sum) at 32 and
+512 tokens, replayed as a graph.
 """
 from __future__ import annotations
 
@@ -312,6 +314,74 @@ def run_mixed(steps: int = 20, warmup: int = 2) -> dict:
     return out
 
 
+def moe_layer_bytes(s, n: int, active: int) -> dict:
+    """Algorithmic HBM bytes of one MoE layer call per kernel: every active expert's weights once,
+    each token row once, the activation rows written then read (dtype), the weighted down rows
+    written then read (fp32), the output written, and the grouping's small int32 arrays."""
+    eb = 2
+    D, I, k = s.hidden, s.inter, s.top_k
+    total = n * k
+    m_max = -(-(total + s.experts * 15) // 16) * 16
+    return {
+        "moe_align": total * 4 + (m_max + m_max // 16 + 1) * 4,
+        "moe_gate_up": active * 2 * I * D * eb + n * D * eb + total * I * eb + m_max * 4,
+        "moe_down": active * D * I * eb + total * I * eb + total * D * 4 + total * 4 + m_max * 4,
+        "moe_sum": total * D * 4 + n * D * eb + total * 4,
+    }
+
+
+def run_moe(steps: int = 50) -> dict:
+    """The Qwen3-30B-A3B expert layer (128 experts, 8 per token, hidden 2048, width 768, bf16) at a
+    32-token decode batch and a 512-token chunk: moe_forward (4 kernels) captured as a graph over
+    static buffers and replayed `steps` times; HBM bytes of the whole call over its time."""
+    import graph_replay_amd as g
+    torch = __import__("torch")
+    from synth import moe as smoe
+    s = smoe.QWEN3_30B_A3B_MOE
+    log("moe weights")
+    gu, dn = (t.cuda() for t in smoe.make_moe_weights(s, 0))
+    out = {"workload": "qwen3-30b-a3b-moe-layer-bf16", "experts": s.experts, "top_k": s.top_k,
+           "hidden": s.hidden, "inter": s.inter, "kernels_per_layer": 4}
+    for n in (32, 512):
+        x = smoe.token_rows(s, n, 3000 + n).cuda()
+        ids, w = smoe.routing(s, n, 3000 + n)
+        d_ids, d_w = torch.as_tensor(ids).cuda(), torch.as_tensor(w).cuda()
+        y = torch.empty_like(x)
+        ws = torch.empty(g.moe_workspace_bytes(x, gu, dn, d_w, d_ids, y), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                g.moe_forward(x, gu, dn, d_w, d_ids, y, ws)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            g.moe_forward(x, gu, dn, d_w, d_ids, y, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            graph.replay()
+            e0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        active = int(np.unique(ids).size)
+        kb = moe_layer_bytes(s, n, active)
+        nbytes = sum(kb.values())
+        flops = 2 * n * s.top_k * 3 * s.inter * s.hidden
+        out[f"n{n}"] = {"tokens": n, "active_experts": active, "us_per_layer": round(us, 2),
+                        "bytes_per_layer": int(nbytes),
+                        "hbm": {"achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+                        "mfma": {"achieved": round(flops / (us * 1e-6) / 1e12, 1), "peak": PEAK_MFMA_F16_TFLOPS,
+                                 "unit": "TFLOP/s"},
+                        "kernel_bytes": kb}
+        log(f"moe n={n}: {us:.1f} us per layer, {active} experts")
+        del graph
+    return out
+
+
 def cpu_baseline(shape, W, budget_s: float = 20.0, ctx_len: int = 1024) -> dict:
     """The oracle (fp32 NumPy, unfused, per request) timed on this host on a bounded sample: decode
     steps of one request over a 1,024-key injected history (same shape as the GPU workload)."""
@@ -350,8 +420,9 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-bs32", action="store_true")
-    ap.add_argument("--workload", choices=["both", "bs1", "bs32", "mixed"], default="both",
-                    help="bs1: the primary line only; bs32 / mixed: that workload only (for profiling)")
+    ap.add_argument("--workload", choices=["both", "bs1", "bs32", "mixed", "moe"], default="both",
+                    help="bs1: the primary line only; bs32 / mixed / moe: that workload only (for profiling)")
+    ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy a 1 GiB device buffer 4 times (calibrates the HBM byte counters)")
@@ -392,10 +463,14 @@ def main():
     if args.workload == "mixed":
         print(json.dumps({"metric": METRIC, **run_mixed()}), flush=True)
         return
+    if args.workload == "moe":
+        print(json.dumps({"metric": METRIC, "moe": run_moe()}), flush=True)
+        return
     r1 = run_bs1(shape, W, args.steps, warmup, weight_prefetch=not args.no_weight_prefetch,
                  persistent=not args.no_persistent)
     r32 = None if (args.no_bs32 or args.workload == "bs1") else run_bs32(shape, W, args.steps, warmup)
     rmix = None if (args.no_mixed or args.workload == "bs1") else run_mixed()
+    rmoe = None if (args.no_moe or args.workload == "bs1") else run_moe()
     cpu = None if args.no_cpu else cpu_baseline(shape, W)
     line = {
         "metric": METRIC, "value": round(r1["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -420,6 +495,8 @@ def main():
                         "roofline": r32["roofline"]}
     if rmix is not None:
         line["mixed"] = rmix
+    if rmoe is not None:
+        line["moe"] = rmoe
     print(json.dumps(line), flush=True)
 
 

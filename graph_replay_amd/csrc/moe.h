@@ -5,15 +5,21 @@
 // multiple of BLOCK_M rows, with shapes that depend on N, k, E and BLOCK_M only; then one launch
 // per projection multiplies each BLOCK_M-row block by its expert's weights, padding rows masked.
 //
-//   k_moe_align   the grouping (sorted_ids, block_expert, num_padded), one block: expert counts by
-//                 LDS atomics, the padded group starts by a block scan, then each assignment's
-//                 place = its group's start + the number of earlier assignments of its expert,
-//                 ranked 64 at a time by one wave (same-expert lanes found with one ballot per id
-//                 bit), so the order inside a group is assignment order, as a stable sort gives.
+//   k_moe_align   the grouping (sorted_ids, block_expert, num_padded), one block of 16 waves.
+//                 The lanes of a wave that hold the same expert are found with one ballot per id
+//                 bit; the group's lowest lane counts the group (one LDS atomic per expert per
+//                 wave). A block scan gives the padded group starts. Then, 1,024 assignments at a
+//                 time, an assignment's place = its group's start + the earlier assignments of its
+//                 expert (earlier chunks, earlier waves of this chunk, earlier lanes of its wave),
+//                 so the order inside a group is assignment order, as a stable sort gives.
 //   k_moe_gemm    one grouped GEMM on the matrix cores. Block = (16-row group block, tile of
 //                 output columns): the expert's weight rows are the 16-row MFMA operand, the
 //                 block's 16 gathered rows the other one, and the four waves take interleaved
-//                 32-wide K steps whose partial tiles are summed in wave order through LDS.
+//                 32-wide K steps whose partial tiles are summed in wave order through LDS. The
+//                 hardware deals workgroups to the 8 XCDs in turn; block ids are renumbered so
+//                 that each XCD takes a contiguous run of (group block, tile) pairs, group blocks
+//                 fastest, so the group blocks of one expert, which read the same weight tile,
+//                 run on one XCD and share its L2.
 //                 GATE_UP: rows from the token (assignment / k); each tile is 8 gate rows and
 //                 the matching 8 up rows, and the epilogue writes SiLU(gate) * up in the dtype,
 //                 one row per assignment (the page's SiLU-and-mul, fused). DOWN: rows from the
@@ -32,23 +38,40 @@ namespace gr {
 constexpr int kMoeBlockM = 16;        // rows per group block of the grouped GEMMs
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeAlignThreads = 1024;
-constexpr int kMoeStage = 4096;       // assignments ranked per LDS pass
+constexpr int kXcds = 8;              // XCDs of an MI355X, each with its own L2
+
+// lanes of this wave holding the same valid expert as this lane (ok: this lane's id is valid);
+// one ballot per bit of the id
+__device__ inline unsigned long long same_expert_lanes(int e, bool ok, int nbits) {
+  unsigned long long peers = __ballot(ok);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = ok && ((e >> b) & 1);
+    const unsigned long long m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
 
 __global__ __launch_bounds__(kMoeAlignThreads) void k_moe_align(const int* __restrict__ ids, int total, int E, int bm,
                                                                 int m_max, int* __restrict__ sorted_ids,
                                                                 int* __restrict__ block_expert, int* __restrict__ num_padded) {
-  __shared__ int cnt[kMoeMaxExperts], pstart[kMoeMaxExperts], run[kMoeMaxExperts];
-  __shared__ int wsum[kMoeAlignThreads / 64];
-  __shared__ int stage[kMoeStage];
+  constexpr int NW = kMoeAlignThreads / 64;
+  __shared__ int cnt[kMoeMaxExperts], pstart[kMoeMaxExperts];
+  __shared__ int wcnt[NW][kMoeMaxExperts];   // per chunk: assignments of each expert in each wave
+  __shared__ int wsum[NW];
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  for (int e = t; e < E; e += kMoeAlignThreads) {
-    cnt[e] = 0;
-    run[e] = 0;
-  }
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  for (int e = t; e < E; e += kMoeAlignThreads) cnt[e] = 0;
   __syncthreads();
-  for (int i = t; i < total; i += kMoeAlignThreads) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // counts: the lowest lane of each same-expert group of a wave adds the group's size
+  for (int c0 = 0; c0 < total; c0 += kMoeAlignThreads) {
+    const int i = c0 + t;
+    const int e = i < total ? ids[i] : -1;
+    const bool ok = e >= 0 && e < E;
+    const unsigned long long peers = same_expert_lanes(e, ok, nbits);
+    if (ok && (peers & lt) == 0ull) atomicAdd(&cnt[e], __popcll(peers));
   }
   __syncthreads();
   // exclusive scan of the padded counts (E <= kMoeAlignThreads: one expert per thread)
@@ -76,32 +99,29 @@ __global__ __launch_bounds__(kMoeAlignThreads) void k_moe_align(const int* __res
   }
   for (int r = npad + t; r < m_max; r += kMoeAlignThreads) sorted_ids[r] = total;
   for (int b = npad / bm + t; b < m_max / bm; b += kMoeAlignThreads) block_expert[b] = E - 1;
-  // places of the assignments, in assignment order
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
-  for (int c0 = 0; c0 < total; c0 += kMoeStage) {
-    const int n = min(kMoeStage, total - c0);
-    for (int i = t; i < n; i += kMoeAlignThreads) stage[i] = ids[c0 + i];
+  // places, one chunk of kMoeAlignThreads assignments at a time: place = group start + earlier
+  // assignments of the expert in earlier chunks (run, kept by the expert's thread in pstart) +
+  // in earlier waves of this chunk + in earlier lanes of this wave
+  for (int c0 = 0; c0 < total; c0 += kMoeAlignThreads) {
+    for (int e = lane; e < E; e += 64) wcnt[wid][e] = 0;
     __syncthreads();
-    if (wid == 0) {
-      const unsigned long long lt = (1ull << lane) - 1ull;
-      for (int base = 0; base < n; base += 64) {
-        const int i = base + lane;
-        const int e = i < n ? stage[i] : -1;
-        const bool ok = e >= 0 && e < E;
-        unsigned long long peers = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-          const bool bit = ok && ((e >> b) & 1);
-          const unsigned long long m = __ballot(bit);
-          peers &= bit ? m : ~m;
-        }
-        const int r0 = ok ? run[e] : 0;
-        if (ok) {
-          sorted_ids[pstart[e] + r0 + __popcll(peers & lt)] = c0 + i;
-          if ((peers & lt) == 0ull) run[e] = r0 + __popcll(peers);   // the group's lowest lane
-        }
+    const int i = c0 + t;
+    const int e = i < total ? ids[i] : -1;
+    const bool ok = e >= 0 && e < E;
+    const unsigned long long peers = same_expert_lanes(e, ok, nbits);
+    if (ok && (peers & lt) == 0ull) wcnt[wid][e] = __popcll(peers);
+    __syncthreads();
+    if (t < E) {   // expert t: exclusive prefix over the waves, from its running place
+      int run = pstart[t];
+      for (int w = 0; w < NW; ++w) {
+        const int v = wcnt[w][t];
+        wcnt[w][t] = run;
+        run += v;
       }
+      pstart[t] = run;
     }
+    __syncthreads();
+    if (ok) sorted_ids[wcnt[wid][e] + __popcll(peers & lt)] = i;
     __syncthreads();
   }
 }
@@ -117,6 +137,7 @@ struct MoeGemmArgs {
   int ncols;                  // output columns: the expert width I (GATE_UP) or the hidden size D (DOWN)
   int K;                      // reduction length, a multiple of 32
   int total, top_k;
+  int mblocks;                // group blocks in the grid (m_max / 16); gridDim.x = mblocks * tiles
 };
 
 // RT tiles per block; GATE_UP tiles are 8 output columns (8 gate + 8 up weight rows), DOWN tiles 16.
@@ -125,11 +146,16 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
   using S = typename T::S;
   __shared__ f32x4_t part[4][RT][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * kMoeBlockM;
+  // workgroup b runs on XCD b % 8 as the (b / 8)-th of that XCD's share; XCD x's share is the
+  // contiguous run of logical ids starting at x * (nb / 8) + min(x, nb % 8)
+  const int nb = gridDim.x, xcd = blockIdx.x % kXcds, per = nb / kXcds, rem = nb % kXcds;
+  const int logical = xcd * per + min(xcd, rem) + static_cast<int>(blockIdx.x) / kXcds;
+  const int mb = logical % a.mblocks, nt = logical / a.mblocks;
+  const int m0 = mb * kMoeBlockM;
   if (m0 >= a.num_padded[0]) return;
   const int K = a.K;
   const int wrows = GATE_UP ? 2 * a.ncols : a.ncols;
-  const int expert = a.block_expert[blockIdx.x];
+  const int expert = a.block_expert[mb];
   const S* W = static_cast<const S*>(a.W) + static_cast<size_t>(expert) * wrows * K;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   const int koff = 8 * (lane >> 4);
@@ -140,11 +166,11 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
   for (int r = 0; r < RT; ++r) {
     int wrow;
     if (GATE_UP) {
-      const int j = (blockIdx.y * RT + r) * 8 + (lane & 7);
+      const int j = (nt * RT + r) * 8 + (lane & 7);
       wrow = ((lane & 15) < 8) ? j : a.ncols + j;
       wok[r] = j < a.ncols;
     } else {
-      wrow = (blockIdx.y * RT + r) * 16 + (lane & 15);
+      wrow = (nt * RT + r) * 16 + (lane & 15);
       wok[r] = wrow < a.ncols;
     }
     wp[r] = W + static_cast<size_t>(min(wrow, wrows - 1)) * K + koff;
@@ -212,7 +238,7 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
       S* out = static_cast<S*>(a.out) + static_cast<size_t>(asg) * a.ncols;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = (blockIdx.y * RT + r) * 8 + cb + i;
+        const int j = (nt * RT + r) * 8 + cb + i;
         if (j < a.ncols) out[j] = T::from_f(silu(sum[i]) * up[i]);
       }
     }
@@ -221,28 +247,48 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
     float* out = static_cast<float*>(a.out) + static_cast<size_t>(asg) * a.ncols;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int n = (blockIdx.y * RT + r) * 16 + cb + i;
+      const int n = (nt * RT + r) * 16 + cb + i;
       if (n < a.ncols) out[n] = sum[i] * wgt;
     }
   }
   (void)row;
 }
 
-// out[t][c] = sum over slots j of rows[t * k + j][c] (valid experts only), in slot order.
+// out[t][c] = sum over slots j of rows[t * k + j][c] (valid experts only), in slot order; four
+// columns per thread, grid (tokens, D / 1024 rounded up), every slot's load issued at once.
 template <class T>
 __global__ __launch_bounds__(256) void k_moe_sum(const float* __restrict__ rows, const int* __restrict__ ids, int k,
                                                  int E, int D, void* __restrict__ out) {
   using S = typename T::S;
   const int tk = blockIdx.x;
-  S* o = static_cast<S*>(out) + static_cast<size_t>(tk) * D;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) {
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= D) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int KU = 8;
+  for (int j0 = 0; j0 < k; j0 += KU) {
+    float4 v[KU];
+    bool ok[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = min(j0 + u, k - 1);
       const int e = ids[tk * k + j];
-      if (e >= 0 && e < E) s += rows[(static_cast<size_t>(tk) * k + j) * D + c];
+      ok[u] = j0 + u < k && e >= 0 && e < E;
+      v[u] = *reinterpret_cast<const float4*>(rows + (static_cast<size_t>(tk) * k + j) * D + c);
     }
-    o[c] = T::from_f(s);
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+      if (ok[u]) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+        s.z += v[u].z;
+        s.w += v[u].w;
+      }
   }
+  S* o = static_cast<S*>(out) + static_cast<size_t>(tk) * D + c;
+  o[0] = T::from_f(s.x);
+  o[1] = T::from_f(s.y);
+  o[2] = T::from_f(s.z);
+  o[3] = T::from_f(s.w);
 }
 
 }  // namespace gr

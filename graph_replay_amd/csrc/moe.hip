@@ -91,6 +91,7 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   g.num_padded = npad;
   g.total = total;
   g.top_k = L->top_k;
+  g.mblocks = mblocks;
   // gate|up: K = hidden, 8 activation columns per tile, 4 tiles per block
   constexpr int RT = 4;
   g.W = L->d_gate_up;
@@ -98,8 +99,8 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   g.out = ws + lay.act;
   g.ncols = L->inter;
   g.K = L->hidden;
-  hipLaunchKernelGGL((gr::k_moe_gemm<T, true, RT, 4>), dim3(mblocks, (L->inter + 8 * RT - 1) / (8 * RT)), dim3(256), 0,
-                     s, g);
+  hipLaunchKernelGGL((gr::k_moe_gemm<T, true, RT, 4>), dim3(mblocks * ((L->inter + 8 * RT - 1) / (8 * RT))), dim3(256),
+                     0, s, g);
   if ((rc = launched("moe gate|up")) != STEP_OK) return rc;
   // down: K = inter, 16 output columns per tile
   g.W = L->d_down;
@@ -108,10 +109,10 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   g.weights = L->d_weights;
   g.ncols = L->hidden;
   g.K = L->inter;
-  hipLaunchKernelGGL((gr::k_moe_gemm<T, false, RT, 2>), dim3(mblocks, (L->hidden + 16 * RT - 1) / (16 * RT)), dim3(256),
-                     0, s, g);
+  hipLaunchKernelGGL((gr::k_moe_gemm<T, false, RT, 2>), dim3(mblocks * ((L->hidden + 16 * RT - 1) / (16 * RT))),
+                     dim3(256), 0, s, g);
   if ((rc = launched("moe down")) != STEP_OK) return rc;
-  hipLaunchKernelGGL(gr::k_moe_sum<T>, dim3(L->n_tokens), dim3(256), 0, s,
+  hipLaunchKernelGGL(gr::k_moe_sum<T>, dim3(L->n_tokens, (L->hidden + 1023) / 1024), dim3(256), 0, s,
                      reinterpret_cast<const float*>(ws + lay.rows), L->d_expert_ids, L->top_k, L->num_experts, L->hidden,
                      L->d_out);
   return launched("moe sum");
