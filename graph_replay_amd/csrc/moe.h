@@ -15,15 +15,17 @@
 //   k_moe_gemm    one grouped GEMM on the matrix cores. Block = (16-row group block, tile of
 //                 output columns): the expert's weight rows are the 16-row MFMA operand, the
 //                 block's 16 gathered rows the other one, and the four waves take interleaved
-//                 32-wide K steps whose partial tiles are summed in wave order through LDS. The
-//                 hardware deals workgroups to the 8 XCDs in turn; block ids are renumbered so
-//                 that each XCD takes a contiguous run of (group block, tile) pairs, group blocks
-//                 fastest, so the group blocks of one expert, which read the same weight tile,
-//                 run on one XCD and share its L2.
+//                 32-wide K steps whose partial tiles are summed in wave order through LDS. When
+//                 experts average 32 rows or more, one workgroup takes up to 4 group blocks of an
+//                 expert, so a weight fragment feeds up to 4 products. The hardware deals
+//                 workgroups to the 8 XCDs in turn: XCD x takes group blocks x, x + 8, ... and all
+//                 output tiles of each, so a block's input rows stay in one L2 and the live
+//                 blocks spread evenly over the XCDs.
 //                 GATE_UP: rows from the token (assignment / k); each tile is 8 gate rows and
-//                 the matching 8 up rows, and the epilogue writes SiLU(gate) * up in the dtype,
-//                 one row per assignment (the page's SiLU-and-mul, fused). DOWN: rows from the
-//                 assignment, scaled by its router weight, fp32 rows per assignment.
+//                 the matching 8 up rows, and the epilogue writes SiLU(gate) * up in the dtype
+//                 (the page's SiLU-and-mul, fused), one row per grouped row, so the next GEMM
+//                 reads each block's rows contiguously. DOWN: rows in grouped order, scaled by
+//                 the router weight, written as fp32 rows in assignment order.
 //   k_moe_sum     out[t] = the sum of token t's k rows in slot order (ids outside [0, E) add
 //                 nothing), rounded to the dtype.
 //
@@ -54,7 +56,8 @@ __device__ inline unsigned long long same_expert_lanes(int e, bool ok, int nbits
 
 __global__ __launch_bounds__(kMoeAlignThreads) void k_moe_align(const int* __restrict__ ids, int total, int E, int bm,
                                                                 int m_max, int* __restrict__ sorted_ids,
-                                                                int* __restrict__ block_expert, int* __restrict__ num_padded) {
+                                                                int* __restrict__ block_expert, int* __restrict__ num_padded,
+                                                                int* __restrict__ block_rank) {
   constexpr int NW = kMoeAlignThreads / 64;
   __shared__ int cnt[kMoeMaxExperts], pstart[kMoeMaxExperts];
   __shared__ int wcnt[NW][kMoeMaxExperts];   // per chunk: assignments of each expert in each wave
@@ -95,10 +98,16 @@ __global__ __launch_bounds__(kMoeAlignThreads) void k_moe_align(const int* __res
   // padding rows of each group and the blocks each group owns
   if (t < E) {
     for (int r = start + c; r < start + pad; ++r) sorted_ids[r] = total;
-    for (int b = start / bm; b < (start + pad) / bm; ++b) block_expert[b] = t;
+    for (int b = start / bm; b < (start + pad) / bm; ++b) {
+      block_expert[b] = t;
+      if (block_rank) block_rank[b] = b - start / bm;
+    }
   }
   for (int r = npad + t; r < m_max; r += kMoeAlignThreads) sorted_ids[r] = total;
-  for (int b = npad / bm + t; b < m_max / bm; b += kMoeAlignThreads) block_expert[b] = E - 1;
+  for (int b = npad / bm + t; b < m_max / bm; b += kMoeAlignThreads) {
+    block_expert[b] = E - 1;
+    if (block_rank) block_rank[b] = 0;
+  }
   // places, one chunk of kMoeAlignThreads assignments at a time: place = group start + earlier
   // assignments of the expert in earlier chunks (run, kept by the expert's thread in pstart) +
   // in earlier waves of this chunk + in earlier lanes of this wave
@@ -128,31 +137,44 @@ __global__ __launch_bounds__(kMoeAlignThreads) void k_moe_align(const int* __res
 
 struct MoeGemmArgs {
   const void* W;              // [E][wrows][K] expert weights
-  const void* A;              // GATE_UP: token rows [N][K]; DOWN: activation rows [N * k][K]
+  const void* A;              // GATE_UP: token rows [N][K]; DOWN: activation rows [m_max][K] (grouped order)
   const int* sorted_ids;      // [m_max]
   const int* block_expert;    // [m_max / 16]
   const int* num_padded;      // [1]
+  const int* block_rank;      // [m_max / 16] rank of each group block inside its expert's group (MB > 1)
   const float* weights;       // DOWN: router weight per assignment [N * k]
-  void* out;                  // GATE_UP: activation rows (dtype) [N * k][ncols]; DOWN: fp32 rows [N * k][ncols]
+  void* out;                  // GATE_UP: activation rows (dtype) [m_max][ncols] in grouped order;
+                              // DOWN: fp32 rows [N * k][ncols] in assignment order
   int ncols;                  // output columns: the expert width I (GATE_UP) or the hidden size D (DOWN)
   int K;                      // reduction length, a multiple of 32
   int total, top_k;
-  int mblocks;                // group blocks in the grid (m_max / 16); gridDim.x = mblocks * tiles
+  int ntiles;                 // output tiles; gridDim.x = (m_max / 16 rounded up to a multiple of 8) * ntiles
 };
 
 // RT tiles per block; GATE_UP tiles are 8 output columns (8 gate + 8 up weight rows), DOWN tiles 16.
-template <class T, bool GATE_UP, int RT, int UN>
+// MB > 1: the workgroup of a group block whose rank inside its expert's group is a multiple of MB
+// also takes the next MB - 1 group blocks of that group (the others exit), so each weight fragment
+// feeds up to MB products.
+template <class T, bool GATE_UP, int RT, int UN, int MB>
 __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
   using S = typename T::S;
-  __shared__ f32x4_t part[4][RT][64];
+  __shared__ f32x4_t part[4][MB][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  // workgroup b runs on XCD b % 8 as the (b / 8)-th of that XCD's share; XCD x's share is the
-  // contiguous run of logical ids starting at x * (nb / 8) + min(x, nb % 8)
-  const int nb = gridDim.x, xcd = blockIdx.x % kXcds, per = nb / kXcds, rem = nb % kXcds;
-  const int logical = xcd * per + min(xcd, rem) + static_cast<int>(blockIdx.x) / kXcds;
-  const int mb = logical % a.mblocks, nt = logical / a.mblocks;
-  const int m0 = mb * kMoeBlockM;
-  if (m0 >= a.num_padded[0]) return;
+  // workgroup b runs on XCD b % 8 as the (b / 8)-th of that XCD's share: XCD x takes the group
+  // blocks x, x + 8, ... and, for each, every tile in turn
+  const int xcd = blockIdx.x % kXcds, slot = static_cast<int>(blockIdx.x) / kXcds;
+  const int mb = xcd + kXcds * (slot / a.ntiles), nt = slot % a.ntiles;
+  const int npad = a.num_padded[0];
+  if (mb * kMoeBlockM >= npad) return;
+  int cnt = 1;   // group blocks of this workgroup
+  if constexpr (MB > 1) {
+    const int rank = a.block_rank[mb];
+    if (rank % MB) return;
+    for (int i = 1; i < MB; ++i) {
+      if ((mb + i) * kMoeBlockM >= npad || a.block_rank[mb + i] != rank + i) break;
+      cnt = i + 1;
+    }
+  }
   const int K = a.K;
   const int wrows = GATE_UP ? 2 * a.ncols : a.ncols;
   const int expert = a.block_expert[mb];
@@ -175,19 +197,30 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
     }
     wp[r] = W + static_cast<size_t>(min(wrow, wrows - 1)) * K + koff;
   }
-  // this lane's gathered row (the group block's row lane % 16); padding rows read row 0, zeroed
-  const int asg = a.sorted_ids[m0 + (lane & 15)];
-  const bool aok = asg < a.total;
-  const int src = aok ? (GATE_UP ? asg / a.top_k : asg) : 0;
-  const S* ap = static_cast<const S*>(a.A) + static_cast<size_t>(src) * K + koff;
-
-  f32x4_t acc[RT];
+  // this lane's gathered row in each group block (row lane % 16); padding rows and group blocks
+  // past cnt read row 0, zeroed
+  // (GATE_UP: the token's row; DOWN: the activation row, stored in grouped order)
+  int asg[MB];
+  bool aok[MB];
+  const S* ap[MB];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MB; ++i) {
+    const int grow = (mb + i) * kMoeBlockM + (lane & 15);
+    asg[i] = i < cnt ? a.sorted_ids[grow] : a.total;
+    aok[i] = asg[i] < a.total;
+    const int src = aok[i] ? (GATE_UP ? asg[i] / a.top_k : grow) : 0;
+    ap[i] = static_cast<const S*>(a.A) + static_cast<size_t>(src) * K + koff;
+  }
+
+  f32x4_t acc[RT][MB];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[r][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int ksteps = K / 32;
   int ks = wid;
   for (; ks + 4 * (UN - 1) < ksteps; ks += 4 * UN) {
-    uint4 wv[UN][RT], av[UN];
+    uint4 wv[UN][RT], av[UN][MB];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int k = (ks + 4 * u) * 32;
@@ -196,62 +229,88 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeGemmArgs a) {
         wv[u][r] = *reinterpret_cast<const uint4*>(wp[r] + k);
         if (!wok[r]) wv[u][r] = zero4;
       }
-      av[u] = *reinterpret_cast<const uint4*>(ap + k);
-      if (!aok) av[u] = zero4;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        av[u][i] = zero4;
+        if (i < cnt) av[u][i] = *reinterpret_cast<const uint4*>(ap[i] + k);
+        if (!aok[i]) av[u][i] = zero4;
+      }
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) acc[r] = mfma16x16x32<T>(wv[u][r], av[u], acc[r]);
+      for (int i = 0; i < MB; ++i)
+        if (i < cnt)
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r][i] = mfma16x16x32<T>(wv[u][r], av[u][i], acc[r][i]);
   }
   for (; ks < ksteps; ks += 4) {
     const int k = ks * 32;
-    uint4 wv[RT];
+    uint4 wv[RT], av[MB];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       wv[r] = *reinterpret_cast<const uint4*>(wp[r] + k);
       if (!wok[r]) wv[r] = zero4;
     }
-    uint4 av = *reinterpret_cast<const uint4*>(ap + k);
-    if (!aok) av = zero4;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r] = mfma16x16x32<T>(wv[r], av, acc[r]);
+    for (int i = 0; i < MB; ++i) {
+      av[i] = zero4;
+      if (i < cnt) av[i] = *reinterpret_cast<const uint4*>(ap[i] + k);
+      if (!aok[i]) av[i] = zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (i < cnt)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r][i] = mfma16x16x32<T>(wv[r], av[i], acc[r][i]);
   }
+  // tile by tile, the four waves' partial sums meet in LDS and wave r keeps tile r's sum (RT <= 4)
+  f32x4_t sum[MB];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) part[wid][r][lane] = acc[r];
-  __syncthreads();
-  // wave r finishes tile r (RT <= 4), summing the four waves in order
-  const int r = wid;
-  if (r >= RT) return;
-  f32x4_t sum = part[0][r][lane];
+  for (int r = 0; r < RT; ++r) {
 #pragma unroll
-  for (int w = 1; w < 4; ++w) sum += part[w][r][lane];
-  const int row = lane & 15;          // the group block's row (one assignment)
-  const int cb = 4 * (lane >> 4);     // first of the 4 weight rows this lane holds
-  // the assignment of this lane's column (the MFMA result holds weight rows x block rows)
-  if (GATE_UP) {
-    // lanes 0..31 hold gate rows 0..7 of the tile, lanes 32..63 the matching up rows
-    f32x4_t up;
+    for (int i = 0; i < MB; ++i) part[wid][i][lane] = acc[r][i];
+    __syncthreads();
+    if (wid == r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) up[i] = __shfl(sum[i], lane + 32, 64);
-    if (lane < 32 && aok) {
-      S* out = static_cast<S*>(a.out) + static_cast<size_t>(asg) * a.ncols;
+      for (int i = 0; i < MB; ++i) {
+        sum[i] = part[0][i][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = (nt * RT + r) * 8 + cb + i;
-        if (j < a.ncols) out[j] = T::from_f(silu(sum[i]) * up[i]);
+        for (int w = 1; w < 4; ++w) sum[i] += part[w][i][lane];
       }
     }
-  } else if (aok) {
-    const float wgt = a.weights[asg];
-    float* out = static_cast<float*>(a.out) + static_cast<size_t>(asg) * a.ncols;
+    __syncthreads();
+  }
+  const int r = wid;
+  if (r >= RT) return;
+  const int cb = 4 * (lane >> 4);     // first of the 4 weight rows this lane holds
+  // the MFMA result holds weight rows (4 per lane) x group-block rows (lane % 16: one assignment)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = (nt * RT + r) * 16 + cb + i;
-      if (n < a.ncols) out[n] = sum[i] * wgt;
+  for (int i = 0; i < MB; ++i) {
+    if (i >= cnt) break;
+    if (GATE_UP) {
+      // lanes 0..31 hold gate rows 0..7 of the tile, lanes 32..63 the matching up rows
+      f32x4_t up;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) up[q] = __shfl(sum[i][q], lane + 32, 64);
+      if (lane < 32 && aok[i]) {
+        S* out = static_cast<S*>(a.out) + static_cast<size_t>((mb + i) * kMoeBlockM + (lane & 15)) * a.ncols;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = (nt * RT + r) * 8 + cb + q;
+          if (j < a.ncols) out[j] = T::from_f(silu(sum[i][q]) * up[q]);
+        }
+      }
+    } else if (aok[i]) {
+      const float wgt = a.weights[asg[i]];
+      float* out = static_cast<float*>(a.out) + static_cast<size_t>(asg[i]) * a.ncols;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = (nt * RT + r) * 16 + cb + q;
+        if (n < a.ncols) out[n] = sum[i][q] * wgt;
+      }
     }
   }
-  (void)row;
 }
 
 // out[t][c] = sum over slots j of rows[t * k + j][c] (valid experts only), in slot order; four

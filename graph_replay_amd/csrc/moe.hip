@@ -26,7 +26,7 @@ int fail(int code, const char* fmt, ...) {
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct MoeLayout {
-  size_t sorted, bexp, npad, act, rows, total;
+  size_t sorted, bexp, brank, npad, act, rows, total;
   int m_max;
 };
 
@@ -57,8 +57,9 @@ int check_layer(const moe_layer* L, MoeLayout* lay) {
   lay->m_max = static_cast<int>(m);
   lay->sorted = take(sizeof(int32_t) * static_cast<size_t>(m));
   lay->bexp = take(sizeof(int32_t) * static_cast<size_t>(m / MOE_BLOCK_M));
+  lay->brank = take(sizeof(int32_t) * static_cast<size_t>(m / MOE_BLOCK_M));
   lay->npad = take(sizeof(int32_t));
-  lay->act = take(2 * static_cast<size_t>(total) * L->inter);
+  lay->act = take(2 * static_cast<size_t>(m) * L->inter);   // grouped order, padding rows included
   lay->rows = take(sizeof(float) * static_cast<size_t>(total) * L->hidden);
   lay->total = off;
   return STEP_OK;
@@ -70,9 +71,9 @@ int launched(const char* what) {
 }
 
 int align_launch(const int32_t* ids, int total, int E, int bm, int m_max, int32_t* sorted, int32_t* bexp,
-                 int32_t* npad, hipStream_t s) {
+                 int32_t* npad, int32_t* brank, hipStream_t s) {
   hipLaunchKernelGGL(gr::k_moe_align, dim3(1), dim3(gr::kMoeAlignThreads), 0, s, ids, total, E, bm, m_max, sorted, bexp,
-                     npad);
+                     npad, brank);
   return launched("moe align");
 }
 
@@ -82,16 +83,19 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + lay.bexp);
   int32_t* npad = reinterpret_cast<int32_t*>(ws + lay.npad);
-  int rc = align_launch(L->d_expert_ids, total, L->num_experts, MOE_BLOCK_M, lay.m_max, sorted, bexp, npad, s);
+  int32_t* brank = reinterpret_cast<int32_t*>(ws + lay.brank);
+  int rc = align_launch(L->d_expert_ids, total, L->num_experts, MOE_BLOCK_M, lay.m_max, sorted, bexp, npad, brank, s);
   if (rc != STEP_OK) return rc;
-  const int mblocks = lay.m_max / MOE_BLOCK_M;
+  // group blocks in the grid: a multiple of 8, so every XCD gets the same share (the extra blocks
+  // lie past the used rows and exit)
+  const int mblocks = (lay.m_max / MOE_BLOCK_M + gr::kXcds - 1) / gr::kXcds * gr::kXcds;
   gr::MoeGemmArgs g{};
   g.sorted_ids = sorted;
   g.block_expert = bexp;
   g.num_padded = npad;
+  g.block_rank = brank;
   g.total = total;
   g.top_k = L->top_k;
-  g.mblocks = mblocks;
   // gate|up: K = hidden, 8 activation columns per tile, 4 tiles per block
   constexpr int RT = 4;
   g.W = L->d_gate_up;
@@ -99,8 +103,14 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   g.out = ws + lay.act;
   g.ncols = L->inter;
   g.K = L->hidden;
-  hipLaunchKernelGGL((gr::k_moe_gemm<T, true, RT, 4>), dim3(mblocks * ((L->inter + 8 * RT - 1) / (8 * RT))), dim3(256),
-                     0, s, g);
+  // when experts average 32 rows or more, one workgroup takes up to 4 group blocks of an expert
+  const bool multi = total >= 32 * L->num_experts;
+  g.ntiles = (L->inter + 8 * RT - 1) / (8 * RT);
+  const dim3 gu_grid(mblocks * g.ntiles);
+  if (multi)
+    hipLaunchKernelGGL((gr::k_moe_gemm<T, true, RT, 2, 4>), gu_grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gr::k_moe_gemm<T, true, RT, 4, 1>), gu_grid, dim3(256), 0, s, g);
   if ((rc = launched("moe gate|up")) != STEP_OK) return rc;
   // down: K = inter, 16 output columns per tile
   g.W = L->d_down;
@@ -109,8 +119,12 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   g.weights = L->d_weights;
   g.ncols = L->hidden;
   g.K = L->inter;
-  hipLaunchKernelGGL((gr::k_moe_gemm<T, false, RT, 2>), dim3(mblocks * ((L->hidden + 16 * RT - 1) / (16 * RT))),
-                     dim3(256), 0, s, g);
+  g.ntiles = (L->hidden + 16 * RT - 1) / (16 * RT);
+  const dim3 dn_grid(mblocks * g.ntiles);
+  if (multi)
+    hipLaunchKernelGGL((gr::k_moe_gemm<T, false, RT, 2, 4>), dn_grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gr::k_moe_gemm<T, false, RT, 2, 1>), dn_grid, dim3(256), 0, s, g);
   if ((rc = launched("moe down")) != STEP_OK) return rc;
   hipLaunchKernelGGL(gr::k_moe_sum<T>, dim3(L->n_tokens, (L->hidden + 1023) / 1024), dim3(256), 0, s,
                      reinterpret_cast<const float*>(ws + lay.rows), L->d_expert_ids, L->top_k, L->num_experts, L->hidden,
@@ -133,7 +147,7 @@ extern "C" int moe_align(const int32_t* d_expert_ids, int32_t total, int32_t num
   if ((total > 0 && !d_expert_ids) || !d_sorted_ids || !d_block_expert || !d_num_padded)
     return fail(STEP_EINVAL, "moe_align: NULL device pointer");
   return align_launch(d_expert_ids, total, num_experts, block_m, static_cast<int>(m), d_sorted_ids, d_block_expert,
-                      d_num_padded, static_cast<hipStream_t>(stream));
+                      d_num_padded, nullptr, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t moe_workspace_bytes(const moe_layer* layer) {

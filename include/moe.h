@@ -65,8 +65,9 @@ typedef struct {
 } moe_layer;
 
 /* Workspace bytes moe_forward needs for this layer (0 when the sizes are invalid): the grouping
- * (sorted ids, block experts, row count), the activation rows [N * k][I] in the dtype and the
- * weighted down rows [N * k][D] in fp32. */
+ * (sorted ids, block experts, block ranks, row count), the activation rows in grouped order
+ * [moe_align_rows(N * k, E, MOE_BLOCK_M)][I] in the dtype and the weighted down rows [N * k][D]
+ * in fp32. */
 size_t moe_workspace_bytes(const moe_layer* layer);
 
 /* The MoE MLP layer: grouping, gate|up grouped GEMM with SiLU(gate) * up in its epilogue, down

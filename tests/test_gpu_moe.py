@@ -83,10 +83,13 @@ def _layer_case(torch, s, n, seed, ids=None, w=None):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_moe_layer_matches_oracle(torch_cuda, dtype):
     """Small and ragged layers against the fp64 oracle: output columns and expert widths that are
-    not whole tiles, an expert without tokens, out-of-range ids, a token with no valid expert."""
+    not whole tiles, an expert without tokens, out-of-range ids, a token with no valid expert, and
+    experts with many group blocks (the workgroups that take four of them)."""
     torch = torch_cuda
     for s, n in ((smoe.TINY_MOE.replace(dtype=dtype), 5),
-                 (smoe.MoeShape("ragged", 16, 4, 544, 96, dtype), 37)):
+                 (smoe.MoeShape("ragged", 16, 4, 544, 96, dtype), 37),
+                 # ~75 rows per expert: workgroups of 4 group blocks plus a remainder
+                 (smoe.MoeShape("ragged-multi", 8, 2, 544, 96, dtype), 300)):
         log("moe layer", s.name, dtype, n, "tokens")
         rid, rw = smoe.routing(s, n, 2100)
         rid[rid == 3] = 4
