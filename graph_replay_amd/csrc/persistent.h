@@ -210,6 +210,24 @@ __device__ inline float wave_sum63(float v) {
   return v;
 }
 
+// the same moves for the maximum (lanes a move does not reach see -inf)
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK,
+                                                             0xf, false)));
+}
+__device__ inline float wave_max63(float v) {
+  v = dpp_max<0xb1, 0xf>(v);
+  v = dpp_max<0x4e, 0xf>(v);
+  v = dpp_max<0x141, 0xf>(v);
+  v = dpp_max<0x140, 0xf>(v);
+  v = dpp_max<0x142, 0xa>(v);
+  v = dpp_max<0x143, 0xc>(v);
+  return v;
+}
+// lane 63's value in every lane (a scalar read)
+__device__ inline float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+
 // the largest 64-bit value over the wave, in every lane
 __device__ inline unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
@@ -556,7 +574,7 @@ struct ExchangeRole {
     for (int j = wid - 4; j <= G; j += 4) {
       float x0 = sh.at.stq[j * D + lane], x1 = sh.at.stq[j * D + lane + half];
       if (qk) {   // RMSNorm over the head with its gain, then rotate-half RoPE
-        const float inv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / static_cast<float>(D) + a.eps);
+        const float inv = 1.0f / sqrtf(lane63(wave_sum63(x0 * x0 + x1 * x1)) / static_cast<float>(D) + a.eps);
         x0 = x0 * inv * (j < G ? kc.gq0 : kc.gk0);
         x1 = x1 * inv * (j < G ? kc.gq1 : kc.gk1);
       }
@@ -583,24 +601,30 @@ struct ExchangeRole {
       return src + sp * (D + 2) + (k < 2 ? k : 2 + c * CW + (k - 2));
     }, [&](int i, int, uint64_t w) { sh.mst[i / RW][i % RW] = word_f(w); });
   }
-  // the splits' partials in split order -> attention output (dtype; zeros without keys), dims 2k
-  // and 2k + 1 of head h in word h * 64 + k
+  // the splits' partials -> attention output (dtype; zeros without keys), dims 2k and 2k + 1 of
+  // head h in word h * 64 + k. Lane s holds split s's max and sum: the row's max, the splits'
+  // rescale factors (back to LDS) and the total come from wave reductions; then the two half-waves
+  // add the 32 dims over alternate splits, with the loads of several splits in flight at once.
   __device__ void merge(int l, int it) {
     constexpr int CW = D / kPMergeChunks;
-    if (et >= 64) return;   // exchange wave 4 (lanes past CW idle in the arithmetic)
+    static_assert(kPMaxSplits <= 64 && CW == 32, "one split per lane; two half-waves of 32 dims");
+    if (et >= 64) return;   // exchange wave 4
     const int h = it / kPMergeChunks, c = it % kPMergeChunks;
     const int ns = st.nsplit;
-    const int d = min(et, CW - 1);
     float out = 0.f;
     if (ns > 0) {
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, sh.mst[s][0]);
-      float Ls = 0.f, O = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float f = __expf(sh.mst[s][0] - M);
-        Ls += sh.mst[s][1] * f;
-        O += sh.mst[s][2 + d] * f;
-      }
+      const bool live = lane < ns;
+      const float ms = live ? sh.mst[lane][0] : -INFINITY;
+      const float ls = live ? sh.mst[lane][1] : 0.f;
+      const float M = lane63(wave_max63(ms));
+      const float fs = live ? __expf(ms - M) : 0.f;
+      const float Ls = lane63(wave_sum63(ls * fs));
+      if (live) sh.mst[lane][1] = fs;   // a wave's LDS accesses complete in order
+      const int d = lane & (CW - 1);
+      float O = 0.f;
+#pragma unroll 4
+      for (int sp = lane >> 5; sp < ns; sp += 2) O += sh.mst[sp][2 + d] * sh.mst[sp][1];
+      O += __shfl_down(O, 32, 64);
       out = round_to<T>(O / Ls);
     }
     const float nb = __shfl_down(out, 1, 64);
