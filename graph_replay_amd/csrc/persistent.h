@@ -777,8 +777,10 @@ struct ComputeRole {
   // Weights (and attention tiles) go out two phases or more before their use, each batch after the
   // issuing phase's own outputs are stored (with the whole chip loading weights at once, issuing
   // loads can stall the wave until queue slots free up): gate|up after QKV, down after O, the next
-  // layer's QKV after gate|up, its attention tiles and O after down. The order keeps every wait
-  // exact: each use waits only for its own batch and the older ones.
+  // layer's QKV after gate|up, its attention tiles and O after down. A block with an attention
+  // item issues gate|up and down after its attention partials instead: its exchange waves are not
+  // polling then, while a poll issued behind a weight burst on the CU waits for the burst. The
+  // order keeps every wait exact or early: each use waits for its own batch and the older ones.
   __device__ void layer_start(int l) { lw = sh.lw[l]; }
   __device__ void qkv_wait(int) {}
   __device__ void norm_stage(int) {}
@@ -951,6 +953,7 @@ struct ComputeRole {
       }
     }
     wg.load(lw.gate_up_w, nullptr, I, gw, NW, R_gu, 0);
+    wd.load(lw.down_w, nullptr, H, gw, NW, R_dn, 0);
   }
   __device__ void merge_wait(int, int) {}
   __device__ void merge(int, int) {}
@@ -962,7 +965,7 @@ struct ComputeRole {
     wo.dot(xv, gw, NW, R_o, 0, [&](int, int row, float y, float) {
       if (lane == 63) put_rep(a.x_o, row, word1(y, tg));
     });
-    wd.load(lw.down_w, nullptr, H, gw, NW, R_dn, 0);
+    if (g0 < 0) wd.load(lw.down_w, nullptr, H, gw, NW, R_dn, 0);   // attention blocks: after partials
   }
   __device__ void mlp_wait(int) {}
   __device__ void gate_up(int l) {
