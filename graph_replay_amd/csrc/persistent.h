@@ -140,25 +140,38 @@ __device__ inline void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" 
 // Wait of the exchange waves for n tagged words: exchange thread t (0..255) takes the words
 // i = t + 256 (B * round + b), b < B, whose address is addr(i), polls them until all carry `tag`
 // (its low 16 bits in the top of the word with tag16), then passes each word to f(i, b, word).
+// `sent` is the block's LDS word through which the watching wave releases the others.
 template <int B, class Addr, class F>
 __device__ inline void poll_words(int t, int n, uint32_t tag, int* err, int where, Addr&& addr, F&& f,
-                                  bool tag16 = false) {
+                                  volatile uint32_t* sent, bool tag16 = false) {
   const uint32_t tmask = tag16 ? 0xffffu : 0xffffffffu;
   const int tshift = tag16 ? 48 : 32;
   tag &= tmask;
   for (int i0 = t; i0 < n; i0 += 256 * B) {
     uint64_t v[B];
-    // While the producers are still at work one lane of the wave watches one word (1/(64 B) of the
-    // polling traffic of reading them all); then every lane reads all B until they carry the tag.
-    // Blocks and waves watch different words, so that no single line is polled by every CU.
-    {
-      const int i = __builtin_amdgcn_readfirstlane((static_cast<int>(blockIdx.x) * 61 + (t >> 6) * 17) % n);
+    // While the producers are still at work one lane of the block watches one word (the fewer
+    // requests spin on the coherent lines, the sooner the others' stores show), and posts the tag
+    // to LDS for the block's other exchange waves; then every lane reads all B until they carry
+    // the tag. Blocks watch different words, so that no single line is polled by every CU.
+    if (t < 64) {
+      const int i = __builtin_amdgcn_readfirstlane((static_cast<int>(blockIdx.x) * 61) % n);
       for (int it = 0;; ++it) {
         uint32_t seen = 0;
-        if ((threadIdx.x & 63) == 0) seen = static_cast<uint32_t>(get_word(addr(i)) >> tshift) & tmask;
+        if (t == 0) seen = static_cast<uint32_t>(get_word(addr(i)) >> tshift) & tmask;
         if (__builtin_amdgcn_readfirstlane(seen) == tag) break;
         if ((it & 63) == 63) {
           if (it >= kPSpin) { atomicCAS(err, 0, where); break; }
+          if (ld_dev(err) != 0) break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (t == 0) *sent = tag;
+    } else {
+      // a stale LDS value can only start the full read early; the full read checks every tag
+      for (int it = 0;; ++it) {
+        if (__builtin_amdgcn_readfirstlane(*sent) == tag) break;
+        if ((it & 63) == 63) {
+          if (it >= 64 * kPSpin) { atomicCAS(err, 0, where); break; }
           if (ld_dev(err) != 0) break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -414,6 +427,7 @@ struct PShared {
   // for all of them, where an LDS read does not.
   PLayer lw[kPMaxLayers];
   unsigned long long cand[8];          // per-wave sampling candidates
+  uint32_t sent;                       // the tag the block's watching wave last saw
   int last;                            // this block is the last of the step to finish
 };
 
@@ -538,7 +552,7 @@ struct ExchangeRole {
     qk = lw.q_norm != nullptr;
   }
   __device__ void add_poll(const uint64_t* src, uint32_t tag, int where) {
-    poll_words<RJ>(et, H, tag, a.err, where, [&](int i) { return src + i; }, [&](int, int b, uint64_t w) { r[b] += word_f(w); });
+    poll_words<RJ>(et, H, tag, a.err, where, [&](int i) { return src + i; }, [&](int, int b, uint64_t w) { r[b] += word_f(w); }, &sh.sent);
   }
   __device__ void qkv_wait(int l) {
     if (l > 0) add_poll(my_copy(a.x_down), st.tag(l - 1, 5), 6);
@@ -567,7 +581,7 @@ struct ExchangeRole {
       const int h = i / D, d = i % D;
       const int c0 = (h < G) ? (gq * G + h) * D : (h == G ? (nq + gq) * D : (nq + nkv + gq) * D);
       return a.x_qkv + c0 + d;
-    }, [&](int i, int, uint64_t w) { sh.at.stq[i] = word_f(w); });
+    }, [&](int i, int, uint64_t w) { sh.at.stq[i] = word_f(w); }, &sh.sent);
   }
   __device__ void attn_rope(int, int) {
     constexpr int half = 64;
@@ -599,7 +613,7 @@ struct ExchangeRole {
     poll_words<3>(et, st.nsplit * RW, st.tag(l, 1), a.err, 3, [&](int i) {
       const int sp = i / RW, k = i % RW;
       return src + sp * (D + 2) + (k < 2 ? k : 2 + c * CW + (k - 2));
-    }, [&](int i, int, uint64_t w) { sh.mst[i / RW][i % RW] = word_f(w); });
+    }, [&](int i, int, uint64_t w) { sh.mst[i / RW][i % RW] = word_f(w); }, &sh.sent);
   }
   // the splits' partials -> attention output (dtype; zeros without keys), dims 2k and 2k + 1 of
   // head h in word h * 64 + k. Lane s holds split s's max and sum: the row's max, the splits'
@@ -637,7 +651,7 @@ struct ExchangeRole {
                    [&](int i, int, uint64_t w) {
                      sh.xs[1][2 * i] = word_h(w, 0);
                      sh.xs[1][2 * i + 1] = word_h(w, 1);
-                   });
+                   }, &sh.sent);
   }
   __device__ void o_proj(int) {}
   __device__ void mlp_wait(int l) { add_poll(my_copy(a.x_o), st.tag(l, 3), 5); }
@@ -650,7 +664,7 @@ struct ExchangeRole {
                                    sh.xs[1][i] = word_h(w, 0);
                                    sh.xs[1][i + I / 3] = word_h(w, 1);
                                    sh.xs[1][i + 2 * (I / 3)] = word_h(w, 2);
-                                 }, true);
+                                 }, &sh.sent, true);
     if (l + 1 < a.layers) {
       load_gains(l + 1);
     } else {
@@ -1016,6 +1030,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
   st.L = a.len[0];
   st.p = min(max(a.pos[0], 0), a.max_position - 1);
   st.slot = a.slot[0];
+  if (threadIdx.x == 0) sh.sent = 0u;
   st.T = a.sample ? a.temp[0] : 0.f;
   st.seed = a.sample ? a.rng[0] : 0ull;
   st.stepc = a.sample ? a.rng[1] : 0ull;
