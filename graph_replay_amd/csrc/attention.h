@@ -418,8 +418,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
     for (int j = 0; j < G; ++j) {
       float bm = fmaxf(sc[0][j], sc[1][j]);
       bm = fmaxf(bm, __shfl_xor(bm, 8, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = max_xor32(max_xor16(bm));
       const float mn = fmaxf(m[j], bm);
       const float corr = __expf(m[j] - mn);
       const float p0 = __expf(sc[0][j] - mn), p1 = __expf(sc[1][j] - mn);
@@ -429,8 +428,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
       }
       float ps = p0 + p1;
       ps += __shfl_xor(ps, 8, 64);
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      ps = add_xor32(add_xor16(ps));
       l[j] = l[j] * corr + ps;
       m[j] = mn;
 #pragma unroll
@@ -606,8 +604,7 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
         bm = fmaxf(bm, s[kb][i]);
       }
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    bm = max_xor32(max_xor16(bm));
     const float mn = fmaxf(m, bm);                          // finite: block b0 has a live key
     const float corr = __expf(m - mn);
     float ps = 0.f;
@@ -622,8 +619,7 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
       }
       pt[kb] = make_uint2(pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]));
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = add_xor32(add_xor16(ps));
     lsum = lsum * corr + ps;
     m = mn;
 #pragma unroll

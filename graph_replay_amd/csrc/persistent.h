@@ -640,7 +640,7 @@ struct ExchangeRole {
       float O = 0.f;
 #pragma unroll 4
       for (int sp = lane >> 5; sp < ns; sp += 2) O += sh.mst[sp][2 + d] * sh.mst[sp][1];
-      O += __shfl_down(O, 32, 64);
+      O = add_xor32(O);   // lanes l and l + 32: their two halves
       out = round_to<T>(O / Ls);
     }
     const float nb = __shfl_down(out, 1, 64);
@@ -898,8 +898,7 @@ struct ComputeRole {
           bm = fmaxf(bm, sc[kb][i]);
         }
       }
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = max_xor32(max_xor16(bm));
       m = bm;                                                   // finite: tile wid has a live key
       float ps = 0.f;
       uint2 pt[kPTiles];
@@ -913,8 +912,7 @@ struct ComputeRole {
         }
         pt[kb] = make_uint2(pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3]));
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      ps = add_xor32(add_xor16(ps));
       lsum = ps;
 #pragma unroll
       for (int kb = 0; kb < kPTiles; ++kb) {

@@ -29,13 +29,17 @@ def _decoder(shape, weights, **kw):
 CONTEXTS = [0, 127, 128, 300, 1023, 1500]
 
 
-def test_persistent_step_matches_oracle_and_multikernel(torch_cuda):
-    """Qwen3-0.6B widths, 2 layers, full vocabulary: every context above as a batch-1 step through
-    the persistent kernel; logits vs the oracle (3e-2) and vs the multi-kernel step (same inputs),
-    greedy tokens under the near-tie rule, the new K/V the kernel writes to its slot, and then three
+@pytest.mark.parametrize("dtype,flags", [("bf16", "qwen3"), ("f16", "qwen3"), ("bf16", "bias-no-qknorm")])
+def test_persistent_step_matches_oracle_and_multikernel(torch_cuda, dtype, flags):
+    """Qwen3-0.6B widths, 2 layers, full vocabulary, bf16 and fp16, and the Qwen2.5 flags (QKV bias,
+    no QK-norm) at the same widths: every context above as a batch-1 step through the persistent
+    kernel; logits vs the oracle (3e-2) and vs the multi-kernel step (same inputs), greedy tokens
+    under the near-tie rule, the new K/V the kernel writes to its slot, and then three
     device-continued steps against the multi-kernel step's."""
     torch = torch_cuda
-    shape = synth.QWEN3_0_6B.replace(layers=2)
+    shape = synth.QWEN3_0_6B.replace(layers=2, dtype=dtype)
+    if flags != "qwen3":
+        shape = shape.replace(qk_norm=False, qkv_bias=True)
     W = synth.make_weights(shape, 0)
     W32 = fp32_weights(W)
     sc = Scenario(shape, W, CONTEXTS, steps=4, seed=1101)
@@ -47,7 +51,7 @@ def test_persistent_step_matches_oracle_and_multikernel(torch_cuda):
     sc.inject(dm)
     bt_all = sc.table_array()
     for j, c in enumerate(CONTEXTS):
-        log("persistent step, context", c)
+        log("persistent step", dtype, "context", c)
         tok = int(sc.tokens[j])
         slot = oracle.slot_of(sc.tables[j], c, 16)
         args = ([tok], [c], [c + 1], [slot], bt_all[j:j + 1])
@@ -59,9 +63,9 @@ def test_persistent_step_matches_oracle_and_multikernel(torch_cuda):
         cache = sc.oracle_cache(j)
         hid = oracle.forward_request(shape, W32, cache, [tok], [c])
         ref = oracle.final_logits(W32, hid)[0]
-        assert max_abs(gp, ref) <= TOL["bf16"], (c, max_abs(gp, ref))
-        assert max_abs(gp, gm) <= TOL["bf16"], (c, max_abs(gp, gm))
-        assert near_tie_ok(int(dp.tokens[0].item()), ref, TOL["bf16"]), c
+        assert max_abs(gp, ref) <= TOL[dtype], (c, max_abs(gp, ref))
+        assert max_abs(gp, gm) <= TOL[dtype], (c, max_abs(gp, gm))
+        assert near_tie_ok(int(dp.tokens[0].item()), ref, TOL[dtype]), c
         assert int(dp.tokens[0].item()) == int(oracle.argmax_lowest(gp))
         # the new key and value the kernel stored at the slot (bf16) against the oracle's fp32 ones:
         # within 3e-2 relative above magnitude 1 (a bf16 ulp is 2^-7 relative, so this allows the
@@ -85,9 +89,9 @@ def test_persistent_step_matches_oracle_and_multikernel(torch_cuda):
         gp, gm = dp.logits[0].cpu().numpy(), dm.logits[0].cpu().numpy()
         tp, tm = int(dp.tokens[0].item()), int(dm.tokens[0].item())
         if tp != tm:   # allowed only at a near tie; the steps then diverge, so stop comparing
-            assert near_tie_ok(tp, gm, TOL["bf16"]), i
+            assert near_tie_ok(tp, gm, TOL[dtype]), i
             break
-        assert max_abs(gp, gm) <= TOL["bf16"], (i, max_abs(gp, gm))
+        assert max_abs(gp, gm) <= TOL[dtype], (i, max_abs(gp, gm))
     assert dp.kernels_per_decode(1) == 1   # the sampler runs inside the step kernel
     dp.close()
     dm.close()
