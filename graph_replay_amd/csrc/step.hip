@@ -167,8 +167,14 @@ __global__ void k_hold(int iters) {
 
 // keys per attention split for a row count and key bound (fixed per bucket, so the grid is too):
 // short splits keep a few rows busy on all CUs, long splits amortise each split's fixed cost
+// Keys per attention split. Up to 8 rows, short splits fill the chip. Up to 64 rows whose contexts
+// cannot pass 2,560 keys, one split per row in most cases: each extra split costs a block's fixed
+// prologue and a merge, which measured more than the parallelism they buy (batch 32, contexts
+// 128-2,048: 47.7 us at 512 keys, 45.0 at 1,024, 44.4 at 2,048 per layer). Where rows can be
+// longer, a few long rows would be the tail of the launch (32 decode rows with contexts up to
+// 4,096 ran 7% slower at 2,048 keys), so they keep 512-key splits.
 int split_tokens_for(int rows, int max_len) {
-  int P = rows <= 8 ? 64 : 512;
+  int P = rows <= 8 ? 64 : (rows <= 64 && max_len <= 2560 ? 2048 : 512);
   while ((max_len + P - 1) / P > gr::kMaxSplits) P *= 2;
   return P;
 }
