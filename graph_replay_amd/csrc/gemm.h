@@ -8,6 +8,8 @@
 //                (the fused residual-add + RMSNorm), optional SiLU(gate) * up epilogue.
 //   k_gemv_mfma  16 or 32 token rows (bf16/fp16): v_mfma_f32_16x16x32 with both operands loaded
 //                straight from memory in the MFMA lane layout; the four waves split K.
+//   k_gemv_stream 9-32 token rows of a wide output (the LM head): x staged in LDS once per
+//                block, whole weight tiles streamed per wave.
 //   k_gemm_ring  >= 33 token rows (bf16/fp16, K a multiple of 64): MFMA GEMM over an LDS ring filled
 //                by direct-to-LDS loads, XCD-ordered blocks
 //   k_gemm       >= 33 token rows otherwise: LDS-tiled MFMA GEMM
@@ -711,6 +713,88 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
         const int n = (blockIdx.x * RT + r) * 16 + rbase + i;
         if (n < a.N) out[static_cast<size_t>(m) * a.ldo + n] = acc[0][t][i] + (b ? T::to_f(b[n]) : 0.f);
       }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Streaming skinny MFMA GEMV for a wide output over 9-32 token rows (the LM head): the MB * 16
+// token rows of x go to LDS once per block, then every wave owns whole 16-row weight tiles (tiles
+// w, w + W, ... for wave w of W in the grid) and streams each tile's K in chunks of kStreamCh
+// k-steps, the next chunk's weight loads in flight while the current chunk's MFMAs run (NWV waves
+// per block, CH k-steps per chunk). In LDS,
+// the 16-byte chunk c of row m sits at chunk c ^ (m & 15), so the 16 rows a lane group reads at
+// one k offset fall in distinct banks. fp32 out [M][ldo]; no bias, no K split; K a multiple of
+// 32 * CH and at most kStreamK.
+constexpr int kStreamK = 1024;
+template <class T, int MB, int NWV, int CH>
+__global__ __launch_bounds__(64 * NWV, 2) void k_gemv_stream(GemmArgs a) {
+  using S = typename T::S;
+  static_assert(sizeof(S) == 2, "16-bit types");
+  __shared__ __align__(16) S xs[MB * 16 * kStreamK];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int K = a.K;
+  const int cpt = K / (32 * CH);                     // chunks per tile
+  const int ntiles = (a.N + 15) / 16;
+  const int nwaves = gridDim.x * NWV;
+  const int tile0 = blockIdx.x * NWV + wid;
+  const int nseq = tile0 < ntiles ? ((ntiles - 1 - tile0) / nwaves + 1) * cpt : 0;
+  const S* W = static_cast<const S*>(a.W);
+  uint4 wa[CH], wb[CH];
+  // the weight chunk q of this wave's sequence (rows past N clamped: loaded, never stored)
+  auto load = [&](uint4(&w)[CH], int q) {
+    const int row = min((tile0 + (q / cpt) * nwaves) * 16 + col, a.N - 1);
+    const S* p = W + static_cast<size_t>(row) * K + (q % cpt) * (32 * CH) + 8 * grp;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) w[j] = *reinterpret_cast<const uint4*>(p + 32 * j);
+  };
+  if (nseq > 0) load(wa, 0);
+  // x -> LDS (zero rows past M), behind the first chunk's loads
+  const int nch = K / 8;
+  const S* X = static_cast<const S*>(a.x);
+  for (int i = threadIdx.x; i < MB * 16 * nch; i += 64 * NWV) {
+    const int m = i / nch, c = i % nch;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (m < a.M) v = *reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * K + 8 * c);
+    *reinterpret_cast<uint4*>(xs + m * K + 8 * (c ^ (m & 15))) = v;
+  }
+  __syncthreads();
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint4(&w)[CH], int q) {
+    const int ks0 = (q % cpt) * CH;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = (ks0 + j) * 4 + grp;
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xs + (t * 16 + col) * K + 8 * (c ^ col));
+        acc[t] = mfma16x16x32<T>(w[j], xv, acc[t]);
+      }
+    }
+    if (q % cpt == cpt - 1) {   // the tile's last chunk: lane holds rows 4 grp + i of token col
+      const int nb = (tile0 + (q / cpt) * nwaves) * 16 + 4 * grp;
+      float* out = static_cast<float*>(a.out);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        const int m = t * 16 + col;
+        if (m < a.M) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < a.N) out[static_cast<size_t>(m) * a.ldo + nb + i] = acc[t][i];
+        }
+        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  for (int q = 0; q < nseq; q += 2) {
+    if (q + 1 < nseq) load(wb, q + 1);
+    compute(wa, q);
+    if (q + 1 < nseq) {
+      if (q + 2 < nseq) load(wa, q + 2);
+      compute(wb, q + 1);
     }
   }
 }

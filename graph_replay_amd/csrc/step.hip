@@ -427,7 +427,16 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       default: e = launch_gemv_mt<T, 8>(a, l.epi, g.rows_pw, g.u, grid, s); break;
     }
   } else if constexpr (!std::is_same<T, F32>::value) {
-    if (l.M <= 32) {
+    constexpr int SW = 8, SC = 8;   // waves per block, k-steps per weight chunk
+    if (l.kind == KK_LM_HEAD && l.M > 8 && l.M <= 32 && !l.bias && l.epi == EPI_F32 && l.K <= gr::kStreamK &&
+        l.K % (32 * SC) == 0) {
+      // the vocabulary-wide output: two blocks per CU, each wave streaming whole weight tiles
+      const int ntiles = (l.N + 15) / 16;
+      const dim3 grid(std::min(2 * 256, (ntiles + SW - 1) / SW));
+      if (l.M <= 16) launch((gr::k_gemv_stream<T, 1, SW, SC>), grid, dim3(64 * SW), 0, s, a);
+      else launch((gr::k_gemv_stream<T, 2, SW, SC>), grid, dim3(64 * SW), 0, s, a);
+      e = hipGetLastError();
+    } else if (l.M <= 32) {
       // two 16-row weight tiles per wave share each activation fragment where the output is wide
       // enough (QKV, gate|up); narrow outputs (O, down) keep one tile and split K instead
       const int rt = (l.M > 16 && l.N >= 2048) ? 2 : 1;
