@@ -73,7 +73,22 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const float* __restr
     const size_t ro = static_cast<size_t>(src) * H;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) v[i] = r_in[ro + min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)];
-    for (int s = 0; s < n_delta; ++s) {
+    // up to kDeltaBatch partials: every load issued before the first add, the adds in partial order
+    constexpr int kDeltaBatch = 8;
+    float db[kDeltaBatch][KPT];
+#pragma unroll
+    for (int s = 0; s < kDeltaBatch; ++s)
+      if (s < n_delta) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) db[s][i] = delta[s * delta_stride + ro + min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)];
+      }
+#pragma unroll
+    for (int s = 0; s < kDeltaBatch; ++s)
+      if (s < n_delta) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) v[i] += db[s][i];
+      }
+    for (int s = kDeltaBatch; s < n_delta; ++s) {
       float dv[KPT];
 #pragma unroll
       for (int i = 0; i < KPT; ++i) dv[i] = delta[s * delta_stride + ro + min(static_cast<int>(threadIdx.x) + 256 * i, H - 1)];

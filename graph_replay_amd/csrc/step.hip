@@ -64,6 +64,10 @@ struct step_ctx {
   Layout lay{};
   hipStream_t stream = nullptr;
   hipStream_t cap_stream = nullptr;
+  // a mixed step's decode-row attention runs on side_stream beside the packed prefill attention
+  // (fork_ev / join_ev order it after the QKV work and before the O projection)
+  hipStream_t side_stream = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
   std::vector<int> kernels_per_bucket;
@@ -933,6 +937,26 @@ int run_attn_prefill(step_ctx* ctx, int layer, const MixedPlan& p, const MixedMe
   return STEP_OK;
 }
 
+// The two attention launches of a mixed step as parallel branches: rows() on the side stream,
+// prefill() on the step's stream, both after the work already enqueued and before what follows
+// (inside a capture, two branches of the graph). The join is enqueued even when a launch fails, so
+// a capture never ends with an unjoined stream.
+template <class Pre, class Rows>
+int attn_branches(step_ctx* ctx, Pre&& prefill, Rows&& rows) {
+  hipStream_t main = ctx->stream;
+  hipError_t e = hipEventRecord(ctx->fork_ev, main);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ctx->side_stream, ctx->fork_ev, 0);
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention fork: %s", hipGetErrorString(e));
+  ctx->stream = ctx->side_stream;
+  const int rc_rows = rows();
+  ctx->stream = main;
+  const int rc_pre = prefill();
+  e = hipEventRecord(ctx->join_ev, ctx->side_stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(main, ctx->join_ev, 0);
+  if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention join: %s", hipGetErrorString(e));
+  return rc_rows != STEP_OK ? rc_rows : rc_pre;
+}
+
 template <class T>
 int run_mixed(step_ctx* ctx, const MixedPlan& p) {
   const step_config& c = ctx->cfg;
@@ -947,10 +971,14 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
       if constexpr (std::is_same<T, F32>::value) {
         return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
       } else {
-        // listed tiles on the packed kernel, listed decode rows on the row kernel (disjoint outputs)
-        TRY(run_attn_prefill<T>(ctx, l, p, m, q, attn_o));
-        return run_attn_rows<T>(ctx, l, std::min(L.RM, L.TM), q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len,
-                                p.max_len, attn_o, m.dec_rows);
+        // listed tiles on the packed kernel, listed decode rows on the row kernel (disjoint outputs,
+        // side by side: two branches of the bucket's graph)
+        return attn_branches(
+            ctx, [&] { return run_attn_prefill<T>(ctx, l, p, m, q, attn_o); },
+            [&] {
+              return run_attn_rows<T>(ctx, l, std::min(L.RM, L.TM), q, 0, nullptr, nullptr, m.bt, W, m.row_req,
+                                      m.row_len, p.max_len, attn_o, m.dec_rows);
+            });
       }
     }
     if (p.mode == 1 || p.n_pre_tok == 0 || std::is_same<T, F32>::value) {
@@ -958,7 +986,8 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
       return run_attn_rows<T>(ctx, l, p.T, q, 0, nullptr, nullptr, m.bt, W, m.row_req, m.row_len, p.max_len, attn_o);
     }
     if constexpr (!std::is_same<T, F32>::value) {
-      // chunk tokens packed on MFMA, decode rows one query row each, into disjoint output rows
+      // chunk tokens packed on MFMA, decode rows one query row each, into disjoint output rows (in
+      // turn: launched eagerly, the cross-stream waits cost more than the overlap saves)
       TRY(run_attn_prefill<T>(ctx, l, p, m, q, attn_o));
       if (p.T > p.n_pre_tok) {
         const int off = p.n_pre_tok;
@@ -1101,6 +1130,9 @@ extern "C" int step_init(const step_config* cfg, const step_weights* w, const st
   };
   hipError_t e;
   if ((e = hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking)) != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  if ((e = hipStreamCreateWithFlags(&ctx->side_stream, hipStreamNonBlocking)) != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  if ((e = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if ((e = hipEventCreateWithFlags(&ctx->join_ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
   ctx->stage_bytes = std::max(ctx->lay.dmeta_bytes, ctx->lay.mmeta_bytes);
   ctx->stage_bytes = std::max(ctx->stage_bytes, 3 * sizeof(float) * static_cast<size_t>(ctx->lay.LM));
   for (int i = 0; i < 2; ++i) {
@@ -1581,6 +1613,10 @@ extern "C" void step_destroy(step_ctx* ctx) {
     if (ctx->h_stage[i]) (void)hipHostFree(ctx->h_stage[i]);
   }
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  if (ctx->side_stream) (void)hipStreamSynchronize(ctx->side_stream);
+  if (ctx->side_stream) (void)hipStreamDestroy(ctx->side_stream);
+  if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
+  if (ctx->join_ev) (void)hipEventDestroy(ctx->join_ev);
   for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
   for (auto& e : ctx->prof_ev_end) (void)hipEventDestroy(e);
   delete ctx;
