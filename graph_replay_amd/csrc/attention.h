@@ -541,10 +541,12 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
 #pragma unroll
     for (int t = 0; t < DT; ++t) vf[kb][t] = *reinterpret_cast<const uint2*>(vp + t * 16 * kBlk);
   };
-  // The first step's blocks are loaded before the query prologue, except in the split that holds
-  // key L-1 of a fused decode row (the prologue writes that key first).
+  // The first step's blocks are loaded before the query prologue, except by the wave whose first
+  // step holds the block of key L-1 of a fused decode row (the prologue writes that key first).
   const bool holds_new = sp == nsplit - 1;
-  const bool pre = (wid < nblk) && !(a.q == nullptr && holds_new);
+  const int nb_new = nblk - 1 - wid;   // the new key's block, relative to this wave's first one
+  const bool new_first = a.q == nullptr && holds_new && nb_new >= 0 && nb_new % 4 == 0 && nb_new / 4 < KB;
+  const bool pre = (wid < nblk) && !new_first;
   if (pre) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {

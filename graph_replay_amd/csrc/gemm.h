@@ -8,7 +8,7 @@
 //                (the fused residual-add + RMSNorm), optional SiLU(gate) * up epilogue.
 //   k_gemv_mfma  16 or 32 token rows (bf16/fp16): v_mfma_f32_16x16x32 with both operands loaded
 //                straight from memory in the MFMA lane layout; the four waves split K.
-//   k_gemv_stream 9-32 token rows of a wide output (the LM head): x staged in LDS once per
+//   k_gemv_stream 9-48 token rows of a wide output (the LM head): x staged in LDS once per
 //                block, whole weight tiles streamed per wave.
 //   k_gemm_ring  >= 33 token rows (bf16/fp16, K a multiple of 64): MFMA GEMM over an LDS ring filled
 //                by direct-to-LDS loads, XCD-ordered blocks
@@ -733,20 +733,19 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Streaming skinny MFMA GEMV for a wide output over 9-32 token rows (the LM head): the MB * 16
+// Streaming skinny MFMA GEMV for a wide output over 9-48 token rows (the LM head): the MB * 16
 // token rows of x go to LDS once per block, then every wave owns whole 16-row weight tiles (tiles
 // w, w + W, ... for wave w of W in the grid) and streams each tile's K in chunks of kStreamCh
 // k-steps, the next chunk's weight loads in flight while the current chunk's MFMAs run (NWV waves
 // per block, CH k-steps per chunk). In LDS,
 // the 16-byte chunk c of row m sits at chunk c ^ (m & 15), so the 16 rows a lane group reads at
 // one k offset fall in distinct banks. fp32 out [M][ldo]; no bias, no K split; K a multiple of
-// 32 * CH and at most kStreamK.
-constexpr int kStreamK = 1024;
-template <class T, int MB, int NWV, int CH>
-__global__ __launch_bounds__(64 * NWV, 2) void k_gemv_stream(GemmArgs a) {
+// 32 * CH and at most KMAX (LDS: MB * 16 * KMAX elements; two blocks per CU up to 64 KiB).
+template <class T, int MB, int NWV, int CH, int KMAX>
+__global__ __launch_bounds__(64 * NWV, MB * 16 * KMAX * 2 <= 65536 ? 2 : 1) void k_gemv_stream(GemmArgs a) {
   using S = typename T::S;
   static_assert(sizeof(S) == 2, "16-bit types");
-  __shared__ __align__(16) S xs[MB * 16 * kStreamK];
+  __shared__ __align__(16) S xs[MB * 16 * KMAX];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K;

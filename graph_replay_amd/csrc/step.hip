@@ -432,13 +432,16 @@ int run_linear(step_ctx* ctx, const Lin& l) {
     }
   } else if constexpr (!std::is_same<T, F32>::value) {
     constexpr int SW = 8, SC = 8;   // waves per block, k-steps per weight chunk
-    if (l.kind == KK_LM_HEAD && l.M > 8 && l.M <= 32 && !l.bias && l.epi == EPI_F32 && l.K <= gr::kStreamK &&
-        l.K % (32 * SC) == 0) {
-      // the vocabulary-wide output: two blocks per CU, each wave streaming whole weight tiles
+    if (l.kind == KK_LM_HEAD && l.M > 8 && !l.bias && l.epi == EPI_F32 && l.K % (32 * SC) == 0 &&
+        ((l.M <= 32 && l.K <= 1024) || (l.M <= 48 && l.K <= 1536))) {
+      // the vocabulary-wide output, each wave streaming whole weight tiles: two blocks per CU up
+      // to 32 rows of K <= 1,024 (64 KiB of LDS each), else one (up to 48 rows of K <= 1,536)
       const int ntiles = (l.N + 15) / 16;
-      const dim3 grid(std::min(2 * 256, (ntiles + SW - 1) / SW));
-      if (l.M <= 16) launch((gr::k_gemv_stream<T, 1, SW, SC>), grid, dim3(64 * SW), 0, s, a);
-      else launch((gr::k_gemv_stream<T, 2, SW, SC>), grid, dim3(64 * SW), 0, s, a);
+      const int per_cu = (l.M <= 32 && l.K <= 1024) ? 2 : 1;
+      const dim3 grid(std::min(per_cu * 256, (ntiles + SW - 1) / SW));
+      if (per_cu == 1) launch((gr::k_gemv_stream<T, 3, SW, SC, 1536>), grid, dim3(64 * SW), 0, s, a);
+      else if (l.M <= 16) launch((gr::k_gemv_stream<T, 1, SW, SC, 1024>), grid, dim3(64 * SW), 0, s, a);
+      else launch((gr::k_gemv_stream<T, 2, SW, SC, 1024>), grid, dim3(64 * SW), 0, s, a);
       e = hipGetLastError();
     } else if (l.M <= 32) {
       // two 16-row weight tiles per wave share each activation fragment where the output is wide

@@ -93,6 +93,34 @@ def test_decode_all_bucket_paths_bf16(torch_cuda):
     dec.close()
 
 
+def test_lm_head_ragged_vocab_9_to_32_rows(torch_cuda):
+    """The streaming LM-head GEMV (9-32 rows) with a vocabulary that is not a multiple of its 16-row
+    tiles: the last tile's rows past the vocabulary are loaded clamped and never stored."""
+    torch = torch_cuda
+    shape = synth.TINY.replace(name="tiny-bf16-v1000", dtype="bf16", vocab=1000)
+    W = synth.make_weights(shape, 0)
+    W32 = fp32_weights(W)
+    rng = np.random.default_rng(6)
+    contexts = rng.integers(1, 120, size=32).tolist()
+    sc = Scenario(shape, W, contexts, steps=2, seed=2025)
+    dec = _decoder(shape, W, num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=256, max_batch=32,
+                   buckets=[16, 32], use_graphs=True)
+    sc.inject(dec)
+    for r in (13, 32):
+        log("bf16 tiny vocab 1000 rows", r)
+        toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
+        dec.logits.fill_(float("nan"))
+        dec.decode(toks[:r], pos[:r], lens[:r], slots[:r], bt[:r])
+        torch.cuda.synchronize()
+        got = dec.logits[:r].cpu().numpy()
+        assert got.shape[1] == 1000
+        for j in range(r):
+            hid = oracle.forward_request(shape, W32, sc.oracle_cache(j), [toks[j]], [pos[j]])
+            ref = oracle.final_logits(W32, hid)[0]
+            assert max_abs(got[j], ref) <= TOL["bf16"], (r, j, max_abs(got[j], ref))
+    dec.close()
+
+
 def test_qwen3_width_two_layers_bs32_gumbel(torch_cuda):
     """Qwen3-0.6B widths (2 layers) at batch 32 over shuffled paged KV, Gumbel-max at T = 1 with Philox."""
     torch = torch_cuda
