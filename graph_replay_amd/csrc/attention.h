@@ -207,6 +207,132 @@ __device__ inline void attn_prologue(const AttnRowsArgs& a, int row, int g, bool
   __syncthreads();
 }
 
+// The fused decode prologue (a.q == nullptr) in two phases: attn_prologue_issue sends every load
+// it needs (RoPE table entries, the first kPNP QKV partials of this wave's query heads and, in the
+// wave that writes it, of the new key and value) before the split's key/value loads go out, and
+// attn_prologue_finish does the sums (same order as attn_prologue, so the same bits), the norms,
+// the rotation, the LDS and pool writes and the closing barrier while those loads are in flight.
+constexpr int kPNP = 4;
+template <int G>
+struct PrologueRegs {
+  static constexpr int HPW = (G + 3) / 4;   // query heads per wave
+  float c = 0.f, sn = 0.f;
+  float gq0 = 1.f, gq1 = 1.f, gk0 = 1.f, gk1 = 1.f;   // QK-norm gains of this lane's dims
+  int slot = -1;
+  float q[HPW][2][kPNP];
+  float kv[4][kPNP];
+};
+
+// norm_rope_pair with the gain already in registers (the same arithmetic)
+template <int D>
+__device__ inline void norm_rope_pair_g(float& x0, float& x1, bool has_gain, float g0, float g1, float eps, float c,
+                                        float s) {
+  constexpr int half = D / 2;
+  const bool act = static_cast<int>(threadIdx.x & 63) < half;
+  if (has_gain) {
+    const float ss = wave_sum(act ? x0 * x0 + x1 * x1 : 0.f);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+    if (act) {
+      x0 = x0 * inv * g0;
+      x1 = x1 * inv * g1;
+    }
+  }
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x1 * c + x0 * s;
+  x0 = y0;
+  x1 = y1;
+}
+
+template <class T, int D, int G>
+__device__ inline void attn_prologue_issue(const AttnRowsArgs& a, int row, int g, bool holds_new, PrologueRegs<G>& pr) {
+  constexpr int half = D / 2;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const bool act = lane < half;
+  const int p = a.pos[row];
+  pr.c = act ? a.rope_cos[static_cast<size_t>(p) * half + lane] : 0.f;
+  pr.sn = act ? a.rope_sin[static_cast<size_t>(p) * half + lane] : 0.f;
+  using S = typename T::S;
+  if (a.q_norm && act) {
+    pr.gq0 = T::to_f(static_cast<const S*>(a.q_norm)[lane]);
+    pr.gq1 = T::to_f(static_cast<const S*>(a.q_norm)[lane + half]);
+  }
+  const float* base = a.qkv + static_cast<size_t>(row) * (a.nq + 2 * a.nkv) * D;
+  auto issue = [&](float(&dst)[kPNP], int col) {
+#pragma unroll
+    for (int k = 0; k < kPNP; ++k) dst[k] = (act && k < a.n_parts) ? base[k * a.part_stride + col] : 0.f;
+  };
+#pragma unroll
+  for (int hh = 0; hh < PrologueRegs<G>::HPW; ++hh) {
+    const int j = wid + 4 * hh;
+    if (j < G) {
+      issue(pr.q[hh][0], (g * G + j) * D + lane);
+      issue(pr.q[hh][1], (g * G + j) * D + lane + half);
+    }
+  }
+  if (holds_new && wid == 3) {
+    const int kcol = (a.nq + g) * D, vcol = (a.nq + a.nkv + g) * D;
+    pr.slot = a.slot[row];
+    if (a.k_norm && act) {
+      pr.gk0 = T::to_f(static_cast<const S*>(a.k_norm)[lane]);
+      pr.gk1 = T::to_f(static_cast<const S*>(a.k_norm)[lane + half]);
+    }
+    issue(pr.kv[0], kcol + lane);
+    issue(pr.kv[1], kcol + lane + half);
+    issue(pr.kv[2], vcol + lane);
+    issue(pr.kv[3], vcol + lane + half);
+  }
+}
+
+template <class T, int D, int G>
+__device__ inline void attn_prologue_finish(const AttnRowsArgs& a, int row, int g, bool holds_new,
+                                            const PrologueRegs<G>& pr, float (*qs)[D]) {
+  using S = typename T::S;
+  constexpr int half = D / 2;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const bool act = lane < half;
+  const float* base = a.qkv + static_cast<size_t>(row) * (a.nq + 2 * a.nkv) * D;
+  // partials in order: the kPNP already loaded, then any further ones
+  auto sum = [&](const float(&src)[kPNP], int col) -> float {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPNP; ++k)
+      if (k < a.n_parts) v += src[k];
+    for (int k = kPNP; k < a.n_parts; ++k) v += base[k * a.part_stride + col];
+    return v;
+  };
+#pragma unroll
+  for (int hh = 0; hh < PrologueRegs<G>::HPW; ++hh) {
+    const int j = wid + 4 * hh;
+    if (j < G) {
+      const int col = (g * G + j) * D;
+      float x0 = act ? sum(pr.q[hh][0], col + lane) : 0.f, x1 = act ? sum(pr.q[hh][1], col + lane + half) : 0.f;
+      norm_rope_pair_g<D>(x0, x1, a.q_norm != nullptr, pr.gq0, pr.gq1, a.eps, pr.c, pr.sn);
+      if (act) {
+        qs[j][lane] = x0 * a.scale;
+        qs[j][lane + half] = x1 * a.scale;
+      }
+    }
+  }
+  if (holds_new && wid == 3) {
+    // write the row's new K and V before any key of the split is read
+    const int kcol = (a.nq + g) * D, vcol = (a.nq + a.nkv + g) * D;
+    float k0 = act ? sum(pr.kv[0], kcol + lane) : 0.f, k1 = act ? sum(pr.kv[1], kcol + lane + half) : 0.f;
+    norm_rope_pair_g<D>(k0, k1, a.k_norm != nullptr, pr.gk0, pr.gk1, a.eps, pr.c, pr.sn);
+    const int sl = pr.slot;
+    const int blk = sl >= 0 ? sl / kBlk : a.num_blocks - 1;
+    const int off = sl >= 0 ? sl % kBlk : 0;
+    if (act) {
+      S* kp = static_cast<S*>(a.k_pool) + pool_k_at(blk, a.nkv, g, off, D);
+      S* vp = static_cast<S*>(a.v_pool) + pool_v_at(blk, a.nkv, g, off, D);
+      kp[lane] = T::from_f(k0);
+      kp[lane + half] = T::from_f(k1);
+      vp[lane * kBlk] = T::from_f(sum(pr.kv[2], vcol + lane));
+      vp[(lane + half) * kBlk] = T::from_f(sum(pr.kv[3], vcol + lane + half));
+    }
+  }
+  __syncthreads();
+}
+
 // Combine the four waves' (max, sum, unnormalised output) in wave order, then write the output
 // (single split) or this split's partial. Call after a block barrier that follows the LDS writes.
 template <class T, int D, int G>
@@ -547,6 +673,9 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
   const int nb_new = nblk - 1 - wid;   // the new key's block, relative to this wave's first one
   const bool new_first = a.q == nullptr && holds_new && nb_new >= 0 && nb_new % 4 == 0 && nb_new / 4 < KB;
   const bool pre = (wid < nblk) && !new_first;
+  // the fused prologue's own loads go out first, so its arithmetic overlaps the key/value loads
+  PrologueRegs<G> pr;
+  if (!a.q) attn_prologue_issue<T, D, G>(a, row, g, holds_new, pr);
   if (pre) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -555,7 +684,8 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
       load_v(kb, pb);
     }
   }
-  attn_prologue<T, D, G>(a, row, g, holds_new, qs);
+  if (a.q) attn_prologue<T, D, G>(a, row, g, holds_new, qs);
+  else attn_prologue_finish<T, D, G>(a, row, g, holds_new, pr, qs);
   if (wid < nblk && !pre) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
