@@ -42,26 +42,47 @@ __global__ __launch_bounds__(64) void k_qkv_post(int nq, int nkv, int d, const f
   const int g = h - nq;
   const int col = is_q ? h * d : (nq + g) * d;
   const bool act = lane < half;
-  auto fetch = [&](int c) -> float {
-    float s = 0.f;
-    for (int p = 0; p < n_parts; ++p) s += qkv[p * part_stride + static_cast<size_t>(row) * ld + c];
-    return s;
+  // every load first (the first four partials of each element at once), then the arithmetic; the
+  // partials are summed in order
+  constexpr int NP = 4;
+  const float* base = qkv + static_cast<size_t>(row) * ld;
+  auto issue = [&](float(&dst)[NP], int c) {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) dst[k] = (act && k < n_parts) ? base[k * part_stride + c] : 0.f;
   };
-  float x0 = act ? fetch(col + lane) : 0.f;
-  float x1 = act ? fetch(col + lane + half) : 0.f;
-  const void* gain = is_q ? q_norm : k_norm;
-  if (gain) {
-    const float ss = wave_sum(x0 * x0 + x1 * x1);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
-    const S* gw = static_cast<const S*>(gain);
-    if (act) {
-      x0 = x0 * inv * T::to_f(gw[lane]);
-      x1 = x1 * inv * T::to_f(gw[lane + half]);
-    }
+  auto sum = [&](const float(&src)[NP], int c) -> float {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+      if (k < n_parts) v += src[k];
+    for (int k = NP; k < n_parts; ++k) v += base[k * part_stride + c];
+    return v;
+  };
+  float p0[NP], p1[NP], pv0[NP], pv1[NP];
+  const int vcol = (nq + nkv + g) * d;
+  issue(p0, col + lane);
+  issue(p1, col + lane + half);
+  if (!is_q) {
+    issue(pv0, vcol + lane);
+    issue(pv1, vcol + lane + half);
   }
+  const void* gain = is_q ? q_norm : k_norm;
+  const S* gw = static_cast<const S*>(gain);
+  const float g0 = (gain && act) ? T::to_f(gw[lane]) : 0.f, g1 = (gain && act) ? T::to_f(gw[lane + half]) : 0.f;
   const int p = pos[row];
   const float c = act ? rope_cos[static_cast<size_t>(p) * half + lane] : 0.f;
   const float s = act ? rope_sin[static_cast<size_t>(p) * half + lane] : 0.f;
+  const int sl = is_q ? -1 : slot[row];
+  float x0 = act ? sum(p0, col + lane) : 0.f;
+  float x1 = act ? sum(p1, col + lane + half) : 0.f;
+  if (gain) {
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+    if (act) {
+      x0 = x0 * inv * g0;
+      x1 = x1 * inv * g1;
+    }
+  }
   const float y0 = x0 * c - x1 * s;
   const float y1 = x1 * c + x0 * s;
   if (is_q) {
@@ -72,7 +93,6 @@ __global__ __launch_bounds__(64) void k_qkv_post(int nq, int nkv, int d, const f
     }
     return;
   }
-  const int sl = slot[row];
   const int blk = sl >= 0 ? sl / kBlk : num_blocks - 1;
   const int off = sl >= 0 ? sl % kBlk : 0;
   if (act) {
@@ -80,9 +100,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(int nq, int nkv, int d, const f
     S* vp = static_cast<S*>(v_pool) + pool_v_at(blk, nkv, g, off, d);
     kp[lane] = T::from_f(y0);
     kp[lane + half] = T::from_f(y1);
-    const int vcol = (nq + nkv + g) * d;
-    vp[lane * kBlk] = T::from_f(fetch(vcol + lane));
-    vp[(lane + half) * kBlk] = T::from_f(fetch(vcol + lane + half));
+    vp[lane * kBlk] = T::from_f(sum(pv0, vcol + lane));
+    vp[(lane + half) * kBlk] = T::from_f(sum(pv1, vcol + lane + half));
   }
 }
 
