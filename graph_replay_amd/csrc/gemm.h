@@ -217,20 +217,31 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a, int epi) {
           const float4 rv = *reinterpret_cast<const float4*>(a.r_in + rowoff[mm] + min(e0 + 1024 * sl, K - 4));
           v[mm][sl][0] = rv.x; v[mm][sl][1] = rv.y; v[mm][sl][2] = rv.z; v[mm][sl][3] = rv.w;
         }
-      for (int s = 0; s < a.n_delta; ++s) {
-        const float* dp = a.delta + s * a.delta_stride;
-        float4 dv[MT][NS];
+      // DB partials per round: every load of a round issued before its adds, the adds in partial
+      // order (DB bounded so that the round's loads fit in registers next to the MT rows)
+      constexpr int DB = MT <= 2 ? 4 : (MT <= 4 ? 2 : 1);
+      for (int s0 = 0; s0 < a.n_delta; s0 += DB) {
+        float4 dv[DB][MT][NS];
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
+        for (int b = 0; b < DB; ++b)
+          if (s0 + b < a.n_delta) {
+            const float* dp = a.delta + (s0 + b) * a.delta_stride;
 #pragma unroll
-          for (int sl = 0; sl < NS; ++sl)
-            dv[mm][sl] = *reinterpret_cast<const float4*>(dp + rowoff[mm] + min(e0 + 1024 * sl, K - 4));
+            for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
+              for (int sl = 0; sl < NS; ++sl)
+                dv[b][mm][sl] = *reinterpret_cast<const float4*>(dp + rowoff[mm] + min(e0 + 1024 * sl, K - 4));
+          }
 #pragma unroll
-          for (int sl = 0; sl < NS; ++sl) {
-            v[mm][sl][0] += dv[mm][sl].x; v[mm][sl][1] += dv[mm][sl].y;
-            v[mm][sl][2] += dv[mm][sl].z; v[mm][sl][3] += dv[mm][sl].w;
+        for (int b = 0; b < DB; ++b)
+          if (s0 + b < a.n_delta) {
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+              for (int sl = 0; sl < NS; ++sl) {
+                v[mm][sl][0] += dv[b][mm][sl].x; v[mm][sl][1] += dv[b][mm][sl].y;
+                v[mm][sl][2] += dv[b][mm][sl].z; v[mm][sl][3] += dv[b][mm][sl].w;
+              }
           }
       }
     }
