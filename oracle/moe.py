@@ -26,8 +26,8 @@ Readings (where the page leaves a step open):
   dtype. The HIP path keeps them in fp32 and rounds the activation to the input dtype.
 
 Parity pins (tests/test_oracle_moe.py): a worked grouping example derived by hand from the
-page's definition (tests/golden/moe_align_example.txt), a second, vectorised grouping that
-follows the page's own steps (counts, padded starts, stable order, ranks, search), the
+page's definition (tests/golden/moe_align_example.txt), a second grouping written as scalar
+counting loops over the assignments (counts, group starts, running rank per expert), the
 grouping invariants, brute-force scalar loops on tiny layers, the dense SwiGLU MLP that one
 expert with weight 1 reduces to, linearity in the router weights, and invariance under a
 relabelling of the experts and under a reordering of a token's k slots.

@@ -1,7 +1,7 @@
 """Pins of the MoE oracle (oracle/moe.py) against things other than itself: the grouping worked
 by hand from the definition in "Removing overhead: fusion, graphs and async scheduling" (section
-"A MoE layer that never asks the host"), a second grouping that follows the page's own steps,
-the grouping's invariants, brute-force loops, the dense SwiGLU MLP that one expert reduces to, and
+"A MoE layer that never asks the host"), a second grouping by scalar counting loops, the
+grouping's invariants, brute-force loops, the dense SwiGLU MLP that one expert reduces to, and
 the symmetries of the layer."""
 import os
 
@@ -34,31 +34,37 @@ def test_align_worked_example(golden_dir):
     assert npad == g["num_padded"][0]
 
 
-def _align_by_page_steps(flat, E, bm):
-    """The page's steps, vectorised: counts by scatter-add, padded counts and their exclusive
-    prefix, the unpadded prefix, a stable argsort by expert, each assignment's rank inside its
-    expert, the scatter to padded_start + rank, and the block -> expert search (right side,
-    clamped)."""
-    total = flat.size
+def _align_by_counting(flat, E, bm):
+    """The grouping contract checked with scalar loops, one assignment at a time: count each
+    expert's assignments, lay the groups out in expert order with each group's length rounded up
+    to whole blocks, then place assignment i at its group's first row plus the number of earlier
+    assignments of the same expert. Ids outside [0, E) get no row."""
+    total = len(flat)
     m_max = -(-(total + E * (bm - 1)) // bm) * bm
-    counts = np.zeros(E, np.int64)
-    np.add.at(counts, flat, 1)
-    padded = (counts + bm - 1) // bm * bm
-    padded_start = np.cumsum(padded) - padded
-    start = np.cumsum(counts) - counts
-    order = np.argsort(flat, kind="stable")
-    se = flat[order]
-    rank = np.arange(total) - start[se]
-    sorted_ids = np.full(m_max, total, np.int64)
-    sorted_ids[padded_start[se] + rank] = order
-    block_starts = np.arange(0, m_max, bm)
-    block_expert = np.searchsorted(np.cumsum(padded), block_starts, side="right")
-    return sorted_ids, np.minimum(block_expert, E - 1), int(padded.sum())
+    count = [0] * E
+    for e in flat:
+        if 0 <= e < E:
+            count[e] += 1
+    first_row, row = [0] * E, 0
+    for e in range(E):
+        first_row[e] = row
+        row += -(-count[e] // bm) * bm
+    sorted_ids = [total] * m_max
+    seen = [0] * E
+    for i, e in enumerate(flat):
+        if 0 <= e < E:
+            sorted_ids[first_row[e] + seen[e]] = i
+            seen[e] += 1
+    block_expert = [E - 1] * (m_max // bm)
+    for e in range(E):
+        for r in range(first_row[e], first_row[e] + -(-count[e] // bm) * bm, bm):
+            block_expert[r // bm] = e
+    return np.asarray(sorted_ids), np.asarray(block_expert), row
 
 
 @pytest.mark.parametrize("E,n,k,bm", [(4, 3, 2, 4), (8, 1, 1, 16), (16, 37, 4, 16), (128, 32, 8, 16),
                                       (5, 50, 3, 1), (3, 20, 2, 64), (64, 9, 6, 7), (1, 10, 1, 16)])
-def test_align_equals_page_steps_and_invariants(E, n, k, bm):
+def test_align_equals_counting_loops_and_invariants(E, n, k, bm):
     rng = np.random.default_rng(E * 1000 + n * 10 + k)
     ids = rng.integers(0, E, size=(n, k))
     if E > 4:
@@ -66,7 +72,7 @@ def test_align_equals_page_steps_and_invariants(E, n, k, bm):
     flat = ids.reshape(-1)
     total = flat.size
     s, be, npad = moe.moe_align(ids, E, bm)
-    s2, be2, npad2 = _align_by_page_steps(flat, E, bm)
+    s2, be2, npad2 = _align_by_counting(flat.tolist(), E, bm)
     assert np.array_equal(s, s2) and np.array_equal(be, be2) and npad == npad2
     m_max = moe.align_rows(total, E, bm)
     assert s.size == m_max and m_max % bm == 0 and be.size == m_max // bm

@@ -360,6 +360,102 @@ def test_single_token_layer_closed_form():
     assert np.allclose(hid[0], want, atol=1e-5)
 
 
+def _layer_by_loops(s, w, toks, positions, qk_norm_order="before_rope", qk_norm_span="head"):
+    """One layer, every token of one request, written out with scalar loops in fp64 in the order
+    the per-layer operations are listed for Qwen3-0.6B (Fast decode: syncs, CUDA graphs and
+    compilation, section "Where the time goes"): RMSNorm, Q/K/V, the two QK-norms, RoPE, cache
+    write, causal attention, O projection + residual, RMSNorm, gate/up, SiLU * up, down +
+    residual. Then the final RMSNorm. The two keyword arguments build the wrong variants the test
+    must tell apart: the QK-norm after RoPE, and the QK-norm over all heads of a token at once."""
+    H, d, nq, nkv, I = s.hidden, s.head_dim, s.q_heads, s.kv_heads, s.intermediate
+    L = w["layers"][0]
+    half = d // 2
+
+    def norm(x, g):
+        rms = math.sqrt(sum(a * a for a in x) / len(x) + s.eps)
+        return [x[i] / rms * float(g[i % len(g)]) for i in range(len(x))]
+
+    def mv(W, x, b=None):
+        return [sum(float(W[i][k]) * x[k] for k in range(len(x))) + (float(b[i]) if b is not None else 0.0)
+                for i in range(len(W))]
+
+    def rot(x, pos):                      # rotate-half on one head
+        y = list(x)
+        for i in range(half):
+            a = pos * s.theta ** (-2.0 * i / d)
+            y[i] = x[i] * math.cos(a) - x[i + half] * math.sin(a)
+            y[i + half] = x[i + half] * math.cos(a) + x[i] * math.sin(a)
+        return y
+
+    def heads(x, n):
+        return [x[j * d:(j + 1) * d] for j in range(n)]
+
+    def qk(x, n, g, pos):
+        hs = heads(x, n)
+        if qk_norm_order == "after_rope":
+            hs = [rot(hh, pos) for hh in hs]
+        if qk_norm_span == "head":
+            hs = [norm(hh, g) for hh in hs]
+        else:
+            flat = norm([a for hh in hs for a in hh], g)
+            hs = heads(flat, n)
+        if qk_norm_order == "before_rope":
+            hs = [rot(hh, pos) for hh in hs]
+        return hs
+
+    K, V, res, out = [], [], [], []
+    for t, pos in zip(toks, positions):
+        r = [float(a) for a in w["embed"][t]]
+        h = norm(r, L["in_norm"])
+        K.append(qk(mv(L["wk"], h, L["bk"]), nkv, L["k_norm"], pos))
+        V.append(heads(mv(L["wv"], h, L["bv"]), nkv))
+        res.append((r, qk(mv(L["wq"], h, L["bq"]), nq, L["q_norm"], pos)))
+    for i, (r, q) in enumerate(res):
+        o = []
+        for head in range(nq):
+            g = head // (nq // nkv)
+            sc = [sum(q[head][c] * K[j][g][c] for c in range(d)) / math.sqrt(d)
+                  for j in range(len(toks)) if positions[j] <= positions[i]]
+            m = max(sc)
+            e = [math.exp(x - m) for x in sc]
+            z = sum(e)
+            o += [sum(e[j] / z * V[j][g][c] for j in range(len(e))) for c in range(d)]
+        y = mv(L["wo"], o)
+        r = [r[c] + y[c] for c in range(H)]
+        h2 = norm(r, L["post_norm"])
+        gate, up = mv(L["wg"], h2), mv(L["wu"], h2)
+        a = [gate[c] / (1 + math.exp(-gate[c])) * up[c] for c in range(I)]
+        x = mv(L["wd"], a)
+        out.append(norm([r[c] + x[c] for c in range(H)], w["final_norm"]))
+    return np.asarray(out)
+
+
+def test_qk_norm_per_head_before_rope_closed_form():
+    """Pins where the QK-norm acts and over what: per head, with one gain [d] shared by the heads,
+    before RoPE. Three tokens at positions 0, 1, 2 see 1, 2 and 3 keys, so the scores matter; the
+    gains differ inside every RoPE pair (norm-then-rotate differs from rotate-then-norm only
+    then) and the heads of a token differ in scale (a norm over all heads differs only then)."""
+    s = MICRO.replace(q_heads=4, kv_heads=2, hidden=8, head_dim=4, intermediate=6)
+    w = _fp32_weights(s, seed=4)
+    rng = np.random.default_rng(44)
+    L = w["layers"][0]
+    L["q_norm"] = rng.uniform(0.3, 2.5, s.head_dim).astype(F32)
+    L["k_norm"] = rng.uniform(0.3, 2.5, s.head_dim).astype(F32)
+    # head-dependent scale in the Q and K projections, so per-head and all-head norms differ
+    L["wq"] = (L["wq"] * np.repeat(np.array([1.0, 4.0, 0.5, 2.0], F32), s.head_dim)[:, None] * 40).astype(F32)
+    L["wk"] = (L["wk"] * np.repeat(np.array([3.0, 0.4], F32), s.head_dim)[:, None] * 40).astype(F32)
+    L["wv"] = (L["wv"] * 40).astype(F32)
+    L["wo"] = (L["wo"] * 40).astype(F32)
+    toks, pos = [3, 7, 1], [0, 1, 2]
+    got = oracle.forward_request(s, w, oracle.RequestCache(1), toks, pos)
+    want = _layer_by_loops(s, w, toks, pos)
+    assert np.allclose(got, want, atol=2e-5), np.abs(got - want).max()
+    # the closed form tells the right order and span from the two plausible wrong ones
+    for kw in ({"qk_norm_order": "after_rope"}, {"qk_norm_span": "all_heads"}):
+        wrong = _layer_by_loops(s, w, toks, pos, **kw)
+        assert np.abs(wrong[1:] - want[1:]).max() > 100 * 2e-5, kw
+
+
 def test_incremental_decode_equals_full_sequence_prefill():
     s = synth.TINY
     w = _fp32_weights(s)
