@@ -19,7 +19,7 @@ from ._lib import (STEP_BF16, STEP_F16, STEP_F32, MoeLayer, StepBatch, StepBuffe
                    StepWeights)
 
 __all__ = ["Decoder", "StepError", "step_workspace_bytes", "step_init", "step_decode", "step_mixed", "step_sample",
-           "step_destroy", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "MoeLayer"]
+           "step_destroy", "step_set_device_status", "step_attention_splits", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "MoeLayer"]
 
 load = _lib.load
 
@@ -100,6 +100,17 @@ def step_sample(ctx, d_logits: int, rows: int, ld: int, vocab: int, h_temperatur
 
 def step_device_status(ctx) -> None:
     _raise(_lib.load().step_device_status(ctx), ctx)
+
+
+def step_set_device_status(ctx, site: int) -> None:
+    _raise(_lib.load().step_set_device_status(ctx, site), ctx)
+
+
+def step_attention_splits(cfg: StepConfig, rows: int, max_len: int):
+    """(splits per row, partial slots of the workspace) of the decode attention grid; host only."""
+    slots = C.c_int64(-1)
+    n = int(_lib.load().step_attention_splits(C.byref(cfg), rows, max_len, C.byref(slots)))
+    return n, int(slots.value)
 
 
 def step_destroy(ctx) -> None:
@@ -373,6 +384,10 @@ class Decoder:
     def device_status(self) -> None:
         """Raise StepError if a wait inside a persistent decode step gave up (waits for the stream)."""
         step_device_status(self.ctx)
+
+    def set_device_status(self, site: int) -> None:
+        """Set the persistent step's give-up flag as a wait that gave up at `site` would (tests)."""
+        step_set_device_status(self.ctx, site)
 
     def phase_stamps(self):
         """Phase timestamps (us) of the last profiled persistent step, or None."""

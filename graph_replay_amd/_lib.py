@@ -75,6 +75,8 @@ EXPORTS = {
     "step_last_error": (C.c_char_p, [P]),
     "step_device_status": (C.c_int, [P]),
     "step_phase_stamps": (C.c_int, [P, C.c_int32, C.POINTER(C.c_double)]),
+    "step_set_device_status": (C.c_int, [P, C.c_int32]),
+    "step_attention_splits": (C.c_int32, [C.POINTER(StepConfig), C.c_int32, C.c_int32, C.POINTER(C.c_int64)]),
     "step_destroy": (None, [P]),
     "moe_align_rows": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32]),
     "moe_align": (C.c_int, [I32P, C.c_int32, C.c_int32, C.c_int32, I32P, I32P, I32P, P]),

@@ -13,13 +13,17 @@ namespace {
 
 thread_local std::string g_err;
 
-int fail(int code, const char* fmt, ...) {
+int fail(int code, const char* fmt, ...) noexcept {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_err = buf;
+  try {
+    g_err = buf;
+  } catch (...) {
+    // no memory for the message: the code still reports the failure
+  }
   return code;
 }
 
@@ -140,6 +144,7 @@ extern "C" int32_t moe_align_rows(int32_t total, int32_t num_experts, int32_t bl
 
 extern "C" int moe_align(const int32_t* d_expert_ids, int32_t total, int32_t num_experts, int32_t block_m,
                          int32_t* d_sorted_ids, int32_t* d_block_expert, int32_t* d_num_padded, void* stream) {
+  // nothing below allocates host memory or throws: the checks are arithmetic and the launch is HIP
   g_err.clear();
   const long long m = rows_for(total, num_experts, block_m);
   if (m < 0) return fail(STEP_EINVAL, "moe_align: total %d, num_experts %d (1..%d), block_m %d (1..65536)", total,
@@ -151,12 +156,14 @@ extern "C" int moe_align(const int32_t* d_expert_ids, int32_t total, int32_t num
 }
 
 extern "C" size_t moe_workspace_bytes(const moe_layer* layer) {
+  // host arithmetic only; fail() swallows a failed message allocation
   MoeLayout lay;
   if (check_layer(layer, &lay) != STEP_OK) return 0;
   return lay.total;
 }
 
 extern "C" int moe_forward(const moe_layer* layer, void* d_workspace, size_t workspace_bytes, void* stream) {
+  // as moe_align: checks and launches only, and fail() never throws
   g_err.clear();
   MoeLayout lay;
   int rc = check_layer(layer, &lay);

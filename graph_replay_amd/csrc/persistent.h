@@ -1068,6 +1068,18 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
   }
   __syncthreads();
   if (!sh.last) return;
+  // A wait that gave up (now or in an earlier step whose failure the host has not yet collected
+  // with step_device_status) leaves this step's values undefined: the logits become NaN, the token
+  // -1, and the row does not advance, so a replay loop cannot feed them forward. Every block's
+  // stores completed before it counted itself in, so these stores come last.
+  if (ld_dev(a.err) != 0) {
+    for (int i = threadIdx.x; i < a.vocab; i += kPThreads) a.logits[i] = __builtin_nanf("");
+    if (threadIdx.x == 0) {
+      if (a.sample) a.tokens[0] = -1;
+      __hip_atomic_store(a.epoch, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
   if (a.sample) {
     unsigned long long b = 0ull;
     for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += kPThreads) {
@@ -1080,8 +1092,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
     if (threadIdx.x == 0) {
       for (int w = 0; w < 8; ++w) b = sh.cand[w] > b ? sh.cand[w] : b;
       const int tok = static_cast<int>(~static_cast<uint32_t>(b));
-      a.tokens[0] = tok;
-      advance_row(tok, a.ids, a.pos, a.len, a.slot, a.bt, a.bt_stride, a.history, a.max_position);
+      // no candidate (every score NaN): token -1 and no advance, as for a wait that gave up
+      const bool ok = tok >= 0 && tok < a.vocab;
+      a.tokens[0] = ok ? tok : -1;
+      if (ok) advance_row(tok, a.ids, a.pos, a.len, a.slot, a.bt, a.bt_stride, a.history, a.max_position);
       a.rng[1] = st.stepc + 1;
     }
   }

@@ -371,6 +371,7 @@ struct SampleArgs {
   int bt_stride;
   int* history;                       // [rows][hist_ld] or nullptr
   int hist_ld;                        // max_position: positions at or past it end the row
+  const int* halt;                    // nonzero *halt: the logits are invalid (token -1, no advance)
 };
 
 __device__ inline void best_merge(float& v, int& i, float v2, int i2) {
@@ -402,9 +403,11 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   __shared__ int si[4];
   __shared__ int last_flag;
   const int row = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+  // invalid logits (see halt): nothing advances, the Philox step counter included
+  const bool halted = a.halt && ld_dev(a.halt) != 0;
   if (a.n_rows && row >= *a.n_rows) {
     // idle row: still counted in by one block, so the step counter and its reset stay exact
-    if (ch == 0 && threadIdx.x == 0 && a.rng && arrive_last(a.done_cnt, gridDim.x)) {
+    if (ch == 0 && threadIdx.x == 0 && a.rng && arrive_last(a.done_cnt, gridDim.x) && !halted) {
       uint64_t* r = const_cast<uint64_t*>(a.rng);
       r[1] = r[1] + 1;
     }
@@ -465,13 +468,16 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     block_best(bv, bi, sv, si);
   }
   if (threadIdx.x != 0) return;
-  const int tok = bi;
+  // a row with no candidate (every score NaN) or whose logits are marked invalid gets token -1 and
+  // is not advanced, so a replay loop never embeds an id outside the vocabulary
+  const bool ok = bi >= 0 && bi < a.vocab && !halted;
+  const int tok = ok ? bi : -1;
   a.tokens_out[row] = tok;
-  if (a.advance)
+  if (a.advance && ok)
     advance_row(tok, a.input_ids + row, a.positions + row, a.seq_lens + row, a.slots + row,
                 a.block_table + static_cast<size_t>(row) * a.bt_stride, a.bt_stride,
                 a.history ? a.history + static_cast<size_t>(row) * a.hist_ld : nullptr, a.hist_ld);
-  if (a.rng && arrive_last(a.done_cnt, gridDim.x)) {
+  if (a.rng && arrive_last(a.done_cnt, gridDim.x) && !halted) {
     uint64_t* r = const_cast<uint64_t*>(a.rng);
     r[1] = step + 1;
   }

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -44,7 +45,7 @@ struct Layout {  // byte offsets into the workspace
   int p_splits;                       // attention splits per KV head the partial words hold
   size_t total;
   int TM, RM, LM;                     // token rows, requests, sampled rows the buffers hold
-  int max_splits_alloc;               // splits per row the partial buffer holds (at 64 keys/split)
+  size_t attn_slots;                  // (row, split) partial slots the attention partials hold
   int ksplit_max;                     // partial copies of split-K outputs
 };
 
@@ -104,14 +105,18 @@ static const void* c_final_norm_of(step_ctx* ctx) { return ctx->w.d_final_norm; 
 
 namespace {
 
-int fail(step_ctx* c, int code, const char* fmt, ...) {
+int fail(step_ctx* c, int code, const char* fmt, ...) noexcept {
   if (c) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    c->err = buf;
+    try {
+      c->err = buf;
+    } catch (...) {
+      // no memory for the message: the code still reports the failure
+    }
   }
   return code;
 }
@@ -183,6 +188,16 @@ int split_tokens_for(int rows, int max_len) {
   return P;
 }
 
+// (row, split) partial slots that attention over `rows` rows may use at any key bound up to
+// max_position. The split count is not monotone in the key bound (the split length doubles once a
+// row would need more than kMaxSplits splits), so the bound uses the shortest split length any key
+// bound can give this row count (512 keys stands for 2,048 where longer rows are possible) and
+// caps it at kMaxSplits.
+size_t attn_slots_bound(int rows, int max_position) {
+  const int P = rows <= 8 ? 64 : (rows <= 64 && max_position <= 2560 ? 2048 : 512);
+  return static_cast<size_t>(rows) * std::min(gr::kMaxSplits, (max_position + P - 1) / P);
+}
+
 // copies of split-K partial outputs the workspace holds
 constexpr int kMaxKsplit = 8;
 // weight-prefetch blocks appended to an attention launch (about one per CU)
@@ -226,14 +241,11 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.d_o = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * H);
   L.d_d = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * H);
   L.act = take(static_cast<size_t>(eb) * TM * I);
-  // attention partials: rows * ceil(max_position / split) splits, maximised over row classes
+  // attention partials: the most (row, split) slots any row count up to TM can use (the bound is
+  // constant inside each row class, so its largest row count gives the class maximum)
   size_t part_rows_splits = 0;
-  for (int rows : {8, TM}) {
-    const int r = std::min(rows, TM);
-    const int P = split_tokens_for(r, c.max_position);
-    part_rows_splits = std::max(part_rows_splits, static_cast<size_t>(r) * ((c.max_position + P - 1) / P));
-  }
-  L.max_splits_alloc = 0;
+  for (int rows : {8, 64, TM}) part_rows_splits = std::max(part_rows_splits, attn_slots_bound(std::min(rows, TM), c.max_position));
+  L.attn_slots = part_rows_splits;
   L.attn_part = take(sizeof(float) * part_rows_splits * nq * (d + 2));
   L.attn_cnt = take(sizeof(unsigned) * static_cast<size_t>(TM) * nkv);
   const int nch_max = (c.vocab + 1023) / 1024;
@@ -573,6 +585,9 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
   const int G = c.q_heads / c.kv_heads;
   if (rows > Ly.TM) return fail(ctx, STEP_EINVAL, "attention over %d rows exceeds the workspace's %d", rows, Ly.TM);
+  if (static_cast<size_t>(rows) * a.max_splits > Ly.attn_slots)
+    return fail(ctx, STEP_EINVAL, "attention over %d rows x %d splits exceeds the workspace's %zu partial slots", rows,
+                a.max_splits, Ly.attn_slots);
   dim3 grid(rows, c.kv_heads, a.max_splits);
   if (ctx->pf.n > 0) {
     a.pf = ctx->pf;
@@ -605,7 +620,8 @@ int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_st
 int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, const float* temp, const float* uniforms,
                const uint64_t* rng, uint64_t seed, uint64_t stepc, int* tokens_out, int advance, int* ids, int* pos,
                int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld,
-               const int* n_rows = nullptr, const int* topk = nullptr, const float* topp = nullptr) {
+               const int* n_rows = nullptr, const int* topk = nullptr, const float* topp = nullptr,
+               const int* halt = nullptr) {
   uint2* filt = nullptr;
   if (temp && (topk || topp)) {
     // per-row top-k / top-p cut first (one block of 1024 threads per row)
@@ -635,6 +651,7 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
   a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
   a.n_rows = n_rows;
   a.filt = filt;
+  a.halt = halt;
   const int nch = (vocab + chunk - 1) / chunk;
   pre_launch(ctx, KK_SAMPLE);
   launch(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
@@ -877,9 +894,10 @@ int run_decode(step_ctx* ctx, int B) {
   if (ctx->p_nb > 0 && B == 1) {
     TRY(run_persist<T>(ctx, m));
     if (!c.sampling_filters) return STEP_OK;
+    // the persistent kernel's give-up word stops the separate sampler's token and advance too
     return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
-                      m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr,
-                      c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
+                      m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr, m.topk, m.topp,
+                      reinterpret_cast<const int*>(ctx->ws + L.p_ctl) + 2);
   }
   const float* q = reinterpret_cast<const float*>(ctx->ws + L.q);
   void* attn_o = ctx->ws + L.attn_o;
@@ -1067,18 +1085,15 @@ int bucket_index(const step_config& c, int b) {
 // ================================================================================================
 // C ABI
 
-extern "C" size_t step_workspace_bytes(const step_config* cfg) {
+static size_t step_workspace_bytes_body(const step_config* cfg) {
   if (validate_config(nullptr, cfg) != STEP_OK) return 0;
   Layout L{};
   compute_layout(*cfg, L);
   return L.total;
 }
 
-extern "C" int step_init(const step_config* cfg, const step_weights* w, const step_buffers* b, void* stream,
-                         step_ctx** out) {
-  if (!out) return STEP_EINVAL;
-  *out = nullptr;
-  step_ctx* ctx = new step_ctx();
+static int step_init_body(step_ctx* ctx, const step_config* cfg, const step_weights* w, const step_buffers* b,
+                          void* stream, step_ctx** out) {
   auto bail = [&](int rc) {
     // keep the context so the caller can read the message; it is marked dead
     ctx->dead = true;
@@ -1291,7 +1306,7 @@ extern "C" int step_init(const step_config* cfg, const step_weights* w, const st
   return STEP_OK;
 }
 
-extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) {
+static int step_decode_body(step_ctx* ctx, const step_batch* hb) {
   if (!ctx || ctx->dead) return STEP_ESTATE;
   const step_config& c = ctx->cfg;
   int B;
@@ -1365,7 +1380,7 @@ extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) {
   return STEP_OK;
 }
 
-extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
+static int step_mixed_body(step_ctx* ctx, const step_packed* hp) {
   if (!ctx || ctx->dead) return STEP_ESTATE;
   const step_config& c = ctx->cfg;
   if (!hp) return fail(ctx, STEP_EINVAL, "batch is NULL");
@@ -1481,7 +1496,7 @@ extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) {
 
 extern "C" int step_last_mixed_bucket(const step_ctx* ctx) { return ctx ? ctx->last_mixed_bucket : STEP_ESTATE; }
 
-extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, int32_t ld, int32_t vocab,
+static int step_sample_body(step_ctx* ctx, const float* d_logits, int32_t rows, int32_t ld, int32_t vocab,
                            const float* h_temperature, const int32_t* h_top_k, const float* h_top_p,
                            const float* d_uniforms, uint64_t seed, uint64_t counter, int32_t* d_tokens_out) {
   if (!ctx || ctx->dead) return STEP_ESTATE;
@@ -1516,7 +1531,7 @@ extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, i
                     nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, topk, topp);
 }
 
-extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_ms, int32_t* h_kind) {
+static int step_profile_decode_body(step_ctx* ctx, int32_t max_kernels, float* h_ms, int32_t* h_kind) {
   if (!ctx || ctx->dead) return STEP_ESTATE;
   if (!ctx->have_batch) return fail(ctx, STEP_EINVAL, "profile step before any batch");
   if (max_kernels < 1 || !h_ms || !h_kind) return fail(ctx, STEP_EINVAL, "bad profile buffers");
@@ -1571,7 +1586,7 @@ extern "C" int step_phase_stamps(const step_ctx* ctx, int32_t max_stamps, double
   return gr::kPStamps;
 }
 
-extern "C" int step_device_status(step_ctx* ctx) {
+static int step_device_status_body(step_ctx* ctx) {
   if (!ctx || ctx->dead) return STEP_ESTATE;
   if (ctx->p_nb == 0) return STEP_OK;
   HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
@@ -1581,6 +1596,84 @@ extern "C" int step_device_status(step_ctx* ctx) {
   if (v == 0) return STEP_OK;
   HIPCHK(ctx, hipMemset(err, 0, sizeof v));
   return fail(ctx, STEP_EHIP, "persistent decode step: a wait gave up (site %d); that step's outputs are invalid", v);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Exported entry points: each runs its body under a catch-all, so no C++ exception (a failed host
+// allocation in a std::vector or std::string, say) ever unwinds across the C ABI.
+
+#define STEP_GUARDED(ctx, body)                                                          \
+  try {                                                                                  \
+    return body;                                                                         \
+  } catch (const std::bad_alloc&) {                                                      \
+    return fail((ctx), STEP_EHIP, "host memory allocation failed");                      \
+  } catch (...) {                                                                        \
+    return fail((ctx), STEP_EHIP, "unexpected C++ exception inside the library");        \
+  }
+
+extern "C" size_t step_workspace_bytes(const step_config* cfg) {
+  try {
+    return step_workspace_bytes_body(cfg);
+  } catch (...) {
+    return 0;
+  }
+}
+
+extern "C" int step_init(const step_config* cfg, const step_weights* w, const step_buffers* b, void* stream,
+                         step_ctx** out) {
+  if (!out) return STEP_EINVAL;
+  *out = nullptr;
+  step_ctx* ctx = new (std::nothrow) step_ctx();
+  if (!ctx) return STEP_EHIP;
+  try {
+    return step_init_body(ctx, cfg, w, b, stream, out);
+  } catch (...) {
+    // the context is handed back dead so that the caller can read the message and destroy it
+    ctx->dead = true;
+    *out = ctx;
+    return fail(ctx, STEP_EHIP, "host memory allocation failed during step_init");
+  }
+}
+
+extern "C" int step_decode(step_ctx* ctx, const step_batch* hb) { STEP_GUARDED(ctx, step_decode_body(ctx, hb)) }
+
+extern "C" int step_mixed(step_ctx* ctx, const step_packed* hp) { STEP_GUARDED(ctx, step_mixed_body(ctx, hp)) }
+
+extern "C" int step_sample(step_ctx* ctx, const float* d_logits, int32_t rows, int32_t ld, int32_t vocab,
+                           const float* h_temperature, const int32_t* h_top_k, const float* h_top_p,
+                           const float* d_uniforms, uint64_t seed, uint64_t counter, int32_t* d_tokens_out) {
+  STEP_GUARDED(ctx, step_sample_body(ctx, d_logits, rows, ld, vocab, h_temperature, h_top_k, h_top_p, d_uniforms, seed,
+                                     counter, d_tokens_out))
+}
+
+extern "C" int step_profile_decode(step_ctx* ctx, int32_t max_kernels, float* h_ms, int32_t* h_kind) {
+  STEP_GUARDED(ctx, step_profile_decode_body(ctx, max_kernels, h_ms, h_kind))
+}
+
+extern "C" int step_device_status(step_ctx* ctx) { STEP_GUARDED(ctx, step_device_status_body(ctx)) }
+
+extern "C" int step_set_device_status(step_ctx* ctx, int32_t site) {
+  if (!ctx || ctx->dead) return STEP_ESTATE;
+  if (ctx->p_nb == 0) return fail(ctx, STEP_EINVAL, "the context has no persistent decode step");
+  if (site <= 0) return fail(ctx, STEP_EINVAL, "site %d: must be positive", site);
+  int* err = reinterpret_cast<int*>(ctx->ws + ctx->lay.p_ctl) + 2;
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  HIPCHK(ctx, hipMemcpy(err, &site, sizeof site, hipMemcpyHostToDevice));
+  return STEP_OK;
+}
+
+extern "C" int32_t step_attention_splits(const step_config* cfg, int32_t rows, int32_t max_len, int64_t* slots) {
+  try {
+    if (validate_config(nullptr, cfg) != STEP_OK) return STEP_EINVAL;
+    Layout L{};
+    compute_layout(*cfg, L);
+    if (slots) *slots = static_cast<int64_t>(L.attn_slots);
+    if (rows < 1 || rows > L.TM || max_len < 1 || max_len > cfg->max_position) return STEP_EINVAL;
+    const int P = split_tokens_for(rows, max_len);
+    return (max_len + P - 1) / P;
+  } catch (...) {
+    return STEP_EHIP;
+  }
 }
 
 extern "C" const char* step_kernel_kind_name(int32_t kind) {

@@ -212,9 +212,27 @@ int step_profile_decode(step_ctx *ctx, int32_t max_kernels, float *h_ms, int32_t
 const char *step_kernel_kind_name(int32_t kind);
 /* Persistent decode only (persistent_decode = 1): waits for the context's stream, then reports
  * whether any wait inside a persistent decode step gave up since the last call (it bounds every
- * wait, so a step always ends; one that gave up has invalid outputs). STEP_OK, or STEP_EHIP with the
- * site in step_last_error; the flag is cleared. Without persistent_decode it returns STEP_OK. */
+ * wait, so a step always ends). STEP_OK, or STEP_EHIP with the site in step_last_error; the flag is
+ * cleared. Without persistent_decode it returns STEP_OK.
+ * While the flag is set, every persistent step (the one whose wait gave up and every later one, in
+ * graph replays too) ends with its outputs marked invalid instead of computed: logits row 0 is NaN,
+ * token 0 is -1, and the row is not advanced (input id, position, seq_len, slot and history keep
+ * their values), so a device-continued loop never feeds an invalid token forward. The same holds
+ * for any sampled row with no candidate (every score NaN): token -1, no advance. */
 int step_device_status(step_ctx *ctx);
+/* Test aid for the failure contract above: waits for the context's stream and sets the persistent
+ * step's give-up flag to `site` (> 0) as a wait that gave up would, so that every bounded wait of
+ * the next steps ends at once and their outputs are marked invalid. STEP_EINVAL without
+ * persistent_decode or for site <= 0. step_device_status reports and clears it. */
+int step_set_device_status(step_ctx *ctx, int32_t site);
+/* Host-only sizing query of the decode attention's split-KV grid ("Removing overhead: fusion,
+ * graphs and async scheduling", section "CUDA graphs for a changing batch": the split count is
+ * fixed per launch shape, never chosen from the batch's contents). Returns the splits per row that
+ * attention over `rows` rows with keys bounded by max_len uses (rows in [1, max(max_batch,
+ * max_tokens)], max_len in [1, max_position]; STEP_EINVAL otherwise or for an invalid config), and
+ * writes to *slots (when not NULL, and whenever cfg is valid) the (row, split) partial slots the
+ * workspace of this config holds. rows * splits never exceeds *slots. */
+int32_t step_attention_splits(const step_config *cfg, int32_t rows, int32_t max_len, int64_t *slots);
 /* Phase timestamps of the last step_profile_decode of a persistent single-row step, in
  * microseconds after the kernel's start (block 0's view; -1 where none was taken): slot 8 l + k for
  * layer l holds k = 1 QKV input normed, 2 attention items done, 3 merges done, 4 O input arrived,

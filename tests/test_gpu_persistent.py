@@ -249,3 +249,56 @@ def test_persistent_fused_sampling_equals_separate_sampler(torch_cuda):
     assert ds.kernels_per_decode(1) == 3   # step kernel, filter, sampler
     df.close()
     ds.close()
+
+
+@pytest.mark.parametrize("filters", [False, True])
+def test_persistent_given_up_wait_poisons_outputs_and_stops_advance(torch_cuda, filters):
+    """The failure contract of the persistent step, forced from the host: with the give-up flag set
+    (as a wait that gave up would set it) every bounded wait ends at once and every kernel exits
+    normally; each step then writes NaN logits and token -1 and does not advance the row (graph
+    replays included), with the sampler fused into the kernel and with the separate sampler behind
+    it. step_device_status reports and clears the flag, and the next step continues exactly where
+    the last good step left off: its logits and token equal, bit for bit, those of an identical
+    decoder that never failed."""
+    import graph_replay_amd as g
+    torch = torch_cuda
+    shape = synth.QWEN3_0_6B.replace(layers=2, vocab=4096)
+    W = synth.make_weights(shape, 0)
+    n = 200
+    sc = Scenario(shape, W, [n], steps=8, seed=1104)
+    table, bt = sc.tables[0], sc.table_array()
+    kw = dict(num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=n + 32, max_batch=1,
+              buckets=[1], history=True, persistent_decode=True, sampling_filters=filters)
+    df = _decoder(shape, W, **kw)     # fails twice in the middle
+    dr = _decoder(shape, W, **kw)     # reference: never fails
+    for d in (df, dr):
+        sc.inject(d)
+    args = ([int(sc.tokens[0])], [n], [n + 1], [oracle.slot_of(table, n, 16)], bt)
+    temp = np.full(1, 0.9, np.float32)
+    for d in (df, dr):
+        d.decode(*args, temperature=temp, seed=77)
+        d.decode_continue()
+    torch.cuda.synchronize()
+    df.device_status()
+    good_hist = df.history[0].cpu().numpy().copy()
+    log("forcing the give-up flag, filters", filters)
+    df.set_device_status(5)
+    for _ in range(2):
+        df.decode_continue()       # graph replays with every wait giving up at once
+        torch.cuda.synchronize()
+        assert int(df.tokens[0].item()) == -1
+        assert bool(torch.isnan(df.logits[0]).all().item())
+        assert np.array_equal(df.history[0].cpu().numpy(), good_hist)   # no advance
+    with pytest.raises(g.StepError, match="site 5"):
+        df.device_status()
+    df.device_status()             # cleared
+    for i in range(3):
+        df.decode_continue()
+        dr.decode_continue()
+        torch.cuda.synchronize()
+        df.device_status()
+        assert np.array_equal(df.logits[0].cpu().numpy(), dr.logits[0].cpu().numpy()), i
+        assert int(df.tokens[0].item()) == int(dr.tokens[0].item()) >= 0, i
+    assert np.array_equal(df.history[0].cpu().numpy(), dr.history[0].cpu().numpy())
+    df.close()
+    dr.close()

@@ -126,3 +126,44 @@ def test_moe_sizes_are_host_only_and_validate():
     assert lib.moe_forward(C.byref(layer(dtype=L.STEP_F32)), None, 0, None) == L.STEP_EUNSUPPORTED
     assert b"dtype" in lib.moe_last_error()
     assert lib.moe_forward(C.byref(layer(inter=700)), None, 0, None) == L.STEP_EINVAL
+
+
+def _q3_cfg(L, max_position, max_batch=8, max_tokens=0):
+    cfg = L.StepConfig(dtype=L.STEP_BF16, layers=2, hidden=1024, q_heads=16, kv_heads=8, head_dim=128,
+                       intermediate=3072, vocab=151936, qk_norm=1, qkv_bias=0, rms_eps=1e-6, rope_theta=1e6,
+                       block_size=16, num_blocks=100, max_blocks_per_seq=(max_position + 15) // 16,
+                       max_position=max_position, max_batch=max_batch, max_tokens=max_tokens,
+                       max_reqs=max(max_batch, 1) if max_tokens else 0, max_logit_rows=max_batch if max_tokens else 0,
+                       num_buckets=1, use_graphs=1)
+    cfg.buckets[0] = max_batch
+    return cfg
+
+
+@pytest.mark.parametrize("max_position,max_batch,max_tokens", [(9000, 8, 32), (9000, 8, 0), (20000, 64, 600),
+                                                               (2304, 32, 0), (8192, 1, 0), (16384, 256, 0)])
+def test_attention_partials_hold_every_split_grid(max_position, max_batch, max_tokens):
+    """For every row count and key bound a launch can use, rows x splits fits the workspace's partial
+    slots. The split count is not monotone in the key bound (the split length doubles past 128
+    splits), so the sweep covers every key bound, not just max_position."""
+    import graph_replay_amd as g
+    import graph_replay_amd._lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libstep.so not built")
+    cfg = _q3_cfg(L, max_position, max_batch, max_tokens)
+    tm = max(max_batch, max_tokens)
+    _, slots = g.step_attention_splits(cfg, 1, 1)
+    assert slots > 0
+    worst = 0
+    for rows in sorted({1, 2, 7, 8, 9, 32, 63, 64, 65, tm} & set(range(1, tm + 1))):
+        for max_len in range(1, max_position + 1, 7 if max_position > 10000 else 3):
+            n, s = g.step_attention_splits(cfg, rows, max_len)
+            assert 1 <= n <= 128 and s == slots
+            worst = max(worst, rows * n)
+        n, _ = g.step_attention_splits(cfg, rows, max_position)
+        worst = max(worst, rows * n)
+    assert worst <= slots
+    # the case that once overflowed: 8 rows at 8,192 keys under a 9,000-position bound uses 128 splits
+    if max_position == 9000:
+        assert g.step_attention_splits(cfg, 8, 8192)[0] == 128 and 8 * 128 <= slots
+    assert g.step_attention_splits(cfg, tm + 1, 16)[0] == L.STEP_EINVAL
+    assert g.step_attention_splits(cfg, 1, max_position + 1)[0] == L.STEP_EINVAL
