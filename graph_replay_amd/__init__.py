@@ -19,7 +19,8 @@ from ._lib import (STEP_BF16, STEP_F16, STEP_F32, MoeLayer, StepBatch, StepBuffe
                    StepWeights)
 
 __all__ = ["Decoder", "StepError", "step_workspace_bytes", "step_init", "step_decode", "step_mixed", "step_sample",
-           "step_destroy", "step_set_device_status", "step_attention_splits", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "MoeLayer"]
+           "step_destroy", "step_set_device_status", "step_attention_splits", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "moe_forward_static",
+           "MoeLayer"]
 
 load = _lib.load
 
@@ -200,6 +201,15 @@ def moe_forward(x, gate_up, down, weights, expert_ids, out=None, workspace=None)
         raise ValueError(f"moe_forward: workspace of {workspace.numel()} bytes, needs {need}")
     _moe_raise(lib.moe_forward(C.byref(L), C.c_void_p(workspace.data_ptr()), workspace.numel(),
                                C.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)))
+    return out
+
+
+def moe_forward_static(x, gate_up, down, weights, expert_ids, out):
+    """moe_forward over libstep's static per-device workspace (no workspace argument, nothing
+    allocated by the call); out [N, D] must be given."""
+    import torch
+    L = _moe_struct(x, gate_up, down, weights, expert_ids, out)
+    _moe_raise(_lib.load().moe_forward_static(C.byref(L), C.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)))
     return out
 
 

@@ -82,6 +82,7 @@ EXPORTS = {
     "moe_align": (C.c_int, [I32P, C.c_int32, C.c_int32, C.c_int32, I32P, I32P, I32P, P]),
     "moe_workspace_bytes": (C.c_size_t, [C.POINTER(MoeLayer)]),
     "moe_forward": (C.c_int, [C.POINTER(MoeLayer), P, C.c_size_t, P]),
+    "moe_forward_static": (C.c_int, [C.POINTER(MoeLayer), P]),
     "moe_last_error": (C.c_char_p, []),
 }
 

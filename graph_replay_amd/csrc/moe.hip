@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -136,6 +137,47 @@ int forward(const moe_layer* L, char* ws, const MoeLayout& lay, hipStream_t s) {
   return launched("moe sum");
 }
 
+// The allocation-free variant's workspace: one array per GPU, resident from the library's load
+// until the process ends. In host code `scratch` names a host-side stand-in, not device memory, so
+// its device address is looked up once per device with hipGetSymbolAddress (with that device
+// current) and only that address is ever passed to a kernel.
+__device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// this device's copy of `scratch` (nullptr and a message on failure)
+void* scratch_for_current_device() noexcept {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(STEP_EHIP, "moe_forward_static: hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(STEP_EUNSUPPORTED, "moe_forward_static: device %d is past the %d devices it keeps a workspace for", dev,
+         kMaxDevices);
+    return nullptr;
+  }
+  try {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        fail(STEP_EHIP, "moe_forward_static: hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        return nullptr;
+      }
+      g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+  } catch (...) {
+    fail(STEP_EHIP, "moe_forward_static: could not lock the workspace table");
+    return nullptr;
+  }
+}
+
 }  // namespace
 
 extern "C" int32_t moe_align_rows(int32_t total, int32_t num_experts, int32_t block_m) {
@@ -177,6 +219,25 @@ extern "C" int moe_forward(const moe_layer* layer, void* d_workspace, size_t wor
   if (workspace_bytes < lay.total)
     return fail(STEP_EINVAL, "moe_forward: workspace %zu bytes, needs %zu", workspace_bytes, lay.total);
   char* ws = static_cast<char*>(d_workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return layer->dtype == STEP_BF16 ? forward<gr::BF16>(layer, ws, lay, s) : forward<gr::F16>(layer, ws, lay, s);
+}
+
+extern "C" int moe_forward_static(const moe_layer* layer, void* stream) {
+  // as moe_forward, over this device's static workspace: no allocation of any kind
+  g_err.clear();
+  MoeLayout lay;
+  int rc = check_layer(layer, &lay);
+  if (rc != STEP_OK) return rc;
+  if (lay.total > MOE_STATIC_SCRATCH_BYTES)
+    return fail(STEP_EINVAL, "moe_forward_static: the layer needs %zu workspace bytes, the static workspace holds %zu",
+                lay.total, static_cast<size_t>(MOE_STATIC_SCRATCH_BYTES));
+  if (layer->n_tokens == 0) return STEP_OK;
+  if (!layer->d_x || !layer->d_gate_up || !layer->d_down || !layer->d_weights || !layer->d_expert_ids ||
+      !layer->d_out)
+    return fail(STEP_EINVAL, "moe_forward_static: NULL device pointer");
+  char* ws = static_cast<char*>(scratch_for_current_device());
+  if (!ws) return STEP_EHIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return layer->dtype == STEP_BF16 ? forward<gr::BF16>(layer, ws, lay, s) : forward<gr::F16>(layer, ws, lay, s);
 }

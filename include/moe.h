@@ -79,6 +79,23 @@ size_t moe_workspace_bytes(const moe_layer* layer);
  * pointers, STEP_EUNSUPPORTED for another dtype, STEP_EHIP when a launch fails. */
 int moe_forward(const moe_layer* layer, void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of moe_forward_static's static per-device workspace (16 MiB): enough for
+ * moe_workspace_bytes at decode-size batches, e.g. up to 177 tokens at the Qwen3-30B-A3B expert
+ * shape (128 experts, top 8, hidden 2048, expert width 768). */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* moe_forward without a caller workspace, for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same four launches and the
+ * same results, over a workspace of MOE_STATIC_SCRATCH_BYTES that the library holds on each GPU
+ * from its load until the process ends (its device address is looked up once per device, on the
+ * first call made with that device current). The call allocates nothing, device or host.
+ * STEP_EINVAL when moe_workspace_bytes(layer) exceeds MOE_STATIC_SCRATCH_BYTES (no launch is
+ * made), and the errors of moe_forward otherwise. Every call on one GPU shares that GPU's
+ * workspace, and each call rewrites all of it that it reads, so nothing has to be cleared between
+ * calls; calls that overlap on one GPU (on different streams, or on one stream under different
+ * graphs replayed concurrently) race and must not be issued. */
+int moe_forward_static(const moe_layer* layer, void* stream);
+
 /* Message of the last error on this thread ("" when none). */
 const char* moe_last_error(void);
 
