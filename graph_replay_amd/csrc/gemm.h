@@ -16,6 +16,7 @@
 //   Both split K on request into fp32 partial outputs that the consumer sums in fixed order.
 #pragma once
 #include "common.h"
+#include "sample.h"
 
 namespace gr {
 
@@ -42,6 +43,13 @@ struct GemmArgs {
   int ldo;
   int ksplit;            // k_gemm / k_gemv_mfma: number of K ranges (gridDim.z / y)
   size_t out_split_stride;
+  // k_gemv_stream with sampling (the LM head fused with the sampler): smp holds k_sample's inputs
+  // (temperatures, the Philox key and step counter, token output, the in-place advance, the device
+  // row count; no filters, no explicit uniforms), cand [gridDim.x][M] the blocks' best keys and
+  // cand_done their arrival counter (zero between launches)
+  SampleArgs smp;
+  unsigned long long* cand;
+  unsigned* cand_done;
 };
 
 // ------------------------------------------------------------------------------------------
@@ -752,7 +760,17 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a, int epi) {
 // the 16-byte chunk c of row m sits at chunk c ^ (m & 15), so the 16 rows a lane group reads at
 // one k offset fall in distinct banks. fp32 out [M][ldo]; no bias, no K split; K a multiple of
 // 32 * CH and at most KMAX (LDS: MB * 16 * KMAX elements; two blocks per CU up to 64 KiB).
-template <class T, int MB, int NWV, int CH, int KMAX>
+//
+// SAMPLE: the sampler fused into the epilogue ("Removing overhead: fusion, graphs and async
+// scheduling", section "Fewer, larger matmuls", lists the LM head fused with sampling among the
+// fusions production engines make). A lane's tile output is four consecutive vocabulary rows of one
+// token row, the four columns of one Philox call, so each lane scores its logits exactly as
+// k_sample would (z at temperature 0, else z / T plus the Gumbel noise of the (row, column)
+// uniform), keeps the best score_key per token row, and the block stores one key per row. The last
+// block to arrive takes each row's best key, writes the token, runs advance_row and moves the step
+// counter on, as k_sample's last blocks do, so the tokens are bit-identical to k_sample's on the
+// stored logits. The logits are still stored.
+template <class T, int MB, int NWV, int CH, int KMAX, bool SAMPLE>
 __global__ __launch_bounds__(64 * NWV, MB * 16 * KMAX * 2 <= 65536 ? 2 : 1) void k_gemv_stream(GemmArgs a) {
   using S = typename T::S;
   static_assert(sizeof(S) == 2, "16-bit types");
@@ -788,6 +806,18 @@ __global__ __launch_bounds__(64 * NWV, MB * 16 * KMAX * 2 <= 65536 ? 2 : 1) void
   f32x4_t acc[MB];
 #pragma unroll
   for (int t = 0; t < MB; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fused sampler state of this lane's token rows t * 16 + col
+  const int n_samp = SAMPLE ? (a.smp.n_rows ? min(*a.smp.n_rows, a.M) : a.M) : 0;
+  const uint64_t seed = SAMPLE ? (a.smp.rng ? a.smp.rng[0] : a.smp.seed) : 0ull;
+  const uint64_t stepc = SAMPLE ? (a.smp.rng ? a.smp.rng[1] : a.smp.step) : 0ull;
+  float temp[MB];
+  unsigned long long best[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) {
+    const int m = t * 16 + col;
+    temp[t] = (SAMPLE && m < n_samp && a.smp.temperature) ? a.smp.temperature[m] : 0.f;
+    best[t] = 0ull;
+  }
   auto compute = [&](const uint4(&w)[CH], int q) {
     const int ks0 = (q % cpt) * CH;
 #pragma unroll
@@ -810,6 +840,24 @@ __global__ __launch_bounds__(64 * NWV, MB * 16 * KMAX * 2 <= 65536 ? 2 : 1) void
           for (int i = 0; i < 4; ++i)
             if (nb + i < a.N) out[static_cast<size_t>(m) * a.ldo + nb + i] = acc[t][i];
         }
+        if (SAMPLE && m < n_samp) {
+          float u[4] = {1.f, 1.f, 1.f, 1.f};
+          if (temp[t] > 0.f) {
+            uint32_t w4[4] = {static_cast<uint32_t>(nb >> 2), static_cast<uint32_t>(m), static_cast<uint32_t>(stepc),
+                              static_cast<uint32_t>(stepc >> 32)};
+            philox4x32_10(w4, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u[i] = static_cast<float>(w4[i] >> 8) * 5.9604644775390625e-08f;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (nb + i < a.N) {
+              const float sc = temp[t] > 0.f ? gumbel_score(acc[t][i] / temp[t], u[i]) : acc[t][i];
+              const unsigned long long k = score_key(sc, nb + i);
+              best[t] = k > best[t] ? k : best[t];
+            }
+          }
+        }
         acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
@@ -820,6 +868,81 @@ __global__ __launch_bounds__(64 * NWV, MB * 16 * KMAX * 2 <= 65536 ? 2 : 1) void
     if (q + 1 < nseq) {
       if (q + 2 < nseq) load(wa, q + 2);
       compute(wb, q + 1);
+    }
+  }
+  if constexpr (SAMPLE) {
+    // the block's best key per token row: the four lane groups of a wave, then the waves
+    constexpr int R = MB * 16;
+    // the reduction's LDS reuses the activation rows (every wave is past its last product after the
+    // barrier), so the block keeps the LDS footprint of the plain kernel
+    static_assert(sizeof(unsigned long long) * (NWV * R + 1) <= sizeof(S) * MB * 16 * KMAX, "LDS reuse");
+    __syncthreads();
+    unsigned long long (*sbest)[R] = reinterpret_cast<unsigned long long (*)[R]>(xs);
+    int& s_last = *reinterpret_cast<int*>(reinterpret_cast<unsigned long long*>(xs) + NWV * R);
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      unsigned long long b = best[t];
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(b), o, 64);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(b >> 32), o, 64);
+        const unsigned long long w = (static_cast<unsigned long long>(hi) << 32) | lo;
+        b = w > b ? w : b;
+      }
+      if (grp == 0) sbest[wid][t * 16 + col] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      unsigned long long b = 0ull;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) b = sbest[w][threadIdx.x] > b ? sbest[w][threadIdx.x] : b;
+      __hip_atomic_store(a.cand + static_cast<size_t>(blockIdx.x) * R + threadIdx.x, b, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = arrive_last(a.cand_done, gridDim.x);
+    __syncthreads();
+    if (!s_last) return;
+    // the last block: row m's best key over all blocks (wave w takes rows w, w + NWV, ...), every
+    // load of the wave issued before the first comparison (fixed trip counts; the grid has at most
+    // 512 blocks)
+    constexpr int RPW = (R + NWV - 1) / NWV;
+    unsigned long long kk[RPW][8];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int m = wid + NWV * r;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int blk = lane + 64 * j;
+        kk[r][j] = (m < n_samp && blk < static_cast<int>(gridDim.x))
+                       ? __hip_atomic_load(a.cand + static_cast<size_t>(blk) * R + m, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0ull;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int m = wid + NWV * r;
+      unsigned long long b = 0ull;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b = kk[r][j] > b ? kk[r][j] : b;
+      b = wave_max_u64(b);
+      if (m < n_samp && lane == 0) {
+        const int idx = b ? static_cast<int>(~static_cast<uint32_t>(b)) : -1;
+        // no candidate (every score NaN): token -1 and no advance, as in k_sample
+        const bool ok = idx >= 0 && idx < a.N;
+        a.smp.tokens_out[m] = ok ? idx : -1;
+        if (a.smp.advance && ok)
+          advance_row(idx, a.smp.input_ids + m, a.smp.positions + m, a.smp.seq_lens + m, a.smp.slots + m,
+                      a.smp.block_table + static_cast<size_t>(m) * a.smp.bt_stride, a.smp.bt_stride,
+                      a.smp.history ? a.smp.history + static_cast<size_t>(m) * a.smp.hist_ld : nullptr,
+                      a.smp.hist_ld);
+      }
+    }
+    if (threadIdx.x == 0 && a.smp.rng) {
+      uint64_t* r = const_cast<uint64_t*>(a.smp.rng);
+      r[1] = stepc + 1;
     }
   }
 }

@@ -243,18 +243,6 @@ __device__ inline float wave_max63(float v) {
 // lane 63's value in every lane (a scalar read)
 __device__ inline float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
 
-// the largest 64-bit value over the wave, in every lane
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, 64);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, 64);
-    const unsigned long long w = (static_cast<unsigned long long>(hi) << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 // Loads and stores through pointers the kernel reads from memory (the per-layer table) are
 // generic; these make them global-memory accesses. A generic (flat) load also counts against
 // the LDS counter, so every LDS access after it would wait for it.

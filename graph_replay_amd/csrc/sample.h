@@ -23,8 +23,12 @@ __device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    // each 32 x 32 -> 64-bit product as one 64-bit multiply (one v_mad_u64_u32 instead of a
+    // separate low and high multiply)
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
+    const uint32_t lo0 = static_cast<uint32_t>(p0), hi0 = static_cast<uint32_t>(p0 >> 32);
+    const uint32_t lo1 = static_cast<uint32_t>(p1), hi1 = static_cast<uint32_t>(p1 >> 32);
     const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0;
     c[1] = lo1;
@@ -33,10 +37,14 @@ __device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
   }
 }
 
-// The Gumbel-max score of a temperature-scaled logit zd = z / T (T > 0) with uniform u.
+// The Gumbel-max score of a temperature-scaled logit zd = z / T (T > 0) with uniform u. The two
+// natural logs use the hardware log2 (v_log_f32, about one ulp) scaled by ln 2: the full-precision
+// library log costs some twenty more instructions each, and the sampler spends them on every logit
+// of every sampled row. Every sampler here (k_sample, the fused LM heads) scores with this function,
+// so their tokens agree bit for bit.
 __device__ inline float gumbel_score(float zd, float u) {
   const float uu = fminf(fmaxf(u, 1e-10f), 1.0f);
-  return zd - logf(-logf(uu));
+  return zd - __logf(-__logf(uu));
 }
 
 // The uniform of (row, column) under the counter scheme above, from one Philox call.
@@ -100,6 +108,24 @@ __device__ inline uint32_t fkey(float z) {
 __device__ inline float fkey_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+// The sampler's order (score descending, then index ascending) as one unsigned 64-bit key: the
+// order-preserving key of the score above the complemented index. A NaN score gets key 0, below
+// every real candidate, as it never wins the sampler's comparisons.
+__device__ inline unsigned long long score_key(float sc, int idx) {
+  if (sc != sc) return 0ull;
+  return (static_cast<unsigned long long>(fkey(sc)) << 32) | static_cast<uint32_t>(~idx);
+}
+// the largest 64-bit value over the wave, in every lane
+__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, 64);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, 64);
+    const unsigned long long w = (static_cast<unsigned long long>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
 __device__ inline unsigned long long qmass(float z, float zmax) {
   return static_cast<unsigned long long>(static_cast<uint32_t>(__expf(z - zmax) * 2147483648.0f));
 }
@@ -144,7 +170,7 @@ __device__ inline unsigned long long block_excl_scan(unsigned long long v, unsig
   return base + inc - v;
 }
 
-__global__ __launch_bounds__(kFilterThreads) void k_sample_filter(FilterArgs a) {
+static __global__ __launch_bounds__(kFilterThreads) void k_sample_filter(FilterArgs a) {
   constexpr int NB = 2048, CAP = 2048, NT = kFilterThreads;
   __shared__ unsigned hcnt[NB];
   __shared__ unsigned long long hmass[NB];
@@ -398,7 +424,7 @@ __device__ inline void block_best(float& v, int& i, float* sv, int* si) {
 // row to finish merges the chunk winners (the order (value desc, index asc) is total, so the merge
 // order cannot change the winner), writes the token and advances the row. The last row to finish
 // moves the Philox step counter on: every block read it before it counted itself in.
-__global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
+static __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
   __shared__ int last_flag;

@@ -39,7 +39,7 @@ struct Layout {  // byte offsets into the workspace
   size_t rope_cos, rope_sin;
   size_t resid[2], h, qkv, q, attn_o, d_o, d_d, act;
   size_t attn_part, attn_cnt, samp_val, samp_idx, samp_cnt, samp_done, samp_temp, samp_rng;
-  size_t samp_topk, samp_topp, samp_filt;
+  size_t samp_topk, samp_topp, samp_filt, samp_cand;
   // persistent decode step: per-layer pointers, tagged hand-off words, control words, stamps
   size_t p_lw, p_qkv, p_part, p_attn, p_o, p_act, p_down, p_ctl, p_stamps, p_cand;
   int p_splits;                       // attention splits per KV head the partial words hold
@@ -258,6 +258,8 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.samp_topk = L.samp_temp + sizeof(float) * static_cast<size_t>(LM);
   L.samp_topp = L.samp_topk + sizeof(int) * static_cast<size_t>(LM);
   L.samp_filt = take(sizeof(uint2) * static_cast<size_t>(std::max(LM, MB)));
+  // the LM head's fused sampler: one key per (block, row) of the streaming GEMV (<= 512 blocks, <= 48 rows)
+  L.samp_cand = take(sizeof(unsigned long long) * 512 * 48);
   L.samp_rng = take(16);
   if (c.persistent_decode) {
     L.p_splits = (c.max_position + gr::kPSplit - 1) / gr::kPSplit;
@@ -368,6 +370,9 @@ struct Lin {
   int ksplit_ok = 0;          // output may be split into fp32 partials (consumer sums them)
   int* ksplit_used = nullptr; // out: partial count
   size_t split_stride = 0;
+  // LM head: the sampler to fuse into the streaming GEMV when that kernel runs (sampled is then set)
+  const SampleArgs* smp = nullptr;
+  bool* sampled = nullptr;
 };
 
 template <class T, int MT, int ROWS, int U>
@@ -451,9 +456,20 @@ int run_linear(step_ctx* ctx, const Lin& l) {
       const int ntiles = (l.N + 15) / 16;
       const int per_cu = (l.M <= 32 && l.K <= 1024) ? 2 : 1;
       const dim3 grid(std::min(per_cu * 256, (ntiles + SW - 1) / SW));
-      if (per_cu == 1) launch((gr::k_gemv_stream<T, 3, SW, SC, 1536>), grid, dim3(64 * SW), 0, s, a);
-      else if (l.M <= 16) launch((gr::k_gemv_stream<T, 1, SW, SC, 1024>), grid, dim3(64 * SW), 0, s, a);
-      else launch((gr::k_gemv_stream<T, 2, SW, SC, 1024>), grid, dim3(64 * SW), 0, s, a);
+      if (l.smp) {
+        // the sampler in the epilogue (no separate sampling launch follows)
+        a.smp = *l.smp;
+        a.cand = reinterpret_cast<unsigned long long*>(ctx->ws + ctx->lay.samp_cand);
+        a.cand_done = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_done) + 1;
+        if (l.sampled) *l.sampled = true;
+        if (per_cu == 1) launch((gr::k_gemv_stream<T, 3, SW, SC, 1536, true>), grid, dim3(64 * SW), 0, s, a);
+        else if (l.M <= 16) launch((gr::k_gemv_stream<T, 1, SW, SC, 1024, true>), grid, dim3(64 * SW), 0, s, a);
+        else launch((gr::k_gemv_stream<T, 2, SW, SC, 1024, true>), grid, dim3(64 * SW), 0, s, a);
+      } else {
+        if (per_cu == 1) launch((gr::k_gemv_stream<T, 3, SW, SC, 1536, false>), grid, dim3(64 * SW), 0, s, a);
+        else if (l.M <= 16) launch((gr::k_gemv_stream<T, 1, SW, SC, 1024, false>), grid, dim3(64 * SW), 0, s, a);
+        else launch((gr::k_gemv_stream<T, 2, SW, SC, 1024, false>), grid, dim3(64 * SW), 0, s, a);
+      }
       e = hipGetLastError();
     } else if (l.M <= 32) {
       // two 16-row weight tiles per wave share each activation fragment where the output is wide
@@ -617,6 +633,26 @@ int run_qkv_post(step_ctx* ctx, int layer, int rows, int n_parts, size_t part_st
   return STEP_OK;
 }
 
+// the sampler's arguments, shared by k_sample and the LM head's fused sampler
+SampleArgs sample_args(step_ctx* ctx, const float* logits, int ld, int vocab, const float* temp, const float* uniforms,
+                       const uint64_t* rng, uint64_t seed, uint64_t stepc, int* tokens_out, int advance, int* ids,
+                       int* pos, int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld,
+                       const int* n_rows, const int* halt) {
+  SampleArgs a{};
+  a.logits = logits; a.ld = ld; a.vocab = vocab;
+  a.temperature = temp; a.uniforms = uniforms; a.rng = rng; a.seed = seed; a.step = stepc;
+  a.part_val = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_val);
+  a.part_idx = reinterpret_cast<int*>(ctx->ws + ctx->lay.samp_idx);
+  a.row_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_cnt);
+  a.done_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_done);
+  a.tokens_out = tokens_out;
+  a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
+  a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
+  a.n_rows = n_rows;
+  a.halt = halt;
+  return a;
+}
+
 int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, const float* temp, const float* uniforms,
                const uint64_t* rng, uint64_t seed, uint64_t stepc, int* tokens_out, int advance, int* ids, int* pos,
                int* lens, int* slots, const int* bt, int bt_stride, int* history, int hist_ld,
@@ -634,24 +670,14 @@ int run_sample(step_ctx* ctx, const float* logits, int rows, int ld, int vocab, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(ctx, STEP_EHIP, "sample filter launch failed: %s", hipGetErrorString(e));
   }
-  SampleArgs a{};
-  a.logits = logits; a.ld = ld; a.vocab = vocab;
+  SampleArgs a = sample_args(ctx, logits, ld, vocab, temp, uniforms, rng, seed, stepc, tokens_out, advance, ids, pos,
+                             lens, slots, bt, bt_stride, history, hist_ld, n_rows, halt);
   // one or two 1,024-column passes per thread while the grid stays within 4,096 blocks: a thread's
   // passes are serial memory round trips, so short chunks finish sooner
   int chunk = 1024;
   while (chunk < 16384 && static_cast<long>(rows) * ((vocab + chunk - 1) / chunk) > 4096) chunk *= 2;
   a.chunk = chunk;
-  a.temperature = temp; a.uniforms = uniforms; a.rng = rng; a.seed = seed; a.step = stepc;
-  a.part_val = reinterpret_cast<float*>(ctx->ws + ctx->lay.samp_val);
-  a.part_idx = reinterpret_cast<int*>(ctx->ws + ctx->lay.samp_idx);
-  a.row_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_cnt);
-  a.done_cnt = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.samp_done);
-  a.tokens_out = tokens_out;
-  a.advance = advance; a.input_ids = ids; a.positions = pos; a.seq_lens = lens; a.slots = slots;
-  a.block_table = bt; a.bt_stride = bt_stride; a.history = history; a.hist_ld = hist_ld;
-  a.n_rows = n_rows;
   a.filt = filt;
-  a.halt = halt;
   const int nch = (vocab + chunk - 1) / chunk;
   pre_launch(ctx, KK_SAMPLE);
   launch(k_sample, dim3(rows, nch), dim3(256), 0, ctx->stream, a);
@@ -718,7 +744,7 @@ void set_prefetch(step_ctx* ctx, int l, int M) {
 
 template <class T, class AttnFn>
 int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* slot, int n_logits, const int* logit_rows,
-               bool fused_rope, AttnFn attn) {
+               bool fused_rope, AttnFn attn, const SampleArgs* smp = nullptr, bool* sampled = nullptr) {
   const step_config& c = ctx->cfg;
   const Layout& L = ctx->lay;
   const int H = c.hidden, d = c.head_dim, nq = c.q_heads, nkv = c.kv_heads, I = c.intermediate;
@@ -798,6 +824,8 @@ int run_layers(step_ctx* ctx, int M, const int* tok, const int* pos, const int* 
                     c_final_norm_of(ctx), h));
     lh.M = rows; lh.x = h;
   }
+  lh.smp = smp;
+  lh.sampled = sampled;
   TRY(run_linear<T>(ctx, lh));
   return STEP_OK;
 }
@@ -905,7 +933,14 @@ int run_decode(step_ctx* ctx, int B) {
   auto attn = [&](int l, int n_qkv) {
     return run_attn_rows<T>(ctx, l, B, nullptr, n_qkv, m.pos, m.slot, m.bt, W, nullptr, m.len, c.max_position, attn_o);
   };
-  TRY(run_layers<T>(ctx, B, m.ids, m.pos, m.slot, 0, nullptr, true, attn));
+  // without filters the sampler may run in the LM head's epilogue (streaming GEMV rows)
+  const SampleArgs smp = sample_args(ctx, ctx->logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1,
+                                     m.ids, m.pos, m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr,
+                                     nullptr);
+  bool sampled = false;
+  TRY(run_layers<T>(ctx, B, m.ids, m.pos, m.slot, 0, nullptr, true, attn, c.sampling_filters ? nullptr : &smp,
+                    &sampled));
+  if (sampled) return STEP_OK;
   return run_sample(ctx, ctx->logits, B, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 1, m.ids, m.pos,
                     m.len, m.slot, m.bt, W, ctx->history, c.max_position, nullptr,
                     c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
@@ -1018,7 +1053,13 @@ int run_mixed(step_ctx* ctx, const MixedPlan& p) {
     }
     return STEP_OK;
   };
-  TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, false, attn));
+  const SampleArgs smp = sample_args(ctx, ctx->logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0,
+                                     p.fixed ? m.n_logits : nullptr, nullptr);
+  bool sampled = false;
+  TRY(run_layers<T>(ctx, p.T, m.tok, m.pos, m.slot, p.n_logits, m.lidx, false, attn,
+                    c.sampling_filters ? nullptr : &smp, &sampled));
+  if (sampled) return STEP_OK;
   return run_sample(ctx, ctx->logits, p.n_logits, c.vocab, c.vocab, m.temp, nullptr, m.rng, 0, 0, ctx->tokens, 0,
                     nullptr, nullptr, nullptr, nullptr, nullptr, W, nullptr, 0, p.fixed ? m.n_logits : nullptr,
                     c.sampling_filters ? m.topk : nullptr, c.sampling_filters ? m.topp : nullptr);
