@@ -82,6 +82,27 @@ def timed_replays(dec, steps: int):
     return e0.elapsed_time(e1)
 
 
+WARM_RUNS, TIMED_RUNS = 2, 5
+
+
+def timed_runs(dec, steps: int, refeed) -> dict:
+    """The measurement protocol of the pages' benchmark (median of 5 timed runs after 2 warm-up
+    runs). Every run starts from the same state: refeed() sends the workload's batch again and runs
+    the warm-up steps (untimed), then exactly `steps` graph replays continue on the device, bracketed
+    by synchronisations and HIP events on the decoder's stream. 2 runs untimed, 5 timed; the median
+    run is the result."""
+    runs = []
+    for r in range(WARM_RUNS + TIMED_RUNS):
+        refeed()
+        ms = timed_replays(dec, steps)
+        if r >= WARM_RUNS:
+            runs.append(ms)
+    med = float(np.median(runs))
+    return {"median_ms": med, "runs_ms_per_step": [round(r / steps, 4) for r in runs],
+            "protocol": f"{WARM_RUNS} warm-up runs, then the median of {TIMED_RUNS} timed runs of {steps} replays, "
+                        "each from the same state"}
+
+
 def measured_traffic(workload: str, kind: str):
     """HBM bytes per launch of `kind` from the committed rocprofv3 counter runs (profiles/), or None
     when there is no such run or the kernels changed since it was taken."""
@@ -153,13 +174,17 @@ def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefe
     torch.cuda.synchronize()
     first = int(dec.tokens[0].item())
     p = ctx_len
-    dec.decode([first], [p], [p + 1], [int(bt[0][p // 16] * 16 + p % 16)], bt)
-    for _ in range(warmup - 1):
-        dec.decode_continue()
-    torch.cuda.synchronize()
-    start_len = ctx_len + 1 + warmup                      # seq_len of the first timed step
-    log("timing", steps, "bs1 steps")
-    ms = timed_replays(dec, steps)
+
+    def refeed():
+        dec.decode([first], [p], [p + 1], [int(bt[0][p // 16] * 16 + p % 16)], bt)
+        for _ in range(warmup - 1):
+            dec.decode_continue()
+        torch.cuda.synchronize()
+
+    start_len = ctx_len + 1 + warmup                      # seq_len of the first timed replay
+    log("timing", steps, "bs1 steps x", TIMED_RUNS, "runs")
+    tr = timed_runs(dec, steps, refeed)
+    ms = tr["median_ms"]
     seq_sum_mean = start_len + (steps - 1) / 2.0
     nbytes = step_bytes(shape, seq_sum_mean)
     ms_step = ms / steps
@@ -184,7 +209,7 @@ def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefe
     out = {
         "tok_s": steps / (ms * 1e-3), "ms_per_step": ms_step, "bytes_per_step": int(nbytes),
         "step_hbm_GBps": nbytes / (ms_step * 1e-3) / 1e9, "kernels_per_step": dec.kernels_per_decode(1),
-        "roofline": roof,
+        "roofline": roof, "timing": {k: v for k, v in tr.items() if k != "median_ms"},
     }
     out["step_hbm_frac"] = out["step_hbm_GBps"] / PEAK_HBM_GBS
     dec.close()
@@ -193,10 +218,12 @@ def run_bs1(shape, W, steps: int, warmup: int, ctx_len: int = 1024, weight_prefe
     return out
 
 
-def run_bs32(shape, W, steps: int, warmup: int):
+def run_bs32(shape, W, steps: int, warmup: int, wl=None):
+    """A many-row decode workload (batch 32 by default; the batch-256 workload with wl) over seeded
+    N(0, 1) KV histories resident in HBM, Gumbel-max at the workload's temperature, shuffled tables."""
     import graph_replay_amd as g
     torch = __import__("torch")
-    wl = synth.workload_q3_bs32()
+    wl = wl or synth.workload_q3_bs32()
     ctx = wl.contexts
     B = len(ctx)
     need = [c + 1 + warmup + steps + 2 for c in ctx]
@@ -204,9 +231,9 @@ def run_bs32(shape, W, steps: int, warmup: int):
     tables = synth.block_tables(need, nb, 1003, shuffled=True)
     width = max(len(t) for t in tables)
     dec = g.Decoder(shape, W, num_blocks=nb, max_blocks_per_seq=width, max_position=max(need) + 16, max_batch=B,
-                    buckets=[1, 2, 4, 8, 16, 32])
+                    buckets=wl.buckets)
     gen = torch.Generator(device=dec.device)
-    gen.manual_seed(1003)
+    gen.manual_seed(wl.input_seed)
     for l in range(shape.layers):                       # seeded N(0, 1) KV history, resident in HBM
         dec.k_pool[l].normal_(generator=gen)
         dec.v_pool[l].normal_(generator=gen)
@@ -215,21 +242,28 @@ def run_bs32(shape, W, steps: int, warmup: int):
         bt[j, :len(t)] = t
     pos = np.asarray(ctx, np.int32)
     slots = np.array([bt[j][pos[j] // 16] * 16 + pos[j] % 16 for j in range(B)], np.int32)
-    toks = synth.tokens(B, shape.vocab, 1003)
-    dec.decode(toks, pos, pos + 1, slots, bt, temperature=np.ones(B, np.float32), seed=1003)
-    for _ in range(warmup - 1):
-        dec.decode_continue()
-    torch.cuda.synchronize()
-    log("timing", steps, "bs32 steps")
-    ms = timed_replays(dec, steps)
+    toks = synth.tokens(B, shape.vocab, wl.input_seed)
+
+    def refeed():
+        dec.decode(toks, pos, pos + 1, slots, bt, temperature=np.full(B, wl.temperature, np.float32),
+                   seed=wl.input_seed)
+        for _ in range(warmup - 1):
+            dec.decode_continue()
+        torch.cuda.synchronize()
+
+    log("timing", steps, f"bs{B} steps x", TIMED_RUNS, "runs")
+    tr = timed_runs(dec, steps, refeed)
+    ms = tr["median_ms"]
     start_sum = sum(c + 1 + warmup for c in ctx)
     seq_sum_mean = start_sum + B * (steps - 1) / 2.0
     nbytes = step_bytes(shape, seq_sum_mean)
     ms_step = ms / steps
     roof = roofline_from_profile(shape, dec, B, start_sum + B * steps)
+    roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     out = {"workload": wl.name, "batch": B, "tok_s": B * steps / (ms * 1e-3), "ms_per_step": ms_step,
            "bytes_per_step": int(nbytes), "step_hbm_GBps": nbytes / (ms_step * 1e-3) / 1e9,
-           "kernels_per_step": dec.kernels_per_decode(32), "roofline": roof}
+           "kernels_per_step": dec.kernels_per_decode(B), "roofline": roof,
+           "timing": {k: v for k, v in tr.items() if k != "median_ms"}}
     out["step_hbm_frac"] = out["step_hbm_GBps"] / PEAK_HBM_GBS
     dec.close()
     return out
@@ -420,8 +454,11 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-bs32", action="store_true")
-    ap.add_argument("--workload", choices=["both", "bs1", "bs32", "mixed", "moe"], default="both",
-                    help="bs1: the primary line only; bs32 / mixed / moe: that workload only (for profiling)")
+    ap.add_argument("--workload", choices=["both", "bs1", "bs32", "bs256", "mixed", "moe"], default="both",
+                    help="bs1: the primary line only; bs32 / bs256 / mixed / moe: that workload only (for profiling)")
+    ap.add_argument("--no-bs256", action="store_true")
+    ap.add_argument("--bs256-steps", type=int, default=32,
+                    help="replays per timed run of the batch-256 workload (each run holds 256 rows x steps keys more)")
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -460,6 +497,12 @@ def main():
                           "unit": "tokens/s", "ms_per_step": round(r32["ms_per_step"], 4),
                           "kernels_per_step": r32["kernels_per_step"], "roofline": r32["roofline"]}), flush=True)
         return
+    if args.workload == "bs256":
+        r = run_bs32(shape, W, min(args.steps, args.bs256_steps), warmup, synth.workload_q3_bs256())
+        print(json.dumps({"metric": METRIC, "workload": r["workload"], "value": round(r["tok_s"], 1),
+                          "unit": "tokens/s", "ms_per_step": round(r["ms_per_step"], 4),
+                          "kernels_per_step": r["kernels_per_step"], "roofline": r["roofline"]}), flush=True)
+        return
     if args.workload == "mixed":
         print(json.dumps({"metric": METRIC, **run_mixed()}), flush=True)
         return
@@ -469,6 +512,8 @@ def main():
     r1 = run_bs1(shape, W, args.steps, warmup, weight_prefetch=not args.no_weight_prefetch,
                  persistent=not args.no_persistent)
     r32 = None if (args.no_bs32 or args.workload == "bs1") else run_bs32(shape, W, args.steps, warmup)
+    r256 = None if (args.no_bs256 or args.workload == "bs1") else run_bs32(
+        shape, W, min(args.steps, args.bs256_steps), warmup, synth.workload_q3_bs256())
     rmix = None if (args.no_mixed or args.workload == "bs1") else run_mixed()
     rmoe = None if (args.no_moe or args.workload == "bs1") else run_moe()
     cpu = None if args.no_cpu else cpu_baseline(shape, W)
@@ -485,14 +530,16 @@ def main():
         "step_hbm": {"bytes_per_step": r1["bytes_per_step"], "achieved": round(r1["step_hbm_GBps"], 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r1["step_hbm_frac"], 4)},
         "roofline": r1["roofline"],
+        "timing": r1["timing"],
         "cpu_baseline": cpu,
     }
-    if r32 is not None:
-        line["bs32"] = {"workload": r32["workload"], "value": round(r32["tok_s"], 1), "unit": "tokens/s",
-                        "ms_per_step": round(r32["ms_per_step"], 4), "kernels_per_step": r32["kernels_per_step"],
-                        "step_hbm": {"bytes_per_step": r32["bytes_per_step"], "achieved": round(r32["step_hbm_GBps"], 1),
-                                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r32["step_hbm_frac"], 4)},
-                        "roofline": r32["roofline"]}
+    for key, r in (("bs32", r32), ("bs256", r256)):
+        if r is not None:
+            line[key] = {"workload": r["workload"], "value": round(r["tok_s"], 1), "unit": "tokens/s",
+                         "ms_per_step": round(r["ms_per_step"], 4), "kernels_per_step": r["kernels_per_step"],
+                         "step_hbm": {"bytes_per_step": r["bytes_per_step"], "achieved": round(r["step_hbm_GBps"], 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r["step_hbm_frac"], 4)},
+                         "roofline": r["roofline"], "timing": r["timing"]}
     if rmix is not None:
         line["mixed"] = rmix
     if rmoe is not None:

@@ -3,7 +3,8 @@
     python -m graph_replay_amd.profiling stats <run>_kernel_stats.csv "<command>" > profiles/<name>.md
     python -m graph_replay_amd.profiling kinds <run>_kernel_trace.csv >> profiles/<name>.md
     python -m graph_replay_amd.profiling traffic <copy FETCH dir> <copy WRITE dir> <FETCH dir> <WRITE dir> \\
-        <workload> "<command>" > profiles/hbm_traffic.json
+        <workload> "<command>" > profiles/hbm_traffic_<workload>.json
+    python -m graph_replay_amd.profiling counters <pmc dir> <workload> "<command>" > profiles/<name>.md
 
 `traffic` turns two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs into HBM bytes per launch:
 each counter (KiB per dispatch) is scaled by what it reads for a plain 1 GiB device copy
@@ -93,13 +94,35 @@ def _kind_bs1(name: str, grid: int) -> str:
     return ""
 
 
+# The kind of a dispatch of any other workload: the step's kernels by name, the projections by
+# kernel and grid size (each projection of a step has its own grid).
+_NAMED = (("k_persist_decode", "decode_step_persistent"), ("k_attn_prefill", "attn_prefill"),
+          ("k_attn_rows", "attn_decode"), ("k_sample_filter", "sample_filter"), ("k_sample", "sample"),
+          ("k_add_rmsnorm", "add_rmsnorm"), ("k_qkv_post", "qknorm_rope_kvwrite"), ("k_gemv_stream", "lm_head"),
+          ("k_moe_align", "moe_align"), ("k_moe_sum", "moe_sum"))
+
+
+def _kind(name: str, grid: int, workload: str) -> str:
+    if "bs1" in workload:
+        return _kind_bs1(name, grid)
+    for key, kind in _NAMED:
+        if key in name:
+            return kind
+    if "k_moe_gemm" in name:
+        return "moe_gate_up" if ", true," in name else "moe_down"
+    for key in ("k_gemv_mfma", "k_gemm_ring", "k_gemm", "k_gemv"):
+        if key + "<" in name:
+            return f"{key}[grid {grid}]"
+    return ""
+
+
 def traffic(cf: str, cw: str, f: str, w: str, workload: str, cmd: str) -> None:
     ff, wf = _copy_factor(cf), _copy_factor(cw)
     kinds = {}
     for d, fac, key in ((f, ff, "fetch_bytes"), (w, wf, "write_bytes")):
         acc = {}
         for r in _counter_rows(d):
-            k = _kind_bs1(r["Kernel_Name"], int(r["Grid_Size"]))
+            k = _kind(r["Kernel_Name"], int(r["Grid_Size"]), workload)
             if k:
                 acc.setdefault(k, []).append(float(r["Counter_Value"]) * 1024 * fac)
         for k, v in acc.items():
@@ -109,8 +132,28 @@ def traffic(cf: str, cw: str, f: str, w: str, workload: str, cmd: str) -> None:
                       "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "kinds": kinds}, indent=1))
 
 
+def counters(d: str, workload: str, cmd: str) -> None:
+    """Markdown table of the mean of every counter per dispatch kind of one rocprofv3 --pmc run."""
+    acc = {}
+    for r in _counter_rows(d):
+        k = _kind(r["Kernel_Name"], int(r["Grid_Size"]), workload) or r["Kernel_Name"][:60]
+        acc.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    names = sorted({c for _, c in acc})
+    print(f"# rocprofv3 counters per dispatch, {workload}\n")
+    print("Command (run from /tmp with TMPDIR=/tmp on one MI355X):\n")
+    print("```\n" + cmd + "\n```\n")
+    print("| kind | dispatches | " + " | ".join(names) + " |")
+    print("|---|---:|" + "---:|" * len(names))
+    for k in sorted({k for k, _ in acc}):
+        vals = [acc.get((k, c), []) for c in names]
+        n = max(len(v) for v in vals)
+        print(f"| {k} | {n} | " + " | ".join(f"{sum(v) / len(v):.4g}" if v else "" for v in vals) + " |")
+
+
 if __name__ == "__main__":
-    if sys.argv[1] == "stats":
+    if sys.argv[1] == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3])
     elif sys.argv[1] == "kinds":
         kinds(sys.argv[2])
