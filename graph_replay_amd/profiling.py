@@ -119,15 +119,25 @@ def _kind(name: str, grid: int, workload: str) -> str:
 def traffic(cf: str, cw: str, f: str, w: str, workload: str, cmd: str) -> None:
     ff, wf = _copy_factor(cf), _copy_factor(cw)
     kinds = {}
+    # per kind, the launch shape with the most dispatches (the timed bucket's; the graph captures of
+    # the other buckets at init launch the same kinds on other grids)
     for d, fac, key in ((f, ff, "fetch_bytes"), (w, wf, "write_bytes")):
         acc = {}
         for r in _counter_rows(d):
             k = _kind(r["Kernel_Name"], int(r["Grid_Size"]), workload)
             if k:
-                acc.setdefault(k, []).append(float(r["Counter_Value"]) * 1024 * fac)
-        for k, v in acc.items():
+                acc.setdefault(k, {}).setdefault(int(r["Grid_Size"]), []).append(
+                    float(r["Counter_Value"]) * 1024 * fac)
+        for k, grids in acc.items():
+            grid, v = max(grids.items(), key=lambda gv: (len(gv[1]), gv[0]))
             kinds.setdefault(k, {})[key] = round(sum(v) / len(v))
             kinds[k]["dispatches"] = len(v)
+            kinds[k]["grid"] = grid
+            if len(grids) > 1:
+                per = kinds[k].setdefault("by_grid", {})
+                for gsz, vv in sorted(grids.items()):
+                    per.setdefault(str(gsz), {})[key] = round(sum(vv) / len(vv))
+                    per[str(gsz)]["dispatches"] = len(vv)
     print(json.dumps({"source_hash": source_hash(), "workload": workload, "command": cmd,
                       "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "kinds": kinds}, indent=1))
 
