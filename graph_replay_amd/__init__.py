@@ -19,7 +19,7 @@ from ._lib import (STEP_BF16, STEP_F16, STEP_F32, MoeLayer, StepBatch, StepBuffe
                    StepWeights)
 
 __all__ = ["Decoder", "StepError", "step_workspace_bytes", "step_init", "step_decode", "step_mixed", "step_sample",
-           "step_destroy", "step_set_device_status", "step_attention_splits", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "moe_forward_static",
+           "step_destroy", "step_set_device_status", "step_attention_slots", "load", "moe_align_rows", "moe_align", "moe_workspace_bytes", "moe_forward", "moe_forward_static",
            "MoeLayer"]
 
 load = _lib.load
@@ -107,11 +107,11 @@ def step_set_device_status(ctx, site: int) -> None:
     _raise(_lib.load().step_set_device_status(ctx, site), ctx)
 
 
-def step_attention_splits(cfg: StepConfig, rows: int, max_len: int):
-    """(splits per row, partial slots of the workspace) of the decode attention grid; host only."""
-    slots = C.c_int64(-1)
-    n = int(_lib.load().step_attention_splits(C.byref(cfg), rows, max_len, C.byref(slots)))
-    return n, int(slots.value)
+def step_attention_slots(cfg: StepConfig, rows: int, max_len: int):
+    """(partial slots one attention launch uses, partial slots the workspace holds); host only."""
+    cap = C.c_int64(-1)
+    n = int(_lib.load().step_attention_slots(C.byref(cfg), rows, max_len, C.byref(cap)))
+    return n, int(cap.value)
 
 
 def step_destroy(ctx) -> None:
@@ -231,7 +231,7 @@ class Decoder:
                  max_reqs: int = 0, max_logit_rows: int = 0, use_graphs: bool = True, history: bool = False,
                  mixed_buckets: Optional[Sequence[int]] = None, sampling_filters: bool = False,
                  weight_prefetch: bool = True, persistent_decode: bool = False,
-                 device: str = "cuda:0"):
+                 balanced_attention_rows: int = 0, device: str = "cuda:0"):
         import torch
         lib = _lib.load()
         self.torch = torch
@@ -315,6 +315,7 @@ class Decoder:
         cfg.sampling_filters = int(sampling_filters)
         cfg.weight_prefetch = int(weight_prefetch)
         cfg.persistent_decode = int(persistent_decode)
+        cfg.balanced_attention_rows = int(balanced_attention_rows)
         self.cfg = cfg
         self.buckets = buckets
         nbytes = step_workspace_bytes(cfg)

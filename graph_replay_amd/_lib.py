@@ -25,7 +25,8 @@ class StepConfig(C.Structure):
         ("num_mixed_buckets", C.c_int32), ("mixed_buckets", C.c_int32 * MAX_BUCKETS),
         ("sampling_filters", C.c_int32),
         ("weight_prefetch", C.c_int32),
-        ("persistent_decode", C.c_int32)]
+        ("persistent_decode", C.c_int32),
+        ("balanced_attention_rows", C.c_int32)]
 
 
 class StepWeights(C.Structure):
@@ -76,7 +77,7 @@ EXPORTS = {
     "step_device_status": (C.c_int, [P]),
     "step_phase_stamps": (C.c_int, [P, C.c_int32, C.POINTER(C.c_double)]),
     "step_set_device_status": (C.c_int, [P, C.c_int32]),
-    "step_attention_splits": (C.c_int32, [C.POINTER(StepConfig), C.c_int32, C.c_int32, C.POINTER(C.c_int64)]),
+    "step_attention_slots": (C.c_int32, [C.POINTER(StepConfig), C.c_int32, C.c_int32, C.POINTER(C.c_int64)]),
     "step_destroy": (None, [P]),
     "moe_align_rows": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32]),
     "moe_align": (C.c_int, [I32P, C.c_int32, C.c_int32, C.c_int32, I32P, I32P, I32P, P]),

@@ -812,4 +812,401 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
   attn_finish<T, D, G>(a, row, prow, g, sp, nsplit, wm, wl, wo);
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// Balanced decode attention for many rows. The split grid above gives each (row, KV head, split) a
+// block, so a launch lasts as long as its longest row: with rows of 16 to 4,352 keys most CUs sit
+// idle for the last part of it, and many short rows leave many blocks with little to read. Here
+// the launch's keys are cut into equal shares instead: the 16-key tiles of every (row, KV head)
+// pair, taken in (row, KV head, tile) order, split into one contiguous share per wave, whatever
+// the rows' lengths (the split-KV reading of "One forward per step", section "Bottleneck, and what
+// follows": the split exists to fill the GPU, so it follows the keys, not the rows). A wave runs
+// alone over its share: for each (row, KV head) piece it holds, the queries (and, in the piece
+// holding key L-1 of a fused decode row, the new K and V), the tiles of the piece in order with
+// KB tiles per online-softmax step, then the output (a whole pair) or the piece's (max, sum,
+// unnormalised output) partial, of which the last-arriving wave merges the pair's pieces in piece
+// order. Every block derives the same shares from the rows' lengths, so the grid is fixed and a
+// captured launch replays at any lengths. It serves decode steps (one query row per request, the
+// row's QK-norm + RoPE + KV write fused in as above). Split points follow the whole launch's lengths, so a
+// row's output can change in its last bits with the other rows' lengths; rows without keys (the
+// padding of a bucket) add no tiles and change nothing.
+constexpr int kFlatBlocks = 256;                  // blocks per launch (one per CU of an MI355X)
+constexpr int kFlatWaves = 4 * kFlatBlocks;       // shares per launch at most
+constexpr int kFlatMaxRows = 1024;                // grid rows the block-wide prefix sums hold
+constexpr int kFlatMaxPieces = 64;                // waves one (row, KV head) pair may span (one lane each in the merge)
+constexpr int kFlatMinTiles = 2;                  // smallest share, in 16-key tiles
+
+// Partial slots of G query heads a flat launch over `rows` grid rows may use. Shares and pairs are
+// both laid out in flat order, so the (wave, pair) intersections form a monotone path and wave +
+// pair index names each one: at most kFlatWaves + rows * nkv slots.
+__host__ __device__ inline long flat_slots(int rows, int nkv) {
+  return static_cast<long>(kFlatWaves) + static_cast<long>(rows) * nkv;
+}
+
+template <class T, int D, int G, int KB>
+__global__ __launch_bounds__(256, 2) void k_attn_flat(AttnRowsArgs a, int R) {
+  using S = typename T::S;
+  static_assert(sizeof(S) == 2 && G <= 8 && D % 32 == 0 && D <= 128, "16-bit types, at most 8 heads per KV head");
+  constexpr int KS = D / 32;   // k-steps of the score product
+  constexpr int DT = D / 16;   // 16-dim tiles of the value product
+  constexpr int half = D / 2;
+  constexpr int RPT = kFlatMaxRows / 256;
+  __shared__ int pre[kFlatMaxRows + 1];   // first tile (per KV head) of each grid row
+  __shared__ int red[2][4];
+  __shared__ __align__(16) float qsw[4][G][D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int nkv = a.nkv;
+
+  // tiles of each grid row (0 for an idle row or one without keys), their prefix sums, the most
+  int n[RPT], loc = 0, mx = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int p = tid * RPT + i;
+    const int L = p < R ? a.seq_lens[p] : 0;
+    n[i] = L > 0 ? (L + kBlk - 1) / kBlk : 0;
+    loc += n[i];
+    mx = max(mx, n[i]);
+  }
+  int inc = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+  if (lane == 63) red[0][wid] = inc;
+  if (lane == 0) red[1][wid] = mx;
+  __syncthreads();
+  int excl = inc - loc;
+  for (int w = 0; w < wid; ++w) excl += red[0][w];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    pre[tid * RPT + i] = excl;
+    excl += n[i];
+  }
+  if (tid == 255) pre[kFlatMaxRows] = excl;
+  const int maxn = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+  __syncthreads();
+  // no block barrier from here on: the waves run independently
+  const int gw = blockIdx.x * 4 + wid, NW = gridDim.x * 4;
+  // rows without keys get a zero output
+  for (int p = gw; p < R; p += NW) {
+    if (pre[p + 1] != pre[p]) continue;
+    S* out = static_cast<S*>(a.out) + static_cast<size_t>(p) * a.nq * D;
+    for (int i = lane; i < a.nq * D; i += 64) out[i] = T::from_f(0.f);
+  }
+  const long total = static_cast<long>(nkv) * pre[kFlatMaxRows];
+  if (total == 0) return;
+  // Active waves: shares of at least kFlatMinTiles tiles, and no pair spread over more than
+  // kFlatMaxPieces of them (a share of at least maxn / (kFlatMaxPieces - 2) tiles: a pair of n <=
+  // maxn tiles then meets at most n / share + 2 shares).
+  long nwa = NW;
+  nwa = min(nwa, max(1L, total / kFlatMinTiles));
+  nwa = min(nwa, max(1L, static_cast<long>(kFlatMaxPieces - 2) * total / (maxn + kFlatMaxPieces - 2)));
+  if (gw >= nwa) return;
+  auto wave_of = [&](long x) -> long { return ((x + 1) * nwa - 1) / total; };   // share holding flat tile x
+  long f = static_cast<long>(gw) * total / nwa;
+  const long f1 = static_cast<long>(gw + 1) * total / nwa;
+  const int ld = (a.nq + 2 * nkv) * D;
+  const bool act = lane < half;
+  while (f < f1) {
+    // the pair holding flat tile f: the last grid row whose first tile is at or before f (a row
+    // with tiles, as f < total), then the KV head and the tile within the row's KV-head range
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (static_cast<long>(nkv) * pre[mid] <= f) lo = mid;
+      else hi = mid - 1;
+    }
+    const int row = __builtin_amdgcn_readfirstlane(lo);
+    const int nr = __builtin_amdgcn_readfirstlane(pre[row + 1] - pre[row]);
+    const long rbase = static_cast<long>(nkv) * pre[row];
+    const int g = __builtin_amdgcn_readfirstlane(static_cast<int>((f - rbase) / nr));
+    const int ta = __builtin_amdgcn_readfirstlane(static_cast<int>((f - rbase) % nr));
+    const long seg0 = rbase + static_cast<long>(g) * nr;
+    const int tb = static_cast<int>(min(static_cast<long>(nr), ta + (f1 - f)));
+    f += tb - ta;
+    const long fw = wave_of(seg0);
+    const int np = static_cast<int>(wave_of(seg0 + nr - 1) - fw + 1);
+    const int piece = static_cast<int>(gw - fw);
+    const long slot0 = fw + static_cast<long>(row) * nkv + g;   // slot of piece 0 (see flat_slots)
+    const int L = a.seq_lens[row];
+    const int* bt = a.block_table + static_cast<size_t>(row) * a.bt_stride;
+    const int nt = tb - ta;                       // tiles of the piece
+    const int k1 = min(L, tb * kBlk);             // its keys: [ta * 16, k1)
+    const bool writes_new = tb == nr;             // holds key L - 1: writes the row's new K and V
+    // table entries of the piece's first 64 tiles, one per lane (later ones are read as needed)
+    const int bt_pre = (lane < nt && ta + lane < a.bt_stride) ? bt[ta + lane] : -1;
+    auto tile_of = [&](int i) -> int {            // i wave-uniform; past the piece: the scratch block
+      int pb0 = -1;
+      if (i < nt) {
+        if (i < 64) pb0 = __builtin_amdgcn_readlane(bt_pre, i);
+        else pb0 = (ta + i < a.bt_stride) ? bt[ta + i] : -1;
+      }
+      return pb0 >= 0 ? pb0 : a.num_blocks - 1;
+    };
+    uint4 kf[KB][KS];   // K fragment: key col, dims ks*32 + 8*grp .. + 8
+    uint2 vf[KB][DT];   // V^T fragment: dim t*16 + col, keys 4*grp .. + 4
+    auto load_k = [&](int kb, int pb) {
+      const S* kp = static_cast<const S*>(a.k_pool) + pool_k_at(pb, nkv, g, col, D) + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *reinterpret_cast<const uint4*>(kp + ks * 32);
+    };
+    auto load_v = [&](int kb, int pb) {
+      const S* vp = static_cast<const S*>(a.v_pool) + pool_v_at(pb, nkv, g, 4 * grp, D) + col * kBlk;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) vf[kb][t] = *reinterpret_cast<const uint2*>(vp + t * 16 * kBlk);
+    };
+    auto load_batch = [&](int i0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int pb = tile_of(i0 + kb);
+        load_k(kb, pb);
+        load_v(kb, pb);
+      }
+    };
+    // Queries: the prologue's loads go out first, then (unless the piece writes the new key,
+    // which must reach the pool before its tile is read) the first tiles, so that the arithmetic
+    // below overlaps those loads.
+    float xq[G][2];
+    float c = 0.f, sn = 0.f, gq0 = 1.f, gq1 = 1.f, gk0 = 1.f, gk1 = 1.f;
+    float kv[4][kPNP];
+    int slot = -1;
+    const float* base = a.qkv + static_cast<size_t>(row) * ld;
+    {
+      float qp[G][2][kPNP];
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int k = 0; k < kPNP; ++k)
+            qp[j][h][k] = (act && k < a.n_parts) ? base[k * a.part_stride + (g * G + j) * D + lane + h * half] : 0.f;
+      const int p = a.pos[row];
+      c = act ? a.rope_cos[static_cast<size_t>(p) * half + lane] : 0.f;
+      sn = act ? a.rope_sin[static_cast<size_t>(p) * half + lane] : 0.f;
+      if (a.q_norm && act) {
+        gq0 = T::to_f(static_cast<const S*>(a.q_norm)[lane]);
+        gq1 = T::to_f(static_cast<const S*>(a.q_norm)[lane + half]);
+      }
+      if (writes_new) {
+        const int kcol = (a.nq + g) * D, vcol = (a.nq + nkv + g) * D;
+        slot = a.slot[row];
+        if (a.k_norm && act) {
+          gk0 = T::to_f(static_cast<const S*>(a.k_norm)[lane]);
+          gk1 = T::to_f(static_cast<const S*>(a.k_norm)[lane + half]);
+        }
+#pragma unroll
+        for (int k = 0; k < kPNP; ++k) {
+          const bool on = act && k < a.n_parts;
+          kv[0][k] = on ? base[k * a.part_stride + kcol + lane] : 0.f;
+          kv[1][k] = on ? base[k * a.part_stride + kcol + lane + half] : 0.f;
+          kv[2][k] = on ? base[k * a.part_stride + vcol + lane] : 0.f;
+          kv[3][k] = on ? base[k * a.part_stride + vcol + lane + half] : 0.f;
+        }
+      } else {
+        load_batch(0);
+      }
+      // partials summed in order: the kPNP loaded above, then any further ones
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int cc = (g * G + j) * D + lane + h * half;
+          float v = 0.f;
+#pragma unroll
+          for (int k = 0; k < kPNP; ++k)
+            if (k < a.n_parts) v += qp[j][h][k];
+          for (int k = kPNP; k < a.n_parts; ++k) v += act ? base[k * a.part_stride + cc] : 0.f;
+          xq[j][h] = act ? v : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < G; ++j) norm_rope_pair_g<D>(xq[j][0], xq[j][1], a.q_norm != nullptr, gq0, gq1, a.eps, c, sn);
+    }
+    if (act) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        qsw[wid][j][lane] = xq[j][0] * a.scale;
+        qsw[wid][j][lane + half] = xq[j][1] * a.scale;
+      }
+    }
+    if (writes_new) {
+      // the row's new K and V to its slot, complete before any tile of the piece is requested
+      const int kcol = (a.nq + g) * D, vcol = (a.nq + nkv + g) * D;
+      auto sum = [&](const float(&src)[kPNP], int cc) -> float {
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < kPNP; ++k)
+          if (k < a.n_parts) v += src[k];
+        for (int k = kPNP; k < a.n_parts; ++k) v += base[k * a.part_stride + cc];
+        return v;
+      };
+      float k0 = act ? sum(kv[0], kcol + lane) : 0.f, k1v = act ? sum(kv[1], kcol + lane + half) : 0.f;
+      norm_rope_pair_g<D>(k0, k1v, a.k_norm != nullptr, gk0, gk1, a.eps, c, sn);
+      const int blk = slot >= 0 ? slot / kBlk : a.num_blocks - 1;
+      const int off = slot >= 0 ? slot % kBlk : 0;
+      if (act) {
+        S* kp = static_cast<S*>(a.k_pool) + pool_k_at(blk, nkv, g, off, D);
+        S* vp = static_cast<S*>(a.v_pool) + pool_v_at(blk, nkv, g, off, D);
+        kp[lane] = T::from_f(k0);
+        kp[lane + half] = T::from_f(k1v);
+        vp[lane * kBlk] = T::from_f(sum(kv[2], vcol + lane));
+        vp[(lane + half) * kBlk] = T::from_f(sum(kv[3], vcol + lane + half));
+      }
+      stores_done();
+      load_batch(0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Q^T fragments: column = query head col (zero past G), k slots = dims ks*32 + 8*grp .. + 8
+    uint4 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (col < G) {
+        const float* src = &qsw[wid][col < G ? col : 0][ks * 32 + 8 * grp];
+        qf[ks] = make_uint4(pack2<T>(src[0], src[1]), pack2<T>(src[2], src[3]), pack2<T>(src[4], src[5]),
+                            pack2<T>(src[6], src[7]));
+      } else {
+        qf[ks] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    f32x4_t acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+    for (int i0 = 0; i0 < nt; i0 += KB) {
+      const bool more = i0 + KB < nt;
+      f32x4_t s[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[kb] = mfma16x16x32<T>(kf[kb][ks], qf[ks], s[kb]);
+      }
+      if (more) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) load_k(kb, tile_of(i0 + KB + kb));
+      }
+      // this lane holds keys t0 + 4*grp + i of head col (t0: first key of tile i0 + kb); keys past
+      // the piece's end, and tiles past the piece, are masked
+      float bm = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int t0 = (ta + i0 + kb) * kBlk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[kb][i] = (t0 + 4 * grp + i < k1) ? s[kb][i] : -INFINITY;
+          bm = fmaxf(bm, s[kb][i]);
+        }
+      }
+      bm = max_xor32(max_xor16(bm));
+      const float mn = fmaxf(m, bm);                          // finite: tile i0 has a live key
+      const float corr = __expf(m - mn);
+      float ps = 0.f;
+      uint2 pt[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = __expf(s[kb][i] - mn);
+          ps += pr[i];
+        }
+        pt[kb] = make_uint2(pack2<T>(pr[0], pr[1]), pack2<T>(pr[2], pr[3]));
+      }
+      ps = add_xor32(add_xor16(ps));
+      lsum = lsum * corr + ps;
+      m = mn;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] *= corr;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int t0 = (ta + i0 + kb) * kBlk;
+        if (t0 + kBlk > k1) {
+          // a masked key adds nothing, even if its slot holds NaN (0 * NaN would not be 0)
+          const int q0 = t0 + 4 * grp;
+          const uint32_t m0 = (q0 < k1 ? 0xffffu : 0u) | (q0 + 1 < k1 ? 0xffff0000u : 0u);
+          const uint32_t m1 = (q0 + 2 < k1 ? 0xffffu : 0u) | (q0 + 3 < k1 ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            vf[kb][t].x &= m0;
+            vf[kb][t].y &= m1;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[t] = mfma16x16x16<T>(vf[kb][t], pt[kb], acc[t]);
+      }
+      if (more) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) load_v(kb, tile_of(i0 + KB + kb));
+      }
+    }
+    S* out = static_cast<S*>(a.out) + (static_cast<size_t>(row) * a.nq + g * G) * D;
+    if (np == 1) {   // the whole pair: its output (lane: dims t*16 + 4*grp + i of head col)
+      if (col < G) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[col * D + t * 16 + 4 * grp + i] = T::from_f(acc[t][i] / lsum);
+      }
+      continue;
+    }
+    // this piece's partial, then the last of the pair's pieces to arrive merges them in piece order
+    float* part = a.partials + static_cast<size_t>(slot0) * G * (D + 2);
+    if (col < G) {
+      float* pp = part + (static_cast<size_t>(piece) * G + col) * (D + 2);
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_dev(pp + 2 + t * 16 + 4 * grp + i, acc[t][i]);
+      if (grp == 0) {
+        st_dev(pp, m);
+        st_dev(pp + 1, lsum);
+      }
+    }
+    stores_done();
+    int last = 0;
+    if (lane == 0) last = arrive_last(a.split_cnt + static_cast<size_t>(row) * nkv + g, np) ? 1 : 0;
+    if (!__builtin_amdgcn_readfirstlane(last)) continue;
+    // lane p holds piece p's (max, sum) of each head: the pair's max, the pieces' factors, the total
+    const bool live = lane < np;
+    float fj[G], Lj[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float2 ml = live ? ld_dev2(part + (static_cast<size_t>(lane) * G + j) * (D + 2)) : make_float2(-INFINITY, 0.f);
+      const float M = wave_max(ml.x);
+      fj[j] = live ? __expf(ml.x - M) : 0.f;
+      Lj[j] = wave_sum(fj[j] * ml.y);
+    }
+    constexpr int kMB = 8;   // pieces' loads in flight at once
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float* pj = part + static_cast<size_t>(j) * (D + 2) + 2;
+      float o0 = 0.f, o1 = 0.f;
+      for (int p0 = 0; p0 < np; p0 += kMB) {
+        float v0[kMB], v1[kMB];
+#pragma unroll
+        for (int k = 0; k < kMB; ++k) {
+          const size_t at = static_cast<size_t>(p0 + k) * G * (D + 2);
+          v0[k] = (p0 + k < np && lane < D) ? ld_dev(pj + at + lane) : 0.f;
+          v1[k] = (p0 + k < np && lane + 64 < D) ? ld_dev(pj + at + lane + 64) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < kMB; ++k) {
+          if (p0 + k < np) {
+            const float fp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fj[j]), p0 + k));
+            o0 += fp * v0[k];
+            o1 += fp * v1[k];
+          }
+        }
+      }
+      if (lane < D) out[j * D + lane] = T::from_f(o0 / Lj[j]);
+      if (lane + 64 < D) out[j * D + lane + 64] = T::from_f(o1 / Lj[j]);
+    }
+  }
+}
+
 }  // namespace gr

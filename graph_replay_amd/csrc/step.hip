@@ -188,12 +188,48 @@ int split_tokens_for(int rows, int max_len) {
   return P;
 }
 
-// (row, split) partial slots that attention over `rows` rows may use at any key bound up to
-// max_position. The split count is not monotone in the key bound (the split length doubles once a
-// row would need more than kMaxSplits splits), so the bound uses the shortest split length any key
-// bound can give this row count (512 keys stands for 2,048 where longer rows are possible) and
-// caps it at kMaxSplits.
-size_t attn_slots_bound(int rows, int max_position) {
+// Rows from which the balanced kernel (k_attn_flat) takes over from the split grid, for 16-bit
+// K/V (step_config.balanced_attention_rows; 0 picks the default). Measured per layer on Qwen3-0.6B:
+// 32 rows of 128-2,048 keys take 46 us on the split grid and 53 us balanced (each wave's share is
+// then ~20 tiles, and the fixed costs of its pieces and merges outweigh the balance); 256 rows of
+// 16-4,352 keys take 403 us on the split grid and 332 us balanced.
+constexpr int kFlatMinRowsDefault = 128;
+constexpr int kFlatMinRowsLeast = 9;   // at most 8 rows stay on the split grid (it carries the weight prefetch)
+int flat_min_rows(const step_config& c) {
+  return c.balanced_attention_rows > 0 ? c.balanced_attention_rows : kFlatMinRowsDefault;
+}
+bool use_flat(int rows, const step_config& c) {
+  return c.dtype != STEP_F32 && rows >= flat_min_rows(c) && rows <= gr::kFlatMaxRows;
+}
+// The balanced kernel serves decode steps only (the fused prologue, one row per request): the mixed
+// step's decode rows run beside the packed prefill attention, where the split grid's launch, sized
+// by the rows, shares the GPU better (a 512-token chunk + 32 decode rows: 4.69 ms per step on the
+// split grid, 5.35 ms with the balanced kernel).
+
+// Partial slots (each nq query heads of head_dim + 2 floats) that one attention launch over `rows`
+// rows with keys bounded by max_len uses: a (row, split) pair each on the split grid; on the
+// balanced kernel gr::flat_slots(rows, nkv) slots of G = nq / nkv heads.
+size_t split_slot_demand(int rows, int max_len) {
+  const int P = split_tokens_for(rows, max_len);
+  return static_cast<size_t>(rows) * std::max(1, (max_len + P - 1) / P);
+}
+size_t flat_slot_demand(int rows, const step_config& c) {
+  const size_t G = static_cast<size_t>(c.q_heads / c.kv_heads);
+  return static_cast<size_t>(rows) + (static_cast<size_t>(gr::kFlatWaves) * G + c.q_heads - 1) / c.q_heads;
+}
+// the most either kind of launch over `rows` rows uses (a decode step may run the balanced kernel,
+// a mixed step's rows always run the split grid)
+size_t attn_slot_demand(int rows, int max_len, const step_config& c) {
+  const size_t sp = split_slot_demand(rows, max_len);
+  return use_flat(rows, c) ? std::max(sp, flat_slot_demand(rows, c)) : sp;
+}
+
+// The most split-grid slots attention over `rows` rows may use at any key bound up to max_position.
+// The split count is not monotone in the key bound (the split length doubles once a row would need
+// more than kMaxSplits splits), so the bound uses the shortest split length any key bound can give
+// this row count (512 keys stands for 2,048 where longer rows are possible) and caps it at
+// kMaxSplits.
+size_t split_slots_bound(int rows, int max_position) {
   const int P = rows <= 8 ? 64 : (rows <= 64 && max_position <= 2560 ? 2048 : 512);
   return static_cast<size_t>(rows) * std::min(gr::kMaxSplits, (max_position + P - 1) / P);
 }
@@ -241,10 +277,13 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.d_o = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * H);
   L.d_d = take(sizeof(float) * static_cast<size_t>(kMaxKsplit) * TM * H);
   L.act = take(static_cast<size_t>(eb) * TM * I);
-  // attention partials: the most (row, split) slots any row count up to TM can use (the bound is
-  // constant inside each row class, so its largest row count gives the class maximum)
+  // attention partials: the most slots any row count up to TM can use on the split grid (the bound
+  // grows with the row count inside each split-length class, so the class's largest row count gives
+  // its maximum), and on the balanced kernel (growing with the row count)
   size_t part_rows_splits = 0;
-  for (int rows : {8, 64, TM}) part_rows_splits = std::max(part_rows_splits, attn_slots_bound(std::min(rows, TM), c.max_position));
+  for (int rows : {8, 64, TM}) part_rows_splits = std::max(part_rows_splits, split_slots_bound(std::min(rows, TM), c.max_position));
+  const int flat_top = std::min(TM, gr::kFlatMaxRows);
+  if (use_flat(flat_top, c)) part_rows_splits = std::max(part_rows_splits, flat_slot_demand(flat_top, c));
   L.attn_slots = part_rows_splits;
   L.attn_part = take(sizeof(float) * part_rows_splits * nq * (d + 2));
   L.attn_cnt = take(sizeof(unsigned) * static_cast<size_t>(TM) * nkv);
@@ -321,6 +360,9 @@ int validate_config(step_ctx* ctx, const step_config* c) {
       return fail(ctx, STEP_EINVAL, "mixed buckets must be ascending and in [1, max_tokens]");
   }
   if (c->persistent_decode != 0 && c->persistent_decode != 1) return fail(ctx, STEP_EINVAL, "persistent_decode must be 0 or 1");
+  if (c->balanced_attention_rows != 0 && c->balanced_attention_rows < kFlatMinRowsLeast)
+    return fail(ctx, STEP_EINVAL, "balanced_attention_rows %d: 0 or at least %d", c->balanced_attention_rows,
+                kFlatMinRowsLeast);
   if (c->persistent_decode) {
     if (c->dtype == STEP_F32 || c->head_dim != 128 || c->hidden != 1024 || c->q_heads * c->head_dim != 2048 ||
         c->intermediate != 3072 || G != 2)
@@ -548,27 +590,30 @@ int run_norm(step_ctx* ctx, int M, const float* r_in, const float* delta, int n_
   return STEP_OK;
 }
 
-// fp32 K/V: FMA kernel; 16-bit K/V: matrix-core kernel, two blocks per wave step for long splits
+// fp32 K/V: FMA kernel; 16-bit K/V: matrix-core kernel, two blocks per wave step for long splits,
+// or (flat_rows > 0) the balanced kernel over flat_rows grid rows
 template <class T, int D, int G>
-void launch_attn_rows_g(const AttnRowsArgs& a, dim3 grid, hipStream_t s) {
+void launch_attn_rows_g(const AttnRowsArgs& a, dim3 grid, hipStream_t s, int flat_rows) {
   if constexpr (std::is_same<T, F32>::value) {
     launch((k_attn_rows<T, D, G>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.split_tokens >= 256) launch((k_attn_rows_mfma<T, D, G, 2>), grid, dim3(256), 0, s, a);
+    if (flat_rows > 0) launch((k_attn_flat<T, D, G, 2>), dim3(gr::kFlatBlocks), dim3(256), 0, s, a, flat_rows);
+    else if (a.split_tokens >= 256) launch((k_attn_rows_mfma<T, D, G, 2>), grid, dim3(256), 0, s, a);
     else launch((k_attn_rows_mfma<T, D, G, 1>), grid, dim3(256), 0, s, a);
   }
 }
 template <class T, int D>
-hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream_t s) {
+hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream_t s, int flat_rows) {
   switch (G) {
-    case 1: launch_attn_rows_g<T, D, 1>(a, grid, s); break;
-    case 2: launch_attn_rows_g<T, D, 2>(a, grid, s); break;
-    case 4: launch_attn_rows_g<T, D, 4>(a, grid, s); break;
-    case 6: launch_attn_rows_g<T, D, 6>(a, grid, s); break;
-    default: launch_attn_rows_g<T, D, 8>(a, grid, s); break;
+    case 1: launch_attn_rows_g<T, D, 1>(a, grid, s, flat_rows); break;
+    case 2: launch_attn_rows_g<T, D, 2>(a, grid, s, flat_rows); break;
+    case 4: launch_attn_rows_g<T, D, 4>(a, grid, s, flat_rows); break;
+    case 6: launch_attn_rows_g<T, D, 6>(a, grid, s, flat_rows); break;
+    default: launch_attn_rows_g<T, D, 8>(a, grid, s, flat_rows); break;
   }
   return hipGetLastError();
 }
+
 
 // Row attention over `rows` query rows; max_len bounds the keys of any row (sets the split grid).
 // q == nullptr: decode rows, whose QK-norm + RoPE + KV write run inside the attention kernel from
@@ -592,8 +637,9 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.eps = c.rms_eps;
   a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
   a.block_table = bt; a.bt_stride = bt_stride; a.row_ids = row_ids; a.row_req = row_req; a.seq_lens = seq_lens;
+  const bool flat = q == nullptr && row_ids == nullptr && row_req == nullptr && use_flat(rows, c);
   a.split_tokens = split_tokens_for(rows, max_len);
-  a.max_splits = std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
+  a.max_splits = flat ? 1 : std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
   a.num_blocks = c.num_blocks;
   a.out = out;
   a.partials = reinterpret_cast<float*>(ctx->ws + Ly.attn_part);
@@ -601,18 +647,19 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
   const int G = c.q_heads / c.kv_heads;
   if (rows > Ly.TM) return fail(ctx, STEP_EINVAL, "attention over %d rows exceeds the workspace's %d", rows, Ly.TM);
-  if (static_cast<size_t>(rows) * a.max_splits > Ly.attn_slots)
+  if ((flat ? flat_slot_demand(rows, c) : split_slot_demand(rows, max_len)) > Ly.attn_slots)
     return fail(ctx, STEP_EINVAL, "attention over %d rows x %d splits exceeds the workspace's %zu partial slots", rows,
                 a.max_splits, Ly.attn_slots);
   dim3 grid(rows, c.kv_heads, a.max_splits);
-  if (ctx->pf.n > 0) {
+  if (ctx->pf.n > 0 && !flat) {
     a.pf = ctx->pf;
     const int plane = rows * c.kv_heads;
     grid.z += (kPrefetchBlocks + plane - 1) / plane;
   }
   pre_launch(ctx, KK_ATTN);
-  hipError_t e = (c.head_dim == 64) ? launch_attn_rows_d<T, 64>(a, G, grid, ctx->stream)
-                                    : launch_attn_rows_d<T, 128>(a, G, grid, ctx->stream);
+  const int flat_rows = flat ? rows : 0;
+  hipError_t e = (c.head_dim == 64) ? launch_attn_rows_d<T, 64>(a, G, grid, ctx->stream, flat_rows)
+                                    : launch_attn_rows_d<T, 128>(a, G, grid, ctx->stream, flat_rows);
   if (e != hipSuccess) return fail(ctx, STEP_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   return STEP_OK;
 }
@@ -1703,15 +1750,14 @@ extern "C" int step_set_device_status(step_ctx* ctx, int32_t site) {
   return STEP_OK;
 }
 
-extern "C" int32_t step_attention_splits(const step_config* cfg, int32_t rows, int32_t max_len, int64_t* slots) {
+extern "C" int32_t step_attention_slots(const step_config* cfg, int32_t rows, int32_t max_len, int64_t* capacity) {
   try {
     if (validate_config(nullptr, cfg) != STEP_OK) return STEP_EINVAL;
     Layout L{};
     compute_layout(*cfg, L);
-    if (slots) *slots = static_cast<int64_t>(L.attn_slots);
+    if (capacity) *capacity = static_cast<int64_t>(L.attn_slots);
     if (rows < 1 || rows > L.TM || max_len < 1 || max_len > cfg->max_position) return STEP_EINVAL;
-    const int P = split_tokens_for(rows, max_len);
-    return (max_len + P - 1) / P;
+    return static_cast<int32_t>(attn_slot_demand(rows, max_len, *cfg));
   } catch (...) {
     return STEP_EHIP;
   }

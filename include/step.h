@@ -113,6 +113,13 @@ typedef struct {
    * configurations get STEP_EUNSUPPORTED at step_init. buckets[0] must be 1. Other buckets keep
    * the multi-kernel step. 0: off. */
   int32_t persistent_decode;
+  /* Row attention launches over at least this many rows (16-bit K/V, at most 1,024 rows) run on the
+   * balanced kernel, which cuts the launch's keys into equal shares per wave whatever the rows'
+   * lengths; fewer rows use the split-KV grid. 0: the default, 128. Otherwise at least 9 (the split
+   * grid keeps 8 rows and fewer); above 1,024: never. The balanced kernel's split points follow the
+   * whole batch's lengths, so a row's output can change in its last bits with the other rows'
+   * lengths (padding rows have none and change nothing); the split grid's follow the row alone. */
+  int32_t balanced_attention_rows;
 } step_config;
 
 typedef struct {
@@ -225,14 +232,17 @@ int step_device_status(step_ctx *ctx);
  * the next steps ends at once and their outputs are marked invalid. STEP_EINVAL without
  * persistent_decode or for site <= 0. step_device_status reports and clears it. */
 int step_set_device_status(step_ctx *ctx, int32_t site);
-/* Host-only sizing query of the decode attention's split-KV grid ("Removing overhead: fusion,
- * graphs and async scheduling", section "CUDA graphs for a changing batch": the split count is
- * fixed per launch shape, never chosen from the batch's contents). Returns the splits per row that
- * attention over `rows` rows with keys bounded by max_len uses (rows in [1, max(max_batch,
- * max_tokens)], max_len in [1, max_position]; STEP_EINVAL otherwise or for an invalid config), and
- * writes to *slots (when not NULL, and whenever cfg is valid) the (row, split) partial slots the
- * workspace of this config holds. rows * splits never exceeds *slots. */
-int32_t step_attention_splits(const step_config *cfg, int32_t rows, int32_t max_len, int64_t *slots);
+/* Host-only sizing query of the row attention's partial outputs ("Removing overhead: fusion,
+ * graphs and async scheduling", section "CUDA graphs for a changing batch": a launch's shape is
+ * fixed per row count, never chosen from the batch's contents). Returns the most partial slots
+ * (each q_heads x (head_dim + 2) floats) one attention launch over `rows` rows with keys bounded by
+ * max_len uses: rows x splits on the split-KV grid, and for a decode step on the balanced kernel
+ * (16-bit K/V, balanced_attention_rows to 1,024 rows) rows + 1,024 x (q_heads / kv_heads) / q_heads
+ * rounded up, whatever the keys; the larger of the two where both can run. rows must lie in
+ * [1, max(max_batch, max_tokens)] and max_len in [1, max_position]; STEP_EINVAL otherwise or for an
+ * invalid config. Writes to *capacity (when not NULL, and whenever cfg is valid) the slots the
+ * workspace of this config holds, which no launch's demand exceeds. */
+int32_t step_attention_slots(const step_config *cfg, int32_t rows, int32_t max_len, int64_t *capacity);
 /* Phase timestamps of the last step_profile_decode of a persistent single-row step, in
  * microseconds after the kernel's start (block 0's view; -1 where none was taken): slot 8 l + k for
  * layer l holds k = 1 QKV input normed, 2 attention items done, 3 merges done, 4 O input arrived,

@@ -184,8 +184,9 @@ def _fill_random(dec, seed):
 
 def test_bs256_sampled_rows_vs_oracle_and_padding(torch_cuda):
     """Qwen3-0.6B bf16 (2 layers), 256 rows, contexts {16..4096} + 64..256, T = 0.7 Gumbel. A 16-row
-    sample is checked against the oracle; padded buckets (13 -> 16, 100 -> 128, 200 -> 256) give the
-    real rows the same bits as an unpadded run of the same kernels."""
+    sample is checked against the oracle (the batch-256 attention runs on the balanced kernel); in
+    padded buckets (13 -> 16, 100 -> 128, 200 -> 256) the padding rows' contents never change the
+    real rows' bits."""
     torch = torch_cuda
     wl, shape, W, sc, dec = _bs256_setup(torch, 2)
     _fill_random(dec, 7)
@@ -215,17 +216,30 @@ def test_bs256_sampled_rows_vs_oracle_and_padding(torch_cuda):
         ref = oracle.final_logits(W32, hid)[0]
         assert max_abs(full[j], ref) <= TOL["bf16"], (j, max_abs(full[j], ref))
         assert near_tie_ok(int(ftok[j]), oracle.gumbel_scores(ref, 0.7, u[j]), TOL["bf16"]), j
-    # padding: the same rows padded up to a bucket reproduce the r = bucket run bit for bit
+    # Padding: r rows padded up to a bucket. Whatever the padding rows hold (here: other tokens and
+    # positions, no keys, slot -1), the real rows get the same bits. Up to 127 rows the attention
+    # is the split grid, which sees each row alone, so there the real rows also match a run of the
+    # bucket's size in real rows bit for bit; from 128 rows the balanced kernel's split points
+    # follow every row's length, so such a run matches to the rounding bound.
     for r, bucket in ((13, 16), (100, 128), (200, 256)):
-        dec.decode(toks[:bucket], pos[:bucket], lens[:bucket], slots[:bucket], bt[:bucket])
-        torch.cuda.synchronize()
-        want = dec.logits[:r].cpu().numpy().copy()
         dec.decode(toks[:r], pos[:r], lens[:r], slots[:r], bt[:r])
         torch.cuda.synchronize()
         assert dec.last_bucket() == bucket
-        got = dec.logits[:r].cpu().numpy()
-        assert np.array_equal(got, want), (r, max_abs(got, want))
+        got = dec.logits[:r].cpu().numpy().copy()
         assert np.all(np.isfinite(dec.logits[:bucket].cpu().numpy()))
+        pt, pp, pl, ps, pb = (x[:bucket].copy() for x in (toks, pos, lens, slots, bt))
+        pt[r:], pp[r:], pl[r:], ps[r:], pb[r:] = 5, 3, 0, -1, 0
+        dec.decode(pt, pp, pl, ps, pb)
+        torch.cuda.synchronize()
+        other = dec.logits[:r].cpu().numpy()
+        assert np.array_equal(got, other), (r, max_abs(got, other))
+        dec.decode(toks[:bucket], pos[:bucket], lens[:bucket], slots[:bucket], bt[:bucket])
+        torch.cuda.synchronize()
+        full = dec.logits[:r].cpu().numpy()
+        if bucket < 128:
+            assert np.array_equal(got, full), (r, max_abs(got, full))
+        else:
+            assert max_abs(got, full) <= TOL["bf16"], (r, max_abs(got, full))
     dec.close()
 
 

@@ -218,11 +218,12 @@ def _randomise(dec, seed):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("persistent", [False, True])
-def test_decode_changes_only_its_slots_and_the_scratch_block(torch_cuda, persistent):
+@pytest.mark.parametrize("persistent,balanced", [(False, 0), (True, 0), (False, 9)])
+def test_decode_changes_only_its_slots_and_the_scratch_block(torch_cuda, persistent, balanced):
     """A host-fed decode step padded to its bucket (13 rows -> 16; the persistent step at 1 row) and
     two device-continued steps after it leave every pool byte bit-unchanged except the slots of the
-    rows' new tokens and the scratch block, which padding rows write."""
+    rows' new tokens and the scratch block, which padding rows write (balanced = 9: the attention
+    of the 16-row bucket, which writes the new keys, on the balanced kernel)."""
     torch = torch_cuda
     shape = synth.QWEN3_0_6B.replace(layers=2, vocab=4096)
     W = synth.make_weights(shape, 0)
@@ -231,7 +232,8 @@ def test_decode_changes_only_its_slots_and_the_scratch_block(torch_cuda, persist
     sc = Scenario(shape, W, ctx, steps=4, seed=2500)
     buckets = [1] if persistent else [1, 4, 16]
     dec = _decoder(shape, W, num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=512,
-                   max_batch=buckets[-1], buckets=buckets, persistent_decode=persistent)
+                   max_batch=buckets[-1], buckets=buckets, persistent_decode=persistent,
+                   balanced_attention_rows=balanced)
     _randomise(dec, 2501)
     toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
     before = _pool_bits(dec)

@@ -67,8 +67,10 @@ def test_tiny_f32_prefill_then_greedy_decode(torch_cuda, shape):
     dec.close()
 
 
-def test_decode_all_bucket_paths_bf16(torch_cuda):
-    """bf16 decode at row counts that hit every matmul path (VALU <= 8, MFMA 16/32, tiled 64) and pad."""
+@pytest.mark.parametrize("balanced", [0, 9])
+def test_decode_all_bucket_paths_bf16(torch_cuda, balanced):
+    """bf16 decode at row counts that hit every matmul path (VALU <= 8, MFMA 16/32, tiled 64) and pad;
+    with balanced = 9 the attention of 9 rows and more runs on the balanced kernel."""
     torch = torch_cuda
     shape = synth.TINY.replace(name="tiny-bf16", dtype="bf16")
     W = synth.make_weights(shape, 0)
@@ -77,7 +79,7 @@ def test_decode_all_bucket_paths_bf16(torch_cuda):
     contexts = rng.integers(1, 200, size=64).tolist()
     sc = Scenario(shape, W, contexts, steps=2, seed=2024)
     dec = _decoder(shape, W, num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=256, max_batch=64,
-                   buckets=[1, 2, 4, 8, 16, 32, 64], use_graphs=True)
+                   buckets=[1, 2, 4, 8, 16, 32, 64], use_graphs=True, balanced_attention_rows=balanced)
     sc.inject(dec)
     for r in (1, 3, 8, 13, 32, 50, 64):
         log("bf16 tiny rows", r)
@@ -121,8 +123,10 @@ def test_lm_head_ragged_vocab_9_to_32_rows(torch_cuda):
     dec.close()
 
 
-def test_qwen3_width_two_layers_bs32_gumbel(torch_cuda):
-    """Qwen3-0.6B widths (2 layers) at batch 32 over shuffled paged KV, Gumbel-max at T = 1 with Philox."""
+@pytest.mark.parametrize("balanced", [0, 9])
+def test_qwen3_width_two_layers_bs32_gumbel(torch_cuda, balanced):
+    """Qwen3-0.6B widths (2 layers) at batch 32 over shuffled paged KV, Gumbel-max at T = 1 with Philox;
+    the attention on the split grid (balanced = 0) and on the balanced kernel (balanced = 9)."""
     torch = torch_cuda
     shape = synth.QWEN3_0_6B.replace(layers=2)
     W = synth.make_weights(shape, 0)
@@ -130,7 +134,7 @@ def test_qwen3_width_two_layers_bs32_gumbel(torch_cuda):
     ctx = np.random.default_rng(1003).integers(128, 2048, size=32, endpoint=True).tolist()
     sc = Scenario(shape, W, ctx, steps=2, seed=1003)
     dec = _decoder(shape, W, num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=2304, max_batch=32,
-                   buckets=[1, 2, 4, 8, 16, 32])
+                   buckets=[1, 2, 4, 8, 16, 32], balanced_attention_rows=balanced)
     sc.inject(dec)
     toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
     seed = 0x1234_5678_9ABC

@@ -139,31 +139,41 @@ def _q3_cfg(L, max_position, max_batch=8, max_tokens=0):
     return cfg
 
 
-@pytest.mark.parametrize("max_position,max_batch,max_tokens", [(9000, 8, 32), (9000, 8, 0), (20000, 64, 600),
-                                                               (2304, 32, 0), (8192, 1, 0), (16384, 256, 0)])
-def test_attention_partials_hold_every_split_grid(max_position, max_batch, max_tokens):
-    """For every row count and key bound a launch can use, rows x splits fits the workspace's partial
-    slots. The split count is not monotone in the key bound (the split length doubles past 128
-    splits), so the sweep covers every key bound, not just max_position."""
+@pytest.mark.parametrize("max_position,max_batch,max_tokens,dtype,bal", [
+    (9000, 8, 32, "bf16", 0), (9000, 8, 0, "bf16", 0), (20000, 64, 600, "bf16", 0), (2304, 32, 0, "bf16", 0),
+    (2304, 32, 0, "bf16", 9), (8192, 1, 0, "bf16", 0), (16384, 256, 0, "bf16", 0), (4096, 1100, 1500, "bf16", 0),
+    (4096, 300, 0, "bf16", 40), (4096, 300, 0, "bf16", 2000), (9000, 8, 600, "f32", 0), (2304, 64, 0, "f32", 9)])
+def test_attention_partials_hold_every_launch(max_position, max_batch, max_tokens, dtype, bal):
+    """For every row count and key bound a launch can use, its partial slots fit the workspace's. On
+    the split grid the split count is not monotone in the key bound (the split length doubles past
+    128 splits), so the sweep covers every key bound, not just max_position; the balanced kernel's
+    demand is fixed by the row count alone."""
     import graph_replay_amd as g
     import graph_replay_amd._lib as L
     if not os.path.exists(L.LIB_PATH):
         pytest.skip("libstep.so not built")
     cfg = _q3_cfg(L, max_position, max_batch, max_tokens)
+    cfg.dtype = L.STEP_BF16 if dtype == "bf16" else L.STEP_F32
+    cfg.balanced_attention_rows = bal
     tm = max(max_batch, max_tokens)
-    _, slots = g.step_attention_splits(cfg, 1, 1)
-    assert slots > 0
-    worst = 0
-    for rows in sorted({1, 2, 7, 8, 9, 32, 63, 64, 65, tm} & set(range(1, tm + 1))):
-        for max_len in range(1, max_position + 1, 7 if max_position > 10000 else 3):
-            n, s = g.step_attention_splits(cfg, rows, max_len)
-            assert 1 <= n <= 128 and s == slots
-            worst = max(worst, rows * n)
-        n, _ = g.step_attention_splits(cfg, rows, max_position)
-        worst = max(worst, rows * n)
-    assert worst <= slots
-    # the case that once overflowed: 8 rows at 8,192 keys under a 9,000-position bound uses 128 splits
+    G = cfg.q_heads // cfg.kv_heads
+    flat_extra = -(-1024 * G // cfg.q_heads)
+    _, cap = g.step_attention_slots(cfg, 1, 1)
+    assert cap > 0
+    rows_set = {1, 2, 7, 8, 9, 32, 39, 40, 63, 64, 65, 127, 128, 1023, 1024, 1025, tm} & set(range(1, tm + 1))
+    for rows in sorted(rows_set):
+        flat = dtype == "bf16" and (bal or 128) <= rows <= 1024
+        for max_len in list(range(1, max_position + 1, 7 if max_position > 10000 else 3)) + [max_position]:
+            n, c = g.step_attention_slots(cfg, rows, max_len)
+            assert c == cap and rows <= n <= cap, (rows, max_len, n, cap)
+            if flat:   # the balanced kernel's demand, or the split grid's where that is larger
+                assert n == rows + flat_extra or (n > rows + flat_extra and n % rows == 0)
+            else:
+                assert n % rows == 0 and 1 <= n // rows <= 128
+    # the case that once overflowed: 8 rows at 8,192 keys under a 9,000-position bound use 128 splits
     if max_position == 9000:
-        assert g.step_attention_splits(cfg, 8, 8192)[0] == 128 and 8 * 128 <= slots
-    assert g.step_attention_splits(cfg, tm + 1, 16)[0] == L.STEP_EINVAL
-    assert g.step_attention_splits(cfg, 1, max_position + 1)[0] == L.STEP_EINVAL
+        assert g.step_attention_slots(cfg, 8, 8192)[0] == 8 * 128 <= cap
+    assert g.step_attention_slots(cfg, tm + 1, 16)[0] == L.STEP_EINVAL
+    assert g.step_attention_slots(cfg, 1, max_position + 1)[0] == L.STEP_EINVAL
+    cfg.balanced_attention_rows = 8   # the split grid keeps 8 rows and fewer
+    assert g.step_attention_slots(cfg, 1, 1)[0] == L.STEP_EINVAL
