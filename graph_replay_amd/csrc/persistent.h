@@ -29,7 +29,7 @@
 // takes rows w, w + W, ...):
 //   P1  QKV: r += down(l-1) (every block keeps the whole residual row r, updated in the same
 //       order everywhere), x = RMSNorm(r) * g_in rounded to the dtype, qkv = W_qkv x (+ b).
-//   P2  attention: item (kv head g, 128-key split s): QK-RMSNorm + RoPE of the G query heads and
+//   P2  attention: item (kv head g, key split s of 64 TPW keys): QK-RMSNorm + RoPE of the G query heads and
 //       the key, the new K and V written to the paged pool by the split that holds them, and
 //       the split's (max, sum, unnormalised output) per query head, on the matrix cores.
 //   P2b merge: item (query head h, 32-dim chunk c) combines the splits in split order ->
@@ -48,9 +48,10 @@
 
 namespace gr {
 
-constexpr int kPSplit = 64;       // keys per attention item
-constexpr int kPTiles = kPSplit / 64;   // 16-key tiles per compute wave and item
-constexpr int kPMaxSplits = 64;   // splits per KV head the merge stages in LDS (max_position <= 8192)
+// Keys per attention item: 64 * TPW, where TPW (the kernel's last template argument) is the number
+// of 16-key tiles each of the four compute waves holds per item: 1 (64-key items) while a step's
+// items fit one per block, 2 (128-key items) for rows twice as long.
+constexpr int kPMaxSplits = 64;   // splits per KV head the merge stages in LDS
 constexpr int kPSpin = 1 << 17;   // polls before a wait gives up (each poll is a memory round trip)
 constexpr int kPPhases = 6;       // tagged phases per layer
 constexpr int kPStamps = 512;     // timestamp slots (block 0, optional)
@@ -349,34 +350,37 @@ __device__ inline void lane_x(const uint16_t* xs, uint4 (&xv)[VR]) {
 template <class T>
 __device__ inline uint16_t bits16(float x) { return __builtin_bit_cast(uint16_t, T::from_f(x)); }
 
-// K and V tiles of one attention item: compute wave w takes the 16-key tiles w + 4 kb (kb <
-// kPTiles) of the split (D = 128: K fragment 4 x 16 B, V^T fragment 8 x 8 B per tile, as in the
-// decode attention kernel). Without an item (g < 0) the scratch block is loaded, so the load count
-// is fixed.
+// K and V tiles of one attention item: compute wave w takes the 16-key tiles w + 4 kb (kb < TPW)
+// of the split (D = 128: K fragment 4 x 16 B, V^T fragment 8 x 8 B per tile, as in the decode
+// attention kernel). Without an item (g < 0) the scratch block is loaded, so the load count is
+// fixed.
+template <int TPW>
 struct AttnTiles {
-  uint4 kf[kPTiles][4];
-  uint2 vf[kPTiles][8];
+  uint4 kf[TPW][4];
+  uint2 vf[TPW][8];
 };
 
 // pool block of tile wid + 4 kb of split s (the scratch block where the split has no such tile);
 // the same for every layer
+template <int TPW>
 __device__ inline int attn_tile_block(const PersistArgs& a, int g, int s, int L, int kb) {
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t0 = s * kPSplit;
-  const int nblk = g < 0 ? 0 : (min(L, t0 + kPSplit) - t0 + kBlk - 1) / kBlk;
+  const int t0 = s * 64 * TPW;
+  const int nblk = g < 0 ? 0 : (min(L, t0 + 64 * TPW) - t0 + kBlk - 1) / kBlk;
   const int bi = wid + 4 * kb;
   const int e = t0 / kBlk + bi;
   const int pb = (bi < nblk && e < a.bt_stride) ? a.bt[e] : -1;
   return __builtin_amdgcn_readfirstlane(pb >= 0 ? pb : a.num_blocks - 1);
 }
 
-__device__ inline void attn_tiles_load(AttnTiles& at, const PersistArgs& a, const PLayer& lw, int g, const int (&pbs)[kPTiles]) {
+template <int TPW>
+__device__ inline void attn_tiles_load(AttnTiles<TPW>& at, const PersistArgs& a, const PLayer& lw, int g, const int (&pbs)[TPW]) {
   constexpr int D = 128;
   const int lane = opaque(static_cast<int>(threadIdx.x & 63));
   const int col = lane & 15, grp = lane >> 4;
   const int gg = g < 0 ? 0 : g;
 #pragma unroll
-  for (int kb = 0; kb < kPTiles; ++kb) {
+  for (int kb = 0; kb < TPW; ++kb) {
     const int pb = pbs[kb];
     const size_t ko = pool_k_at(pb, a.nkv, gg, col, D) + 8 * grp;          // elements; multiple of 8
 #pragma unroll
@@ -735,7 +739,7 @@ __device__ void ExchangeRole<T, VH, VQ, VI, G>::lm_head() {
 
 // Compute role (waves 0-3): the projections' weights in registers, issued one phase ahead, their
 // dot products, and the attention products on the matrix cores.
-template <class T, int VH, int VQ, int VI, int G>
+template <class T, int VH, int VQ, int VI, int G, int TPW>
 struct ComputeRole {
   using S = typename T::S;
   static constexpr int D = 128, H = 512 * VH, I = 512 * VI, XS_ = 512 * (VI > VQ ? (VI > VH ? VI : VH) : (VQ > VH ? VQ : VH));
@@ -748,13 +752,13 @@ struct ComputeRole {
   PShared<XS_, G>& sh;
   const int lane, wid, gw, NW, NQKV;
   int R_qkv, R_o, R_gu, R_dn;
-  int g0, pbs[kPTiles];        // the block's attention item: KV head (-1: none), its tiles' pool blocks
+  int g0, pbs[TPW];            // the block's attention item: KV head (-1: none), its tiles' pool blocks
   PLayer lw;
   WTile<T, VH, 1, TQ> wq;
   WTile<T, VQ, 1, TO> wo;
   WTile<T, VH, 2, TG> wg;
   WTile<T, VI, 1, TD> wd;
-  AttnTiles at;
+  AttnTiles<TPW> at;
   LmHead<T, VH> lm;
 
   __device__ ComputeRole(const PersistArgs& a_, const PStep& s_, PShared<XS_, G>& sh_)
@@ -773,7 +777,7 @@ struct ComputeRole {
     g0 = has ? it / st.nsplit : -1;
     const int s0 = has ? it % st.nsplit : 0;
 #pragma unroll
-    for (int kb = 0; kb < kPTiles; ++kb) pbs[kb] = attn_tile_block(a, g0, s0, st.L, kb);
+    for (int kb = 0; kb < TPW; ++kb) pbs[kb] = attn_tile_block<TPW>(a, g0, s0, st.L, kb);
     wq.load(sh.lw[0].qkv_w, sh.lw[0].qkv_b, NQKV, gw, NW, R_qkv, 0);
     attn_tiles_load(at, a, sh.lw[0], g0, pbs);
     wo.load(sh.lw[0].o_w, nullptr, H, gw, NW, R_o, 0);
@@ -808,7 +812,7 @@ struct ComputeRole {
     const int g = item / st.nsplit, s = item % st.nsplit;
     const int col = lane & 15, grp = lane >> 4;
     const int L = st.L;
-    const int t0 = s * kPSplit, t1 = min(L, t0 + kPSplit);
+    const int t0 = s * 64 * TPW, t1 = min(L, t0 + 64 * TPW);
     const int nblk = (t1 - t0 + kBlk - 1) / kBlk;
     const float* vnew = sh.at.stq + (G + 1) * D;
     if (s == st.nsplit - 1) {
@@ -826,7 +830,7 @@ struct ComputeRole {
       if ((bn & 3) == wid) {
         const int kb = bn >> 2;
 #pragma unroll
-        for (int q = 0; q < kPTiles; ++q) {
+        for (int q = 0; q < TPW; ++q) {
           if (q != kb) continue;
           if (col == on) {
 #pragma unroll
@@ -869,16 +873,16 @@ struct ComputeRole {
     for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
     if (wid < nblk) {
-      f32x4_t sc[kPTiles];
+      f32x4_t sc[TPW];
 #pragma unroll
-      for (int kb = 0; kb < kPTiles; ++kb) {
+      for (int kb = 0; kb < TPW; ++kb) {
         sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16x16x32<T>(at.kf[kb][ks], qf[ks], sc[kb]);
       }
       float bm = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < kPTiles; ++kb) {
+      for (int kb = 0; kb < TPW; ++kb) {
         const int tb = t0 + (wid + 4 * kb) * kBlk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -889,9 +893,9 @@ struct ComputeRole {
       bm = max_xor32(max_xor16(bm));
       m = bm;                                                   // finite: tile wid has a live key
       float ps = 0.f;
-      uint2 pt[kPTiles];
+      uint2 pt[TPW];
 #pragma unroll
-      for (int kb = 0; kb < kPTiles; ++kb) {
+      for (int kb = 0; kb < TPW; ++kb) {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -903,7 +907,7 @@ struct ComputeRole {
       ps = add_xor32(add_xor16(ps));
       lsum = ps;
 #pragma unroll
-      for (int kb = 0; kb < kPTiles; ++kb) {
+      for (int kb = 0; kb < TPW; ++kb) {
         const int tb = t0 + (wid + 4 * kb) * kBlk;
         if (tb + kBlk > t1) {
           // a masked key adds nothing, even if its slot holds NaN (0 * NaN would not be 0)
@@ -1007,7 +1011,7 @@ struct ComputeRole {
 // multiple of 512); G: query heads per KV head. Every compute wave must own at least one row of
 // the QKV, O, gate|up and down phases and every wave one LM-head row (the host keeps 4 * gridDim.x
 // <= the narrowest projection and 8 * gridDim.x <= the vocabulary).
-template <class T, int VH, int VQ, int VI, int G>
+template <class T, int VH, int VQ, int VI, int G, int TPW>
 __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) {
   constexpr int XS = 512 * (VI > VQ ? (VI > VH ? VI : VH) : (VQ > VH ? VQ : VH));
   __shared__ __align__(16) PShared<XS, G> sh;
@@ -1030,7 +1034,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
     for (int i = threadIdx.x; i < a.layers * kw; i += kPThreads) dst[i] = src[i];
   }
   __syncthreads();
-  st.nsplit = (st.L + kPSplit - 1) / kPSplit;
+  st.nsplit = (st.L + 64 * TPW - 1) / (64 * TPW);
   st.n_items = a.nkv * st.nsplit;
   st.tag0 = (ep + 1u) * static_cast<uint32_t>(kPPhases * a.layers + 1);
   stamp(a, 0);
@@ -1038,7 +1042,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_persist_decode(PersistArgs a) 
     ExchangeRole<T, VH, VQ, VI, G> ro(a, st, sh);
     run_step(ro, st, a.layers, a.nq);
   } else {
-    ComputeRole<T, VH, VQ, VI, G> ro(a, st, sh);
+    ComputeRole<T, VH, VQ, VI, G, TPW> ro(a, st, sh);
     run_step(ro, st, a.layers, a.nq);
   }
   // the last block to finish takes the token (when sampling) and advances the epoch for the next

@@ -239,6 +239,10 @@ constexpr int kMaxKsplit = 8;
 // weight-prefetch blocks appended to an attention launch (about one per CU)
 constexpr int kPrefetchBlocks = 256;
 
+// 16-key tiles per compute wave and attention item of the persistent step: one (64-key items) while
+// a row's items fit one per block, else two (128-key items)
+int persist_tpw(const step_config& c) { return c.max_position <= 64 * gr::kPBlocks / c.kv_heads ? 1 : 2; }
+
 bool compute_layout(const step_config& c, Layout& L) {
   const int H = c.hidden, d = c.head_dim, nq = c.q_heads, nkv = c.kv_heads, I = c.intermediate;
   const int QKV = (nq + 2 * nkv) * d;
@@ -301,7 +305,8 @@ bool compute_layout(const step_config& c, Layout& L) {
   L.samp_cand = take(sizeof(unsigned long long) * 512 * 48);
   L.samp_rng = take(16);
   if (c.persistent_decode) {
-    L.p_splits = (c.max_position + gr::kPSplit - 1) / gr::kPSplit;
+    const int split = 64 * persist_tpw(c);
+    L.p_splits = (c.max_position + split - 1) / split;
     L.p_lw = take(sizeof(gr::PLayer) * static_cast<size_t>(c.layers));
     L.p_qkv = take(sizeof(uint64_t) * static_cast<size_t>(QKV));
     L.p_part = take(sizeof(uint64_t) * static_cast<size_t>(nq) * L.p_splits * (d + 2));
@@ -371,7 +376,7 @@ int validate_config(step_ctx* ctx, const step_config* c) {
                   "3072 and 2 query heads per KV head");
     if (c->layers > gr::kPMaxLayers)
       return fail(ctx, STEP_EUNSUPPORTED, "persistent_decode holds at most %d layers", gr::kPMaxLayers);
-    const int max_keys = std::min(gr::kPSplit * gr::kPMaxSplits, gr::kPSplit * gr::kPBlocks / c->kv_heads);
+    const int max_keys = std::min(128 * gr::kPMaxSplits, 128 * gr::kPBlocks / c->kv_heads);
     if (c->max_position > max_keys)
       return fail(ctx, STEP_EUNSUPPORTED, "persistent_decode needs max_position <= %d", max_keys);
     if (c->buckets[0] != 1) return fail(ctx, STEP_EINVAL, "persistent_decode serves bucket 1, which the buckets must hold");
@@ -953,7 +958,8 @@ int run_persist(step_ctx* ctx, const DecodeMeta& m) {
     a.temp = m.temp; a.rng = m.rng; a.tokens = ctx->tokens; a.history = ctx->history;
     a.cand = reinterpret_cast<uint64_t*>(ws + L.p_cand);
     pre_launch(ctx, KK_PERSIST);
-    launch((k_persist_decode<T, 2, 4, 6, 2>), dim3(ctx->p_nb), dim3(gr::kPThreads), 0, ctx->stream, a);
+    if (persist_tpw(c) == 1) launch((k_persist_decode<T, 2, 4, 6, 2, 1>), dim3(ctx->p_nb), dim3(gr::kPThreads), 0, ctx->stream, a);
+    else launch((k_persist_decode<T, 2, 4, 6, 2, 2>), dim3(ctx->p_nb), dim3(gr::kPThreads), 0, ctx->stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(ctx, STEP_EHIP, "persistent decode launch failed: %s", hipGetErrorString(e));
     return STEP_OK;
@@ -1287,8 +1293,12 @@ static int step_init_body(step_ctx* ctx, const step_config* cfg, const step_weig
     if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return hip_fail(e, "hipDeviceGetAttribute");
-    const void* kfn = c.dtype == STEP_BF16 ? reinterpret_cast<const void*>(&k_persist_decode<BF16, 2, 4, 6, 2>)
-                                           : reinterpret_cast<const void*>(&k_persist_decode<F16, 2, 4, 6, 2>);
+    const bool two = persist_tpw(c) == 2;
+    const void* kfn = c.dtype == STEP_BF16
+                          ? (two ? reinterpret_cast<const void*>(&k_persist_decode<BF16, 2, 4, 6, 2, 2>)
+                                 : reinterpret_cast<const void*>(&k_persist_decode<BF16, 2, 4, 6, 2, 1>))
+                          : (two ? reinterpret_cast<const void*>(&k_persist_decode<F16, 2, 4, 6, 2, 2>)
+                                 : reinterpret_cast<const void*>(&k_persist_decode<F16, 2, 4, 6, 2, 1>));
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, gr::kPThreads, 0)) != hipSuccess)
       return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (per_cu < 1) return bail(fail(ctx, STEP_EUNSUPPORTED, "persistent decode kernel does not fit on a CU"));

@@ -108,8 +108,9 @@ typedef struct {
    * their outputs to the next through tagged device-memory words inside the kernel. Same results
    * as the multi-kernel step up to rounding order. Built for 16-bit dtypes at hidden 1024, 16 x 128
    * query dims, intermediate 3072, 2 query heads per KV head (Qwen3-0.6B's widths; up to 64 layers,
-   * vocabulary >= 2048), max_position <= 64 * 256 / kv_heads (2048 at those widths: one 64-key
-   * attention split per block) and a device of at least 256 CUs (one block each); other
+   * vocabulary >= 2048), max_position <= 128 * 256 / kv_heads (4,096 at those widths: one attention
+   * split per block, of 64 keys up to 64 * 256 / kv_heads positions and of 128 keys beyond) and a
+   * device of at least 256 CUs (one block each); other
    * configurations get STEP_EUNSUPPORTED at step_init. buckets[0] must be 1. Other buckets keep
    * the multi-kernel step. 0: off. */
   int32_t persistent_decode;

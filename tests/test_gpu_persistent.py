@@ -27,30 +27,36 @@ def _decoder(shape, weights, **kw):
 # with the new one), the new key alone in the second split, ragged splits and tiles, and the
 # 1,024-key context of the batch-1 workload
 CONTEXTS = [0, 127, 128, 300, 1023, 1500]
+# past 2,048 positions the items hold 128 keys: one item exactly (128 with the new key), the last
+# 64-key width, the new key alone in an item, ragged items and tiles, and a 4,001-key row
+CONTEXTS_WIDE = [0, 127, 2047, 2048, 2100, 3001, 4000]
 
 
-@pytest.mark.parametrize("dtype,flags", [("bf16", "qwen3"), ("f16", "qwen3"), ("bf16", "bias-no-qknorm")])
-def test_persistent_step_matches_oracle_and_multikernel(torch_cuda, dtype, flags):
+@pytest.mark.parametrize("dtype,flags,wide", [("bf16", "qwen3", False), ("f16", "qwen3", False),
+                                              ("bf16", "bias-no-qknorm", False), ("bf16", "qwen3", True)])
+def test_persistent_step_matches_oracle_and_multikernel(torch_cuda, dtype, flags, wide):
     """Qwen3-0.6B widths, 2 layers, full vocabulary, bf16 and fp16, and the Qwen2.5 flags (QKV bias,
     no QK-norm) at the same widths: every context above as a batch-1 step through the persistent
     kernel; logits vs the oracle (3e-2) and vs the multi-kernel step (same inputs), greedy tokens
     under the near-tie rule, the new K/V the kernel writes to its slot, and then three
-    device-continued steps against the multi-kernel step's."""
+    device-continued steps against the multi-kernel step's. wide: max_position 4,096, where the
+    kernel's attention items hold 128 keys."""
     torch = torch_cuda
     shape = synth.QWEN3_0_6B.replace(layers=2, dtype=dtype)
     if flags != "qwen3":
         shape = shape.replace(qk_norm=False, qkv_bias=True)
     W = synth.make_weights(shape, 0)
     W32 = fp32_weights(W)
-    sc = Scenario(shape, W, CONTEXTS, steps=4, seed=1101)
-    kw = dict(num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=1536 + 16, max_batch=1,
-              buckets=[1])
+    contexts = CONTEXTS_WIDE if wide else CONTEXTS
+    sc = Scenario(shape, W, contexts, steps=4, seed=1101)
+    kw = dict(num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=4096 if wide else 1536 + 16,
+              max_batch=1, buckets=[1])
     dp = _decoder(shape, W, persistent_decode=True, **kw)
     dm = _decoder(shape, W, persistent_decode=False, **kw)
     sc.inject(dp)
     sc.inject(dm)
     bt_all = sc.table_array()
-    for j, c in enumerate(CONTEXTS):
+    for j, c in enumerate(contexts):
         log("persistent step", dtype, "context", c)
         tok = int(sc.tokens[j])
         slot = oracle.slot_of(sc.tables[j], c, 16)

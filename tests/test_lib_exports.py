@@ -64,8 +64,9 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
 
 def test_persistent_decode_config_is_validated():
     """persistent_decode is accepted only at the widths its kernel is built for, with bucket 1,
-    max_position <= 64 keys x 256 blocks / 8 KV heads = 2048 and 2048 <= vocab <= 262144 (every one of
-    the 2048 LM-head waves owns 1 to 128 rows); the workspace grows by its hand-off words."""
+    max_position <= 128 keys x 256 blocks / 8 KV heads = 4096 (64-key items up to 2048) and
+    2048 <= vocab <= 262144 (every one of the 2048 LM-head waves owns 1 to 128 rows); the workspace
+    grows by its hand-off words."""
     import graph_replay_amd as g
     import graph_replay_amd._lib as L
     if not os.path.exists(L.LIB_PATH):
@@ -87,12 +88,18 @@ def test_persistent_decode_config_is_validated():
     assert with_p > base
     assert g.step_workspace_bytes(cfg(persistent_decode=1, dtype=L.STEP_F16)) > 0
     for bad in (dict(dtype=L.STEP_F32), dict(hidden=1536), dict(intermediate=8960), dict(kv_heads=4),
-                dict(max_position=2049), dict(vocab=2047), dict(vocab=262145), dict(persistent_decode=2)):
+                dict(max_position=4097), dict(vocab=2047), dict(vocab=262145), dict(persistent_decode=2)):
         kw = dict(persistent_decode=1)
         kw.update(bad)
         assert g.step_workspace_bytes(cfg(**kw)) == 0, bad
-    for good in (dict(max_position=2048), dict(vocab=2048), dict(vocab=262144)):
+    for good in (dict(max_position=2048), dict(max_position=2049, max_blocks_per_seq=257),
+                 dict(max_position=4096, max_blocks_per_seq=256), dict(vocab=2048), dict(vocab=262144)):
         assert g.step_workspace_bytes(cfg(persistent_decode=1, **good)) > 0, good
+    # the 128-key items halve the split count: the partials of 4,096 positions take what 2,048 did
+    w2k = g.step_workspace_bytes(cfg(persistent_decode=1, max_position=2048))
+    w4k = g.step_workspace_bytes(cfg(persistent_decode=1, max_position=4096, max_blocks_per_seq=256))
+    assert w4k - w2k == g.step_workspace_bytes(cfg(max_position=4096, max_blocks_per_seq=256)) - \
+        g.step_workspace_bytes(cfg(max_position=2048))
     c = cfg(persistent_decode=1, max_batch=2, num_buckets=1)
     c.buckets[0] = 2
     assert g.step_workspace_bytes(c) == 0            # bucket 1 is what the persistent step serves
