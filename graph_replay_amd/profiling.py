@@ -97,7 +97,7 @@ def _kind_bs1(name: str, grid: int) -> str:
 # The kind of a dispatch of any other workload: the step's kernels by name, the projections by
 # kernel and grid size (each projection of a step has its own grid).
 _NAMED = (("k_persist_decode", "decode_step_persistent"), ("k_attn_prefill", "attn_prefill"),
-          ("k_attn_rows", "attn_decode"), ("k_sample_filter", "sample_filter"), ("k_sample", "sample"),
+          ("k_attn_rows", "attn_decode"), ("k_attn_flat", "attn_decode"), ("k_sample_filter", "sample_filter"), ("k_sample", "sample"),
           ("k_add_rmsnorm", "add_rmsnorm"), ("k_qkv_post", "qknorm_rope_kvwrite"), ("k_gemv_stream", "lm_head"),
           ("k_moe_align", "moe_align"), ("k_moe_sum", "moe_sum"))
 
