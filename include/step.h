@@ -238,8 +238,8 @@ int step_set_device_status(step_ctx *ctx, int32_t site);
  * fixed per row count, never chosen from the batch's contents). Returns the most partial slots
  * (each q_heads x (head_dim + 2) floats) one attention launch over `rows` rows with keys bounded by
  * max_len uses: rows x splits on the split-KV grid, and for a decode step on the balanced kernel
- * (16-bit K/V, balanced_attention_rows to 1,024 rows) rows + 1,024 x (q_heads / kv_heads) / q_heads
- * rounded up, whatever the keys; the larger of the two where both can run. rows must lie in
+ * (16-bit K/V, balanced_attention_rows to 1,024 rows) rows + 2,048 x (q_heads / kv_heads) / q_heads
+ * rounded up (2,048 waves), whatever the keys; the larger of the two where both can run. rows must lie in
  * [1, max(max_batch, max_tokens)] and max_len in [1, max_position]; STEP_EINVAL otherwise or for an
  * invalid config. Writes to *capacity (when not NULL, and whenever cfg is valid) the slots the
  * workspace of this config holds, which no launch's demand exceeds. */
