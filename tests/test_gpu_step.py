@@ -160,3 +160,31 @@ def test_qwen3_width_two_layers_bs32_gumbel(torch_cuda, balanced):
         assert near_tie_ok(int(gtok[j]), sref, TOL["bf16"]), j
     assert mism <= 1
     dec.close()
+
+
+def test_balanced_attention_long_short_and_padding_rows(torch_cuda):
+    """The balanced attention kernel (balanced_attention_rows = 9) on a batch that stresses its share
+    arithmetic: one 8,001-key row spread over ~60 waves (a merge of that many pieces), rows of 1 to
+    18 keys (pieces of one or two tiles, tile edges), a 3,001-key row, and six padding rows of the
+    16-row bucket. Every real row's logits against the oracle."""
+    torch = torch_cuda
+    shape = synth.QWEN3_0_6B.replace(layers=2, vocab=4096)
+    W = synth.make_weights(shape, 0)
+    W32 = fp32_weights(W)
+    contexts = [8000, 0, 1, 15, 16, 17, 3000, 5, 100, 63]
+    sc = Scenario(shape, W, contexts, steps=2, seed=3301)
+    dec = _decoder(shape, W, num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=8016,
+                   max_batch=16, buckets=[16], balanced_attention_rows=9)
+    sc.inject(dec)
+    toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
+    dec.decode(toks, pos, lens, slots, bt)
+    torch.cuda.synchronize()
+    assert dec.last_bucket() == 16
+    got = dec.logits[:len(contexts)].cpu().numpy()
+    assert np.all(np.isfinite(dec.logits[:16].cpu().numpy()))
+    for j, c in enumerate(contexts):
+        log("balanced attention row", j, "context", c)
+        hid = oracle.forward_request(shape, W32, sc.oracle_cache(j), [toks[j]], [pos[j]])
+        ref = oracle.final_logits(W32, hid)[0]
+        assert max_abs(got[j], ref) <= TOL["bf16"], (j, c, max_abs(got[j], ref))
+    dec.close()
