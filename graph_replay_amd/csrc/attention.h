@@ -827,9 +827,10 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
 // unnormalised output) partial, of which the last-arriving wave merges the pair's pieces in piece
 // order. Every block derives the same shares from the rows' lengths, so the grid is fixed and a
 // captured launch replays at any lengths. It serves decode steps (one query row per request, the
-// row's QK-norm + RoPE + KV write fused in as above). Split points follow the whole launch's lengths, so a
-// row's output can change in its last bits with the other rows' lengths; rows without keys (the
-// padding of a bucket) add no tiles and change nothing.
+// row's QK-norm + RoPE + KV write fused in as above). Split points follow the whole launch's
+// lengths, so a row's output can change in its last bits with the other rows' lengths; rows
+// without keys (the padding of a bucket) add no tiles and change nothing.
+//
 // Blocks per launch: two per CU of an MI355X (eight waves per CU; the kernel's registers allow two
 // blocks per CU). Against one per CU, the second block's waves stream while the first's wait at a
 // piece boundary: batch 256 (contexts 16-4,352) 328 -> 306 us per layer.
@@ -862,7 +863,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_flat(AttnRowsArgs a, int R) {
   const int col = lane & 15, grp = lane >> 4;
   const int nkv = a.nkv;
 
-  // tiles of each grid row (0 for an idle row or one without keys), their prefix sums, the most
+  // tiles of each row (0 for a row without keys), their prefix sums, the most
   int n[RPT], loc = 0, mx = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
