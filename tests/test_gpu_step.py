@@ -188,3 +188,33 @@ def test_balanced_attention_long_short_and_padding_rows(torch_cuda):
         ref = oracle.final_logits(W32, hid)[0]
         assert max_abs(got[j], ref) <= TOL["bf16"], (j, c, max_abs(got[j], ref))
     dec.close()
+
+
+def test_balanced_attention_qwen25_fp16_six_heads_per_kv(torch_cuda):
+    """The balanced attention kernel's fp16, six-query-heads-per-KV-head instance (Qwen2.5-1.5B widths:
+    12 query heads over 2 KV heads, QKV bias, no QK-norm), 2 layers, 13 rows padded to 16, against
+    the oracle and against the split grid on the same state."""
+    torch = torch_cuda
+    shape = synth.QWEN2_5_1_5B.replace(layers=2, vocab=4096, dtype="f16")
+    W = synth.make_weights(shape, 0)
+    W32 = fp32_weights(W)
+    contexts = np.random.default_rng(3402).integers(1, 1500, size=13).tolist()
+    sc = Scenario(shape, W, contexts, steps=2, seed=3402)
+    kw = dict(num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=1536, max_batch=16, buckets=[16])
+    db = _decoder(shape, W, balanced_attention_rows=9, **kw)
+    ds = _decoder(shape, W, **kw)
+    sc.inject(db)
+    sc.inject(ds)
+    toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
+    for dec in (db, ds):
+        dec.decode(toks, pos, lens, slots, bt)
+    torch.cuda.synchronize()
+    gb = db.logits[:13].cpu().numpy()
+    gs = ds.logits[:13].cpu().numpy()
+    assert max_abs(gb, gs) <= TOL["f16"], max_abs(gb, gs)
+    for j in range(13):
+        hid = oracle.forward_request(shape, W32, sc.oracle_cache(j), [toks[j]], [pos[j]])
+        ref = oracle.final_logits(W32, hid)[0]
+        assert max_abs(gb[j], ref) <= TOL["f16"], (j, max_abs(gb[j], ref))
+    db.close()
+    ds.close()
