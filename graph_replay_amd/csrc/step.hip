@@ -192,7 +192,7 @@ int split_tokens_for(int rows, int max_len) {
 // K/V (step_config.balanced_attention_rows; 0 picks the default). Measured per layer on Qwen3-0.6B:
 // 32 rows of 128-2,048 keys take 46 us on the split grid and 53 us balanced (each wave's share is
 // then ~20 tiles, and the fixed costs of its pieces and merges outweigh the balance); 256 rows of
-// 16-4,352 keys take 403 us on the split grid and 332 us balanced.
+// 16-4,352 keys take 403 us on the split grid and 306 us balanced.
 constexpr int kFlatMinRowsDefault = 128;
 constexpr int kFlatMinRowsLeast = 9;   // at most 8 rows stay on the split grid (it carries the weight prefetch)
 int flat_min_rows(const step_config& c) {
@@ -201,10 +201,6 @@ int flat_min_rows(const step_config& c) {
 bool use_flat(int rows, const step_config& c) {
   return c.dtype != STEP_F32 && rows >= flat_min_rows(c) && rows <= gr::kFlatMaxRows;
 }
-// The balanced kernel serves decode steps only (the fused prologue, one row per request): the mixed
-// step's decode rows run beside the packed prefill attention, where the split grid's launch, sized
-// by the rows, shares the GPU better (a 512-token chunk + 32 decode rows: 4.69 ms per step on the
-// split grid, 5.35 ms with the balanced kernel).
 
 // Partial slots (each nq query heads of head_dim + 2 floats) that one attention launch over `rows`
 // rows with keys bounded by max_len uses: a (row, split) pair each on the split grid; on the
@@ -213,9 +209,9 @@ size_t split_slot_demand(int rows, int max_len) {
   const int P = split_tokens_for(rows, max_len);
   return static_cast<size_t>(rows) * std::max(1, (max_len + P - 1) / P);
 }
-size_t flat_slot_demand(int rows, const step_config& c) {
+size_t flat_slot_demand(int rows, const step_config& c) {   // flat slots of G heads, in slots of nq heads
   const size_t G = static_cast<size_t>(c.q_heads / c.kv_heads);
-  return static_cast<size_t>(rows) + (static_cast<size_t>(gr::kFlatWaves) * G + c.q_heads - 1) / c.q_heads;
+  return (static_cast<size_t>(gr::flat_slots(rows, c.kv_heads)) * G + c.q_heads - 1) / c.q_heads;
 }
 // the most either kind of launch over `rows` rows uses (a decode step may run the balanced kernel,
 // a mixed step's rows always run the split grid)
@@ -619,7 +615,6 @@ hipError_t launch_attn_rows_d(const AttnRowsArgs& a, int G, dim3 grid, hipStream
   return hipGetLastError();
 }
 
-
 // Row attention over `rows` query rows; max_len bounds the keys of any row (sets the split grid).
 // q == nullptr: decode rows, whose QK-norm + RoPE + KV write run inside the attention kernel from
 // the n_qkv fp32 partial outputs of the QKV projection.
@@ -642,6 +637,10 @@ int run_attn_rows(step_ctx* ctx, int layer, int rows, const float* q, int n_qkv,
   a.eps = c.rms_eps;
   a.k_pool = ctx->k_pool[layer]; a.v_pool = ctx->v_pool[layer];
   a.block_table = bt; a.bt_stride = bt_stride; a.row_ids = row_ids; a.row_req = row_req; a.seq_lens = seq_lens;
+  // The balanced kernel serves decode steps only (the fused prologue, one row per request): the
+  // mixed step's decode rows run beside the packed prefill attention, where the split grid's launch,
+  // sized by the rows, shares the GPU better (a 512-token chunk + 32 decode rows: 4.69 ms per step
+  // on the split grid, 5.35 ms with the balanced kernel).
   const bool flat = q == nullptr && row_ids == nullptr && row_req == nullptr && use_flat(rows, c);
   a.split_tokens = split_tokens_for(rows, max_len);
   a.max_splits = flat ? 1 : std::max(1, (max_len + a.split_tokens - 1) / a.split_tokens);
