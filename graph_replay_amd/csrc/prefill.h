@@ -2,7 +2,8 @@
 //
 // "One forward per step", section "What changed": chunk positions stay packed and run the prefill
 // kernel, decode positions get one query row per request. Here a chunk's tokens are cut into tiles
-// of 16 consecutive queries of one request; one wave handles one (tile, query head):
+// of 16 consecutive queries of one request; one block handles one (tile, query head), and each of its
+// waves a quarter of the tile's key blocks:
 //   S^T[key][query] = K Q^T            v_mfma_f32_16x16x32 (K straight from the pool, Q from registers)
 //   causal mask key_pos <= query_pos, online softmax per query (column)
 //   O^T[dim][query] += V^T P^T          v_mfma_f32_16x16x16 (V^T fragments are 8-byte loads from the
@@ -33,18 +34,23 @@ struct PrefillArgs {
   void* out;                 // [tokens][nq * D] model dtype
 };
 
-// Grid (tiles, ceil(nq / 4)), block 4 waves; wave w takes query head blockIdx.y * 4 + w.
+// Grid (tiles, nq), block 4 waves: block (tile, h) takes query head h of the tile, and its waves
+// split the tile's key blocks (wave w: blocks w, w + 4, ...), each with its own online softmax;
+// the four states merge in wave order through LDS at the end. A tile of the chunk's last queries
+// sees the chunk's whole causal prefix, so one wave per (tile, head) would walk every key block in
+// turn, one memory round trip each, on few waves per CU.
 template <class T, int D>
 __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
   using S = typename T::S;
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int DT = D / 16;   // 16-dim output tiles
+  __shared__ float wm[4][16], wl[4][16];
+  __shared__ float wo[4][16][D];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int h = blockIdx.y * 4 + wid;
-  if (h >= a.nq) return;       // waves never synchronise with each other
+  const int h = blockIdx.y;
   const int tile = blockIdx.x;
   const int req = a.tile_req[tile], q0 = a.tile_q0[tile];
-  if (req < 0) return;         // padding tile (the tile list is padded to a fixed length)
+  if (req < 0) return;         // padding tile (the tile list is padded to a fixed length); whole block
   const int cnt = min(16, a.qsl[req + 1] - q0);
   const int g = h / (a.nq / a.nkv);
   const int col = lane & 15, grp = lane >> 4;
@@ -68,11 +74,14 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
   for (int t = 0; t < DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
   const int nkb = maxpos / 16 + 1;
-  // table entries of the first 64 key blocks (lane j holds block j), fetched before the loop
-  const int bt_pre = (lane < a.bt_stride) ? bt[lane] : -1;
-  auto pool_block = [&](int kb) -> int {   // kb is wave-uniform
+  // table entries of this wave's first 64 key blocks (lane j holds block wid + 4 j), fetched
+  // before the loop
+  const int bt_lane = wid + 4 * lane;
+  const int bt_pre = (bt_lane < a.bt_stride) ? bt[bt_lane] : -1;
+  auto pool_block = [&](int kb) -> int {   // kb is wave-uniform, one of this wave's blocks
+    const int j = (kb - wid) / 4;
     int pb0;
-    if (kb < 64) pb0 = __builtin_amdgcn_readlane(bt_pre, kb);
+    if (j < 64) pb0 = __builtin_amdgcn_readlane(bt_pre, j);
     else pb0 = (kb < a.bt_stride) ? bt[kb] : -1;
     return pb0 >= 0 ? pb0 : a.num_blocks - 1;
   };
@@ -88,16 +97,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) vf[t] = *reinterpret_cast<const uint2*>(vp + (t * 16 + col) * 16 + 4 * grp);
   };
-  {
-    const int pb = pool_block(0);
+  if (wid < nkb) {
+    const int pb = pool_block(wid);
     load_k(pb);
     load_v(pb);
   }
-  // software-pipelined: block kb + 1's K is requested once block kb's score product has issued,
+  // software-pipelined: block kb + 4's K is requested once block kb's score product has issued,
   // its V once the value product has
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    const int next = pool_block(more ? kb + 1 : kb);
+  for (int kb = wid; kb < nkb; kb += 4) {
+    const bool more = kb + 4 < nkb;
+    const int next = pool_block(more ? kb + 4 : kb);
     f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s = mfma16x16x32<T>(kf[ks], qf[ks], s);
@@ -142,13 +151,31 @@ __global__ __launch_bounds__(256) void k_attn_prefill(PrefillArgs a) {
     for (int t = 0; t < DT; ++t) acc[t] = mfma16x16x16<T>(vf[t], pt, acc[t]);
     if (more) load_v(next);
   }
-  if (col < cnt) {
-    S* o = static_cast<S*>(a.out) + (static_cast<size_t>(q0 + col) * a.nq + h) * D;
-    const float inv = 1.0f / lsum;
+  // the four waves' states of each query (a wave without keys for a query has m = -inf), merged in
+  // wave order; key 0 is visible to every query, so wave 0's state is never empty
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+  for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[t * 16 + 4 * grp + i] = T::from_f(acc[t][i] * inv);
+    for (int i = 0; i < 4; ++i) wo[wid][col][t * 16 + 4 * grp + i] = acc[t][i];
+  if (grp == 0) {
+    wm[wid][col] = m;
+    wl[wid][col] = lsum;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < cnt * D; e += 256) {
+    const int qc = e / D, dd = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][qc]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (wm[w][qc] == -INFINITY) ? 0.f : __expf(wm[w][qc] - M);
+      Ls += wl[w][qc] * f;
+      O += wo[w][qc][dd] * f;
+    }
+    S* o = static_cast<S*>(a.out) + (static_cast<size_t>(q0 + qc) * a.nq + h) * D;
+    o[dd] = T::from_f(O / Ls);
   }
 }
 

@@ -1036,7 +1036,7 @@ int run_attn_prefill(step_ctx* ctx, int layer, const MixedPlan& p, const MixedMe
   a.num_blocks = c.num_blocks;
   a.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
   a.out = out;
-  dim3 grid(p.n_tiles, (c.q_heads + 3) / 4);
+  dim3 grid(p.n_tiles, c.q_heads);
   pre_launch(ctx, KK_PREFILL_ATTN);
   if (c.head_dim == 64) launch((k_attn_prefill<T, 64>), grid, dim3(256), 0, ctx->stream, a);
   else launch((k_attn_prefill<T, 128>), grid, dim3(256), 0, ctx->stream, a);
