@@ -129,7 +129,7 @@ struct AttnRowsArgs {
                              // a negative entry is an idle grid row. Partials are kept per grid row.
   const int* row_req;        // row -> block-table row (nullptr: identity)
   const int* seq_lens;       // [rows] keys visible to the row, its own token included
-  int split_tokens;          // P: keys per split (multiple of 64)
+  int split_tokens;          // P: keys per split (multiple of 16)
   int max_splits;            // splits per row (gridDim.z, past which come prefetch blocks)
   int num_blocks;            // pool blocks; a negative table entry reads the scratch block
   void* out;                 // [rows][nq * D] in the model dtype
@@ -150,6 +150,62 @@ __device__ inline bool attn_prefetch_block(const AttnRowsArgs& a) {
 }
 
 constexpr int kMaxSplits = 128;   // splits per row one launch may use (the host sizes P for it)
+
+// The split grid's live pieces, packed. The grid holds rows x nkv x max_splits blocks (fixed per
+// bucket, so it replays as captured), but a row of L keys uses only ceil(L / P) splits (one, which
+// writes zeros, when L <= 0; none for a padding row). The dispatcher hands consecutive blocks to
+// the XCDs and CUs in turn, so in grid order the live blocks of a batch with a few long rows land
+// on a few XCDs and pile up on shared CUs. With more than one split per row, block b instead takes
+// the b-th live piece in (KV head, row, split) order, and blocks past the last one exit: every
+// block counts the pieces of all rows (a block scan over the row table), then the thread whose
+// rows hold piece b names it. Returns false for a block without a piece (block-uniform).
+__device__ inline bool attn_piece(const AttnRowsArgs& a, int& prow, int& g, int& sp) {
+  if (a.max_splits == 1) {   // one block per (row, KV head): the grid is already dense
+    prow = blockIdx.x; g = blockIdx.y; sp = 0;
+    return true;
+  }
+  __shared__ int s_w[4], s_piece[3];
+  const int rows = gridDim.x, nkv = gridDim.y;
+  const int b = blockIdx.x + rows * (blockIdx.y + nkv * blockIdx.z);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int per = (rows + 255) / 256;   // rows of this thread: [r0, r1)
+  const int r0 = min(rows, threadIdx.x * per), r1 = min(rows, r0 + per);
+  auto pieces = [&](int r) -> int {
+    const int row = a.row_ids ? a.row_ids[r] : r;
+    if (row < 0) return 0;
+    const int L = a.seq_lens[row];
+    return L <= 0 ? 1 : (L + a.split_tokens - 1) / a.split_tokens;
+  };
+  int mine = 0;
+  for (int r = r0; r < r1; ++r) mine += pieces(r);
+  int incl = mine;   // inclusive scan over the wave, then over the four waves
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_w[wid] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += s_w[w];
+  const int total = s_w[0] + s_w[1] + s_w[2] + s_w[3];   // pieces of one KV head
+  if (b >= nkv * total) return false;
+  const int q = b % total;
+  int at = incl - mine + before;   // first piece of this thread's rows
+  if (q >= at && q < at + mine) {
+    for (int r = r0; r < r1; ++r) {
+      const int n = pieces(r);
+      if (q < at + n) {
+        s_piece[0] = r; s_piece[1] = b / total; s_piece[2] = q - at;
+        break;
+      }
+      at += n;
+    }
+  }
+  __syncthreads();
+  prow = s_piece[0]; g = s_piece[1]; sp = s_piece[2];
+  return true;
+}
 
 // RMSNorm over one head (optional gain) then rotate-half RoPE: lane holds the pair (lane, lane+D/2).
 template <class T, int D>
@@ -451,9 +507,10 @@ __device__ inline void attn_finish(const AttnRowsArgs& a, int row, int prow, int
 
 // Attention with one query row per request ("One forward per step", section "What changed"),
 // split over the key range so that short batches still fill the GPU (the same page, section
-// "Bottleneck, and what follows"). Grid (rows, nkv, max_splits); split s of a row covers keys
-// [s*P, min(seq_len, (s+1)*P)); splits past the row's keys exit at once, so the grid depends on
-// the bucket only and replays as captured. A row with one split writes its output; otherwise each
+// "Bottleneck, and what follows"). Grid (rows, nkv, max_splits), whose blocks take the live (row,
+// KV head, split) pieces in a packed order (attn_piece); split s of a row covers keys
+// [s*P, min(seq_len, (s+1)*P)); blocks without a piece exit at once, so the grid depends on the
+// bucket only and replays as captured. A row with one split writes its output; otherwise each
 // split writes (max, sum, unnormalised output) and the last split to finish merges them in split
 // order. Block = 4 waves; wave w takes the 16-key blocks w, w+4, ... of the split; the G = nq / nkv
 // query heads sharing the KV head are processed together. Blocks past the split grid (z >=
@@ -471,7 +528,8 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnRowsArgs a) {
   __shared__ float wo[4][G][D];
   __shared__ float qs[G][D];
   if (attn_prefetch_block(a)) return;
-  const int prow = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  int prow, g, sp;
+  if (!attn_piece(a, prow, g, sp)) return;
   const int row = a.row_ids ? a.row_ids[prow] : prow;
   if (row < 0) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -635,7 +693,8 @@ __global__ __launch_bounds__(256, KB == 1 ? 4 : 3) void k_attn_rows_mfma(AttnRow
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wo[4][G][D];
   if (attn_prefetch_block(a)) return;
-  const int prow = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  int prow, g, sp;
+  if (!attn_piece(a, prow, g, sp)) return;
   const int row = a.row_ids ? a.row_ids[prow] : prow;
   if (row < 0) return;
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -174,17 +174,23 @@ __global__ void k_hold(int iters) {
   for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
-// keys per attention split for a row count and key bound (fixed per bucket, so the grid is too):
-// short splits keep a few rows busy on all CUs, long splits amortise each split's fixed cost
-// Keys per attention split. Up to 8 rows, short splits fill the chip. Up to 64 rows whose contexts
-// cannot pass 2,560 keys, one split per row in most cases: each extra split costs a block's fixed
-// prologue and a merge, which measured more than the parallelism they buy (batch 32, contexts
-// 128-2,048: 47.7 us at 512 keys, 45.0 at 1,024, 44.4 at 2,048 per layer). Where rows can be
-// longer, a few long rows would be the tail of the launch (32 decode rows with contexts up to
-// 4,096 ran 7% slower at 2,048 keys), so they keep 512-key splits.
+// Keys per attention split for a row count and key bound (fixed per bucket, so the grid is too).
+// Up to 8 rows, short splits fill the chip. Up to 64 rows whose contexts cannot pass 2,560 keys,
+// one split per row in most cases: each extra split costs a block's fixed prologue and a merge,
+// which measured more than the parallelism they buy (batch 32, contexts 128-2,048: 47.7 us at 512
+// keys, 45.0 at 1,024, 44.4 at 2,048 per layer). Where rows can be longer, a few long rows would be
+// the tail of the launch (32 decode rows with contexts up to 4,096 ran 7% slower at 2,048 keys), so
+// they keep 512-key splits. From 256 keys up the length is then spread over the splits the bound
+// needs, rounded up to whole 16-key blocks, so that no split holds only a few keys (a bound of
+// 4,097 keys takes 8 splits of 528 rather than 9 of 512, the last with one key): batch 32 at
+// 128-2,048 keys 2.201 against 2.234 ms per step.
 int split_tokens_for(int rows, int max_len) {
   int P = rows <= 8 ? 64 : (rows <= 64 && max_len <= 2560 ? 2048 : 512);
   while ((max_len + P - 1) / P > gr::kMaxSplits) P *= 2;
+  if (P >= 256) {
+    const int n = std::max(1, max_len / P);
+    P = ((max_len + n - 1) / n + gr::kBlk - 1) / gr::kBlk * gr::kBlk;
+  }
   return P;
 }
 
@@ -224,7 +230,7 @@ size_t attn_slot_demand(int rows, int max_len, const step_config& c) {
 // The split count is not monotone in the key bound (the split length doubles once a row would need
 // more than kMaxSplits splits), so the bound uses the shortest split length any key bound can give
 // this row count (512 keys stands for 2,048 where longer rows are possible) and caps it at
-// kMaxSplits.
+// kMaxSplits; spreading the length over the splits only ever lowers the count.
 size_t split_slots_bound(int rows, int max_position) {
   const int P = rows <= 8 ? 64 : (rows <= 64 && max_position <= 2560 ? 2048 : 512);
   return static_cast<size_t>(rows) * std::min(gr::kMaxSplits, (max_position + P - 1) / P);
