@@ -162,11 +162,14 @@ def test_qwen3_width_two_layers_bs32_gumbel(torch_cuda, balanced):
     dec.close()
 
 
-def test_balanced_attention_long_short_and_padding_rows(torch_cuda):
+@pytest.mark.parametrize("bal", [9, 0])
+def test_balanced_attention_long_short_and_padding_rows(torch_cuda, bal):
     """The balanced attention kernel (balanced_attention_rows = 9) on a batch that stresses its share
     arithmetic: one 8,001-key row spread over ~60 waves (a merge of that many pieces), rows of 1 to
     18 keys (pieces of one or two tiles, tile edges), a 3,001-key row, and six padding rows of the
-    16-row bucket. Every real row's logits against the oracle."""
+    16-row bucket. Every real row's logits against the oracle. With bal = 0 the same batch runs on
+    the split grid (16 rows), where the long row takes 15 splits and the blocks take the live
+    pieces in packed order past a row without keys and the padding rows."""
     torch = torch_cuda
     shape = synth.QWEN3_0_6B.replace(layers=2, vocab=4096)
     W = synth.make_weights(shape, 0)
@@ -174,7 +177,7 @@ def test_balanced_attention_long_short_and_padding_rows(torch_cuda):
     contexts = [8000, 0, 1, 15, 16, 17, 3000, 5, 100, 63]
     sc = Scenario(shape, W, contexts, steps=2, seed=3301)
     dec = _decoder(shape, W, num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=8016,
-                   max_batch=16, buckets=[16], balanced_attention_rows=9)
+                   max_batch=16, buckets=[16], balanced_attention_rows=bal)
     sc.inject(dec)
     toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
     dec.decode(toks, pos, lens, slots, bt)
