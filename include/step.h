@@ -119,7 +119,9 @@ typedef struct {
    * lengths; fewer rows use the split-KV grid. 0: the default, 128. Otherwise at least 9 (the split
    * grid keeps 8 rows and fewer); above 1,024: never. The balanced kernel's split points follow the
    * whole batch's lengths, so a row's output can change in its last bits with the other rows'
-   * lengths (padding rows have none and change nothing); the split grid's follow the row alone. */
+   * lengths (padding rows have none and change nothing); the split grid's follow the row and the
+   * launch's key bound (max_position for decode steps and bucketed mixed steps, the step's longest
+   * row in the exact-size mixed plan). */
   int32_t balanced_attention_rows;
 } step_config;
 
