@@ -184,3 +184,31 @@ def test_attention_partials_hold_every_launch(max_position, max_batch, max_token
     assert g.step_attention_slots(cfg, 1, max_position + 1)[0] == L.STEP_EINVAL
     cfg.balanced_attention_rows = 8   # the split grid keeps 8 rows and fewer
     assert g.step_attention_slots(cfg, 1, 1)[0] == L.STEP_EINVAL
+
+
+def test_split_lengths_leave_no_short_last_split():
+    """The split grid's split count for a key bound (seen through the partial-slot demand, rows x
+    splits, with the balanced kernel off): from 256-key splits up the length is spread over the
+    splits the bound needs, so a bound just past a multiple of the nominal length (2,048 keys for up
+    to 64 rows whose bound stays within 2,560, else 512) takes no extra split for its last few keys,
+    the average split never falls below the nominal length, and no bound takes more splits than
+    the nominal length would give it."""
+    import graph_replay_amd as g
+    import graph_replay_amd._lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libstep.so not built")
+    cfg = _q3_cfg(L, 9000, 128, 0)
+    cfg.balanced_attention_rows = 2000   # the split grid at every row count
+    # the mixed step's decode rows at a 4,097-key bound: 8 splits, not 9 with one key in the last
+    assert g.step_attention_slots(cfg, 32, 4097)[0] == 32 * 8
+    # up to 64 rows at 2,049 keys: one split of 2,064 keys, not a second one holding one key
+    assert g.step_attention_slots(cfg, 32, 2049)[0] == 32
+    for rows in (9, 32, 64, 65, 128):
+        for max_len in range(1, 9001, 13):
+            n = g.step_attention_slots(cfg, rows, max_len)[0]
+            assert n > 0 and n % rows == 0, (rows, max_len, n)
+            splits = n // rows
+            nominal = 2048 if rows <= 64 and max_len <= 2560 else 512
+            assert splits <= -(-max_len // nominal), (rows, max_len, splits)
+            assert splits == 1 or max_len / splits >= nominal, (rows, max_len, splits)
+            assert splits == max(1, max_len // nominal), (rows, max_len, splits)
