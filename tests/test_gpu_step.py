@@ -221,3 +221,39 @@ def test_balanced_attention_qwen25_fp16_six_heads_per_kv(torch_cuda):
         assert max_abs(gb[j], ref) <= TOL["f16"], (j, max_abs(gb[j], ref))
     db.close()
     ds.close()
+
+
+def test_split_grid_packed_pieces_past_256_rows(torch_cuda):
+    """The split grid over 260 rows (balanced kernel off), where each thread of the block's piece
+    count takes two rows: contexts of 0 to 1,100 keys under a 1,152-position bound (at most two
+    576-key splits per row; rows of 576 and 577 keys on either side of the split edge, and a row
+    without keys), against the balanced kernel on the same state for every row and against the
+    oracle for a sample of rows."""
+    torch = torch_cuda
+    shape = synth.QWEN3_0_6B.replace(layers=2, vocab=4096)
+    W = synth.make_weights(shape, 0)
+    W32 = fp32_weights(W)
+    contexts = np.random.default_rng(3501).integers(0, 1101, size=260).tolist()
+    contexts[5], contexts[200], contexts[257], contexts[258], contexts[259] = 0, 1100, 574, 575, 576
+    sc = Scenario(shape, W, contexts, steps=1, seed=3501)
+    kw = dict(num_blocks=sc.num_blocks, max_blocks_per_seq=sc.width, max_position=1152, max_batch=260,
+              buckets=[260])
+    ds = _decoder(shape, W, balanced_attention_rows=2000, **kw)
+    db = _decoder(shape, W, **kw)
+    sc.inject(ds)
+    sc.inject(db)
+    toks, pos, lens, slots, bt = sc.step_inputs(sc.tokens, sc.contexts)
+    for dec in (ds, db):
+        dec.decode(toks, pos, lens, slots, bt)
+    torch.cuda.synchronize()
+    gs = ds.logits[:260].cpu().numpy()
+    gb = db.logits[:260].cpu().numpy()
+    assert np.all(np.isfinite(gs))
+    assert max_abs(gs, gb) <= TOL["bf16"], max_abs(gs, gb)
+    for j in (0, 5, 100, 200, 257, 258, 259):
+        log("split grid row", j, "context", contexts[j])
+        hid = oracle.forward_request(shape, W32, sc.oracle_cache(j), [toks[j]], [pos[j]])
+        ref = oracle.final_logits(W32, hid)[0]
+        assert max_abs(gs[j], ref) <= TOL["bf16"], (j, contexts[j], max_abs(gs[j], ref))
+    ds.close()
+    db.close()
